@@ -1,0 +1,176 @@
+"""Python binding of libdq.so, the MI355X dual-scale weight-reconstruction solver.
+
+Argument marshalling only: every step of the solver runs in the HIP kernels behind the C ABI
+declared in include/dq.h. PyTorch provides device memory and the current stream. There is
+no CPU fallback: if libdq.so is missing or no GPU is present, calls raise.
+
+    import dual_scale_w4a4_amd as dq
+    out = dq.solve(W_cuda_bf16, "mxfp4", group=32, T=20)
+    out["codes"], out["scales"], out["a"], out["b"], out["mse"], out["g"]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdq.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "dq.h")
+
+FMT = {"int4_bf16": 0, "mxint4": 1, "mxfp4": 2, "nvfp4": 3}
+DTYPE = {"f32": 0, "bf16": 1}
+STATUS = {0: "DQ_OK", 1: "DQ_ERR_ARG", 2: "DQ_ERR_UNSUPPORTED", 3: "DQ_ERR_NONFINITE",
+          4: "DQ_ERR_RANGE", 5: "DQ_ERR_WORKSPACE", 6: "DQ_ERR_HIP", 7: "DQ_ERR_INTERNAL"}
+SOLVE_TWO_SWEEP = 1
+KERNEL_KINDS = ("setup", "fused", "row", "col", "final", "emit")
+
+
+class DQError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class _Timing(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
+                ("used_fused", ctypes.c_int)]
+
+
+class _Init(ctypes.Structure):
+    _fields_ = [("a0", ctypes.c_void_p), ("b0", ctypes.c_void_p), ("g0", ctypes.c_float),
+                ("flags", ctypes.c_uint), ("timing", ctypes.POINTER(_Timing))]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdq.so (built by dual_scale_w4a4_amd.build); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m dual_scale_w4a4_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.dq_workspace_bytes.argtypes = [I64, I64, I, I]
+        L.dq_workspace_bytes.restype = SZ
+        L.dq_solve.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P, P, P, P, P,
+                               P, SZ, P]
+        L.dq_solve.restype = I
+        L.dq_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, SZ, P]
+        L.dq_quantize.restype = I
+        L.dq_status_str.argtypes = [I]
+        L.dq_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().dq_status_str(int(status)).decode()
+
+
+def workspace_bytes(rows: int, cols: int, fmt: str, group: int) -> int:
+    return int(lib().dq_workspace_bytes(int(rows), int(cols), FMT[fmt], int(group)))
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_w(W):
+    torch = _torch()
+    if not W.is_cuda:
+        raise ValueError("W must be a CUDA (HIP) tensor")
+    if W.dtype not in (torch.float32, torch.bfloat16) or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D float32 or bfloat16 tensor")
+    return "bf16" if W.dtype == torch.bfloat16 else "f32"
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _outputs(W, fmt, group):
+    torch = _torch()
+    rows, cols = W.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=W.device)
+    sdt = torch.int16 if fmt == "int4_bf16" else torch.uint8
+    scales = torch.empty((rows, cols // group), dtype=sdt, device=W.device)
+    return codes, scales
+
+
+def _vec(v, n, device):
+    torch = _torch()
+    if v is None:
+        return None
+    v = torch.as_tensor(v, dtype=torch.float32, device=device).contiguous()
+    if v.numel() != n:
+        raise ValueError("scale vector has the wrong length")
+    return v
+
+
+def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
+          two_sweep: bool = False, workspace=None, timing: bool = False,
+          stream=None) -> Dict[str, object]:
+    """dq_solve on W (rows x cols, CUDA float32 / bfloat16). Returns a dict of device
+    tensors codes (rows x cols/2 u8), scales (rows x cols/group; int16 holding bf16 bits for
+    int4_bf16, else u8), a, b (float32), mse (T+1 float64), g (float32[1]) and, when
+    ``timing``, per-kernel-kind milliseconds and launch counts."""
+    torch = _torch()
+    dt = _check_w(W)
+    rows, cols = W.shape
+    dev = W.device
+    codes, scales = _outputs(W, fmt, group)
+    a = torch.empty(rows, dtype=torch.float32, device=dev)
+    b = torch.empty(cols, dtype=torch.float32, device=dev)
+    mse = torch.empty(T + 1, dtype=torch.float64, device=dev)
+    g = torch.zeros(1, dtype=torch.float32, device=dev)
+    a0 = _vec(a0, rows, dev)
+    b0 = _vec(b0, cols, dev)
+    tm = _Timing() if timing else None
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), SOLVE_TWO_SWEEP if two_sweep else 0,
+                 ctypes.pointer(tm) if tm is not None else None)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = lib().dq_solve(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T,
+                        ctypes.byref(init), codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+                        a.data_ptr(), b.data_ptr(), mse.data_ptr(), ws_ptr, ws_bytes,
+                        _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_solve")
+    out = {"codes": codes, "scales": scales, "a": a, "b": b, "mse": mse, "g": g}
+    if tm is not None:
+        out["timing"] = {k: (tm.ms[i], tm.launches[i]) for i, k in enumerate(KERNEL_KINDS)}
+        out["used_fused"] = bool(tm.used_fused)
+    return out
+
+
+def quantize(W, fmt: str, group: int, a=None, b=None, g: float = 0.0, workspace=None,
+             stream=None) -> Dict[str, object]:
+    """dq_quantize: one pass of Q on X(a, b). ``g`` > 0 fixes NVFP4's tensor scale."""
+    torch = _torch()
+    dt = _check_w(W)
+    rows, cols = W.shape
+    dev = W.device
+    codes, scales = _outputs(W, fmt, group)
+    gbuf = torch.full((1,), float(g), dtype=torch.float32, device=dev)
+    a = _vec(a, rows, dev)
+    b = _vec(b, cols, dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = lib().dq_quantize(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, _ptr(a),
+                           _ptr(b), gbuf.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                           ws_ptr, ws_bytes, _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_quantize")
+    return {"codes": codes, "scales": scales, "g": gbuf}

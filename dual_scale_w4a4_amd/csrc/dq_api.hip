@@ -1,0 +1,442 @@
+// dq_api.hip -- host side of libdq.so: argument checks, workspace layout, the launch sequence
+// of one solve on the caller's stream, and status reporting.
+//
+// Launch sequence of dq_solve (daiwk notes, "核心公式" eq. 2 and the conventions under it;
+// trove summary, "How it works" flowchart), all on `stream`, no host round trip inside:
+//   setup   clear the device status, a <- Pi(a0) or 1, b <- Pi(b0) or 1, ra, rb (synced
+//           inner copies), E_i = sum_j W_ij^2 and the finite check, NVFP4 tensor scale g
+//   t = 0 .. T-1
+//     MX formats (single sweep): one pass gives the codes of X(a, b), the row sums and the
+//           column sums; with power-of-two scales the re-quantization after the row update
+//           reproduces the same codes and a_i * d_ig (checked per group, see below), so one
+//           finalize applies both closed-form updates.
+//     otherwise (two sweeps): row pass -> finalize a; column pass on X(a', b) -> finalize b.
+//   emit    Q(X(a_T, b_T)): packed codes, inner scales, and the sums for mse[T].
+// If the MX single-sweep check fails anywhere, the solve is re-run on the two-sweep path,
+// which always re-quantizes; both give the same result whenever the check passes.
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/dq.h"
+#include "dq_internal.h"
+
+namespace {
+
+constexpr int kTileCols = 512;
+constexpr int kTargetBlocks = 512;  // two 4-wave workgroups per CU on 256 CUs
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Plan {
+  int64_t m = 0, n = 0;
+  int G = 0, fmt = 0;
+  int nct = 0, nrc = 0;
+  int64_t rpc = 0;
+  int nblk_rows = 0, nblk_cols = 0;
+  size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
+         off_gs = 0;
+  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, total = 0;
+};
+
+bool shape_ok(int64_t rows, int64_t cols, int group) {
+  if (rows <= 0 || cols <= 0) return false;
+  if (group != 16 && group != 32 && group != 64) return false;
+  if (cols % group != 0) return false;
+  if (rows > ((int64_t)1 << 40) / cols) return false;  // at most 2^40 elements
+  return true;
+}
+
+bool fmt_ok(int fmt) { return fmt >= 0 && fmt <= 3; }
+
+Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
+  Plan p;
+  p.m = m;
+  p.n = n;
+  p.G = G;
+  p.fmt = fmt;
+  p.nct = (int)((n + kTileCols - 1) / kTileCols);
+  int64_t want = (kTargetBlocks + p.nct - 1) / p.nct;
+  int64_t max_rc = (m + 3) / 4;  // at least one row per wave
+  p.nrc = (int)(want < 1 ? 1 : (want > max_rc ? max_rc : want));
+  p.rpc = (m + p.nrc - 1) / p.nrc;
+  p.nrc = (int)((m + p.rpc - 1) / p.rpc);  // drop empty trailing chunks
+  p.nblk_rows = (int)((m + 255) / 256);
+  p.nblk_cols = (int)((n + 255) / 256);
+  size_t o = 0;
+  p.off_status = o; o = align_up(o + 64);
+  p.off_ra = o; o = align_up(o + sizeof(float) * m);
+  p.off_rb = o; o = align_up(o + sizeof(float) * n);
+  p.off_a0 = o; o = align_up(o + sizeof(float) * m);
+  p.off_b0 = o; o = align_up(o + sizeof(float) * n);
+  p.off_E = o; o = align_up(o + sizeof(double) * m);
+  p.off_amax = o; o = align_up(o + sizeof(float) * m);
+  p.off_gs = o; o = align_up(o + 16);
+  p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * (size_t)p.nct * m);
+  p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * (size_t)p.nrc * n);
+  p.off_msepart = o; o = align_up(o + sizeof(double) * p.nblk_rows);
+  p.total = o;
+  return p;
+}
+
+// workspace status words: [0] device flags, [1] mse block counter
+template <class T>
+T* at(char* base, size_t off) {
+  return reinterpret_cast<T*>(base + off);
+}
+
+struct Timer {
+  dq_timing* out;
+  hipStream_t s;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;
+  hipEvent_t pending = nullptr;
+  void before(int k) {
+    if (!out) return;
+    hipEvent_t e0;
+    (void)hipEventCreate(&e0);
+    (void)hipEventRecord(e0, s);
+    pending = e0;
+    kind.push_back(k);
+  }
+  void after() {
+    if (!out) return;
+    hipEvent_t e1;
+    (void)hipEventCreate(&e1);
+    (void)hipEventRecord(e1, s);
+    ev.push_back(pending);
+    ev.push_back(e1);
+  }
+  void collect() {
+    if (!out) return;
+    for (size_t k = 0; k < kind.size(); k++) {
+      float ms = 0.0f;
+      (void)hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]);
+      out->ms[kind[k]] += ms;
+      out->launches[kind[k]] += 1;
+    }
+  }
+  ~Timer() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
+#define DQ_TRY(expr)                     \
+  do {                                   \
+    if ((expr) != hipSuccess) return DQ_ERR_HIP; \
+  } while (0)
+
+dq_status map_status(int flags) {
+  if (flags & dq::kStInitArg) return DQ_ERR_ARG;
+  if (flags & dq::kStNonFinite) return DQ_ERR_NONFINITE;
+  if (flags & dq::kStRange) return DQ_ERR_RANGE;
+  if (flags & dq::kStInternal) return DQ_ERR_INTERNAL;
+  return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dq_status_str(dq_status s) {
+  switch (s) {
+    case DQ_OK: return "DQ_OK";
+    case DQ_ERR_ARG: return "DQ_ERR_ARG: invalid argument";
+    case DQ_ERR_UNSUPPORTED: return "DQ_ERR_UNSUPPORTED: unknown format or weight dtype";
+    case DQ_ERR_NONFINITE: return "DQ_ERR_NONFINITE: W holds a NaN or an infinity";
+    case DQ_ERR_RANGE: return "DQ_ERR_RANGE: a scaled weight value overflowed";
+    case DQ_ERR_WORKSPACE: return "DQ_ERR_WORKSPACE: workspace too small";
+    case DQ_ERR_HIP: return "DQ_ERR_HIP: HIP runtime error";
+    case DQ_ERR_INTERNAL: return "DQ_ERR_INTERNAL: non-positive closed-form numerator";
+    default: return "unknown dq_status";
+  }
+}
+
+size_t dq_workspace_bytes(int64_t rows, int64_t cols, dq_format fmt, int group) {
+  if (!fmt_ok(fmt) || !shape_ok(rows, cols, group)) return 0;
+  return make_plan(rows, cols, fmt, group).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct SolveIo {
+  const void* W;
+  bool bf16;
+  const dq_init* init;
+  uint8_t* codes;
+  void* scales;
+  float* tensor_scale;
+  float* a;
+  float* b;
+  double* mse;
+  int T;
+};
+
+// Enqueue one full solve. `fused` selects the MX single-sweep path. `again` re-runs a solve
+// from the projected initial scales that the first attempt saved in the workspace (the
+// caller's a0 / b0 may alias the outputs a / b, which the first attempt overwrote).
+dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, bool again,
+                        Timer& tm, hipStream_t s) {
+  using namespace dq;
+  int* status = at<int>(ws, p.off_status);
+  unsigned* counter = reinterpret_cast<unsigned*>(status + 1);
+  float* ra = at<float>(ws, p.off_ra);
+  float* rb = at<float>(ws, p.off_rb);
+  double* E = at<double>(ws, p.off_E);
+  float* amax = at<float>(ws, p.off_amax);
+  float* gs = at<float>(ws, p.off_gs);
+  double2* rowpart = at<double2>(ws, p.off_rowpart);
+  double2* colpart = at<double2>(ws, p.off_colpart);
+  double* msepart = at<double>(ws, p.off_msepart);
+  const bool nv = p.fmt == kNvFp4;
+
+  tm.before(DQ_K_SETUP);
+  DQ_TRY(launch_clear(status, 16, s));
+  float* a0s = at<float>(ws, p.off_a0);
+  float* b0s = at<float>(ws, p.off_b0);
+  const float* a_src = again ? a0s : (io.init ? io.init->a0 : nullptr);
+  const float* b_src = again ? b0s : (io.init ? io.init->b0 : nullptr);
+  VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, status};
+  DQ_TRY(launch_vec(va, s));
+  VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, status};
+  DQ_TRY(launch_vec(vb, s));
+  RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
+  DQ_TRY(launch_rowstat(io.bf16, rs, s));
+  if (nv) {
+    ScaleArgs sa{amax, p.m, nullptr, io.init ? io.init->g0 : 0.0f, gs, io.tensor_scale, status};
+    DQ_TRY(launch_tensor_scale(sa, s));
+  }
+  tm.after();
+
+  SweepArgs sw{};
+  sw.W = io.W;
+  sw.m = p.m;
+  sw.n = p.n;
+  sw.G = p.G;
+  sw.ra = ra;
+  sw.rb = rb;
+  sw.a = io.a;
+  sw.b = io.b;
+  sw.gs = gs;
+  sw.nct = p.nct;
+  sw.nrc = p.nrc;
+  sw.rpc = p.rpc;
+  sw.rowpart = rowpart;
+  sw.colpart = colpart;
+  sw.codes = io.codes;
+  sw.scales = io.scales;
+  sw.status = status;
+
+  FinArgs fa{};
+  fa.m = p.m;
+  fa.n = p.n;
+  fa.fmt = p.fmt;
+  fa.rowpart = rowpart;
+  fa.nct = p.nct;
+  fa.E = E;
+  fa.a = io.a;
+  fa.ra = ra;
+  fa.msepart = msepart;
+  fa.counter = counter;
+  fa.inv_mn = 1.0 / ((double)p.m * (double)p.n);
+  fa.colpart = colpart;
+  fa.nrc = p.nrc;
+  fa.b = io.b;
+  fa.rb = rb;
+  fa.status = status;
+
+  for (int t = 0; t < io.T; t++) {
+    fa.mse_out = io.mse + t;
+    if (fused) {
+      tm.before(DQ_K_FUSED);
+      DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow | kModeCol | kModeGauge, sw, s));
+      tm.after();
+      fa.nblk_rows = p.nblk_rows;
+      fa.update_a = 1;
+      fa.gauge_check = 1;
+      fa.nblk_cols = p.nblk_cols;
+      tm.before(DQ_K_FINAL);
+      DQ_TRY(launch_finalize(fa, s));
+      tm.after();
+    } else {
+      tm.before(DQ_K_ROW);
+      DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow, sw, s));
+      tm.after();
+      fa.nblk_rows = p.nblk_rows;
+      fa.update_a = 1;
+      fa.gauge_check = 0;
+      fa.nblk_cols = 0;
+      tm.before(DQ_K_FINAL);
+      DQ_TRY(launch_finalize(fa, s));
+      tm.after();
+      tm.before(DQ_K_COL);
+      DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeCol, sw, s));
+      tm.after();
+      fa.nblk_rows = 0;
+      fa.nblk_cols = p.nblk_cols;
+      tm.before(DQ_K_FINAL);
+      DQ_TRY(launch_finalize(fa, s));
+      tm.after();
+    }
+  }
+  tm.before(DQ_K_EMIT);
+  DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeEmit | kModeRow, sw, s));
+  tm.after();
+  fa.mse_out = io.mse + io.T;
+  fa.nblk_rows = p.nblk_rows;
+  fa.update_a = 0;
+  fa.gauge_check = 0;
+  fa.nblk_cols = 0;
+  tm.before(DQ_K_FINAL);
+  DQ_TRY(launch_finalize(fa, s));
+  tm.after();
+  return DQ_OK;
+}
+
+dq_status read_flags(char* ws, const Plan& p, hipStream_t s, int* flags) {
+  int host[2] = {0, 0};
+  DQ_TRY(hipMemcpyAsync(host, ws + p.off_status, sizeof host, hipMemcpyDeviceToHost, s));
+  DQ_TRY(hipStreamSynchronize(s));
+  *flags = host[0];
+  return DQ_OK;
+}
+
+dq_status check_common(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                       int group, const uint8_t* codes, const void* scales) {
+  if (!fmt_ok(fmt) || (wt != DQ_F32 && wt != DQ_BF16)) return DQ_ERR_UNSUPPORTED;
+  if (!W || !codes || !scales) return DQ_ERR_ARG;
+  if (!shape_ok(rows, cols, group)) return DQ_ERR_ARG;
+  if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)codes & 3u) != 0) return DQ_ERR_ARG;
+  if (fmt == DQ_FMT_INT4_BF16 && ((uintptr_t)scales & 1u) != 0) return DQ_ERR_ARG;
+  return DQ_OK;
+}
+
+// Owns the workspace for one call: the caller's, or a stream-ordered allocation.
+struct WsGuard {
+  char* ptr = nullptr;
+  bool owned = false;
+  hipStream_t s = nullptr;
+  ~WsGuard() {
+    if (owned && ptr) (void)hipFreeAsync(ptr, s);
+  }
+};
+
+dq_status get_workspace(const Plan& p, void* workspace, size_t bytes, hipStream_t s, WsGuard& g) {
+  g.s = s;
+  if (workspace) {
+    if (bytes < p.total) return DQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return DQ_ERR_ARG;
+    g.ptr = static_cast<char*>(workspace);
+    return DQ_OK;
+  }
+  void* ptr = nullptr;
+  DQ_TRY(hipMallocAsync(&ptr, p.total, s));
+  g.ptr = static_cast<char*>(ptr);
+  g.owned = true;
+  return DQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                   int group, int T, const dq_init* init, uint8_t* codes, void* inner_scales,
+                   float* tensor_scale, float* a, float* b, double* mse, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  dq_status st = check_common(W, wt, rows, cols, fmt, group, codes, inner_scales);
+  if (st != DQ_OK) return st;
+  if (T < 0 || !a || !b || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale)) return DQ_ERR_ARG;
+  if (init && (init->g0 != init->g0 || (init->g0 > 0.0f && init->g0 > 3.4028234663852886e38f)))
+    return DQ_ERR_ARG;
+  const Plan p = make_plan(rows, cols, fmt, group);
+  WsGuard ws;
+  st = get_workspace(p, workspace, workspace_bytes, stream, ws);
+  if (st != DQ_OK) return st;
+
+  SolveIo io{W, wt == DQ_BF16, init, codes, inner_scales, tensor_scale, a, b, mse, T};
+  const bool mx = fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4;
+  bool fused = mx && !(init && (init->flags & DQ_SOLVE_TWO_SWEEP));
+  dq_timing* timing = init ? init->timing : nullptr;
+  if (timing) memset(timing, 0, sizeof *timing);
+
+  int flags = 0;
+  for (int attempt = 0; attempt < 2; attempt++) {
+    if (timing) memset(timing, 0, sizeof *timing);
+    Timer tm{timing, stream};
+    st = enqueue_solve(p, ws.ptr, io, fused, attempt > 0, tm, stream);
+    if (st != DQ_OK) return st;
+    st = read_flags(ws.ptr, p, stream, &flags);
+    if (st != DQ_OK) return st;
+    tm.collect();
+    if (timing) timing->used_fused = fused ? 1 : 0;
+    if (fused && (flags & dq::kStGauge) && !(flags & ~dq::kStGauge)) {
+      fused = false;  // the single-sweep identity was not guaranteed: redo on the general path
+      continue;
+    }
+    break;
+  }
+  return map_status(flags & ~dq::kStGauge);
+}
+
+dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                      int group, const float* a, const float* b, float* tensor_scale_inout,
+                      uint8_t* codes, void* inner_scales, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  using namespace dq;
+  dq_status st = check_common(W, wt, rows, cols, fmt, group, codes, inner_scales);
+  if (st != DQ_OK) return st;
+  if (fmt == DQ_FMT_NVFP4 && !tensor_scale_inout) return DQ_ERR_ARG;
+  const Plan p = make_plan(rows, cols, fmt, group);
+  WsGuard ws;
+  st = get_workspace(p, workspace, workspace_bytes, stream, ws);
+  if (st != DQ_OK) return st;
+  char* base = ws.ptr;
+  int* status = at<int>(base, p.off_status);
+  float* ra = at<float>(base, p.off_ra);
+  float* rb = at<float>(base, p.off_rb);
+  float* amax = at<float>(base, p.off_amax);
+  float* gs = at<float>(base, p.off_gs);
+  // a, b are used as given: copy them into the synced slots (no projection)
+  float* acopy = at<float>(base, p.off_rowpart);  // rowpart holds >= 4 m floats
+  float* bcopy = at<float>(base, p.off_colpart);  // colpart holds >= 4 n floats
+  const bool nv = fmt == DQ_FMT_NVFP4;
+
+  DQ_TRY(launch_clear(status, 16, stream));
+  VecArgs va{a, acopy, ra, nullptr, rows, fmt, 0, status};
+  DQ_TRY(launch_vec(va, stream));
+  VecArgs vb{b, bcopy, rb, nullptr, cols, fmt, 0, status};
+  DQ_TRY(launch_vec(vb, stream));
+  RowStatArgs rs{W, rows, cols, ra, rb, at<double>(base, p.off_E), nv ? amax : nullptr, status};
+  DQ_TRY(launch_rowstat(wt == DQ_BF16, rs, stream));
+  if (nv) {
+    ScaleArgs sa{amax, rows, tensor_scale_inout, 0.0f, gs, tensor_scale_inout, status};
+    DQ_TRY(launch_tensor_scale(sa, stream));
+  }
+  SweepArgs sw{};
+  sw.W = W;
+  sw.m = rows;
+  sw.n = cols;
+  sw.G = group;
+  sw.ra = ra;
+  sw.rb = rb;
+  sw.a = acopy;
+  sw.b = bcopy;
+  sw.gs = gs;
+  sw.nct = p.nct;
+  sw.nrc = p.nrc;
+  sw.rpc = p.rpc;
+  sw.codes = codes;
+  sw.scales = inner_scales;
+  sw.status = status;
+  DQ_TRY(launch_sweep(fmt, wt == DQ_BF16, kModeEmit, sw, stream));
+  int flags = 0;
+  st = read_flags(base, p, stream, &flags);
+  if (st != DQ_OK) return st;
+  return map_status(flags);
+}
+
+}  // extern "C"

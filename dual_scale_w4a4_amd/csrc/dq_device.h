@@ -1,0 +1,256 @@
+// dq_device.h -- device-side format codecs and wavefront helpers for the gfx950 solver
+// kernels. Every rounding step here is chosen to give exactly the IEEE result the method's
+// arithmetic names (one binary32 rounding per "fl32" step, exact quotients for codes), so
+// that a single Q pass is bit-identical to an exact-arithmetic evaluation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dq_internal.h"
+
+namespace dq {
+
+constexpr int kWave = 64;
+constexpr int kEpl = 8;                 // weight elements per lane per row
+constexpr int kTileCols = kWave * kEpl;  // 512 columns per wave-row
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kBlock = kWave * kWaves;
+
+// Codec functions compile for both host and device, so that they can be checked
+// exhaustively on the CPU; the cross-lane helpers at the end are device-only.
+#define DQ_HD __host__ __device__ __forceinline__
+
+DQ_HD float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+DQ_HD uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+DQ_HD double u2d(unsigned long long u) { return __builtin_bit_cast(double, u); }
+DQ_HD unsigned long long d2u(double d) { return __builtin_bit_cast(unsigned long long, d); }
+
+// 2^e as a float for e in [-126, 127]
+DQ_HD float exp2i(int e) { return u2f((uint32_t)(e + 127) << 23); }
+
+// ----------------------------------------------------------------------------- rounding
+
+// nearest bf16 value (as float) of a finite non-negative float, ties to even; the bit
+// trick is exact for subnormals too because their spacing is uniform
+DQ_HD float bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u2f(u & 0xFFFF0000u);
+}
+
+// nearest E4M3FN value of a finite non-negative float, ties to even, saturating at 448
+DQ_HD float e4m3_rne_sat(float u) {
+  if (u >= 448.0f) return 448.0f;
+  if (u < 0x1p-6f) return rintf(u * 512.0f) * 0x1p-9f;  // subnormal grid, exact scaling
+  uint32_t b = f2u(u);
+  b += 0x7FFFFu + ((b >> 20) & 1u);  // keep 3 of 23 mantissa bits
+  float r = u2f(b & 0xFFF00000u);
+  return r > 448.0f ? 448.0f : r;
+}
+
+// E4M3FN bits of an exact positive E4M3 value
+DQ_HD uint32_t e4m3_bits(float s) {
+  if (s < 0x1p-6f) return (uint32_t)(s * 512.0f);
+  uint32_t u = f2u(s);
+  uint32_t e = ((u >> 23) & 0xFFu) - 127u + 7u;
+  return (e << 3) | ((u >> 20) & 7u);
+}
+
+// E2M1 magnitude nearest to v in [0, 8), ties to the even index: adding
+// C = 2^22 * max(1, 2^floor(log2 v)) makes the fp32 ulp at C equal to the E2M1 spacing of
+// v's binade (0.5 below 2, then 1, then 2), so (v + C) - C rounds v to that grid with the
+// adder's round-to-nearest-even; the even significand is the even E2M1 index.
+DQ_HD float e2m1_mag(float v) {
+  uint32_t base = f2u(v) & 0x7F800000u;
+  base = base > 0x3F800000u ? base : 0x3F800000u;
+  float c = u2f(base + (22u << 23));
+  float r = (v + c) - c;
+  return fminf(r, 6.0f);
+}
+
+// magnitude index 0..7 of an E2M1 magnitude
+DQ_HD uint32_t e2m1_index(float r) {
+  // 0,.5,1,1.5 -> 2r ; 2,3 -> r + 2 ; 4,6 -> r/2 + 4
+  float k = r < 2.0f ? 2.0f * r : (r < 4.0f ? r + 2.0f : 0.5f * r + 4.0f);
+  return (uint32_t)k;
+}
+
+// nearest integer to the exact quotient ax / d (ax >= 0, d > 0), ties to even. k0 comes from
+// the rounded product ax * rd and is at most one off; the two fused multiply-adds give the
+// exact signs of ax - (k0 +- 1/2) d, which settle the neighbour and the tie.
+DQ_HD float rne_quotient_int(float ax, float d, float rd) {
+  float k0 = rintf(ax * rd);
+  float dh = fmaf(-(k0 + 0.5f), d, ax);
+  float dl = fmaf(-(k0 - 0.5f), d, ax);
+  bool odd = ((int)k0 & 1) != 0;
+  float up = (dh > 0.0f || (dh == 0.0f && odd)) ? 1.0f : 0.0f;
+  float dn = (dl < 0.0f || (dl == 0.0f && odd)) ? 1.0f : 0.0f;
+  return k0 + up - dn;
+}
+
+// nearest E2M1 magnitude to the exact quotient ax / d (ax >= 0, d > 0, rd ~ 1/d). The caller
+// rescales ax and d by the same power of two when d is tiny, so that the fused multiply-adds
+// below cannot underflow. The candidate from ax * rd is at most one grid step off; the exact
+// signs of ax - t d at the two neighbouring midpoints t settle the step and any tie.
+DQ_HD float e2m1_quotient(float ax, float d, float rd) {
+  float r = e2m1_mag(fminf(ax * rd, 8.0f));
+  float qa = r < 2.0f ? 0.5f : (r < 4.0f ? 1.0f : 2.0f);   // step to the next value
+  float qb = r <= 2.0f ? 0.5f : (r <= 4.0f ? 1.0f : 2.0f);  // step to the previous value
+  float dh = fmaf(-(r + 0.5f * qa), d, ax);
+  float dl = fmaf(-(r - 0.5f * qb), d, ax);
+  bool odd = (e2m1_index(r) & 1u) != 0;
+  if (r < 6.0f && (dh > 0.0f || (dh == 0.0f && odd))) return r + qa;
+  if (r > 0.0f && (dl < 0.0f || (dl == 0.0f && odd))) return r - qb;
+  return r;
+}
+
+// ------------------------------------------------------------- projections of outer scales
+// Pi_F: the value of the format's scale set nearest to v > 0 (v computed in fp64).
+
+DQ_HD float proj_bf16(double v) {
+  if (!(v > 0x1p-126)) return 0x1p-126f;
+  unsigned long long u = d2u(v);
+  u += 0xFFFFFFFFFFFull + ((u >> 45) & 1ull);  // keep 7 of 52 mantissa bits, ties to even
+  u &= ~0x1FFFFFFFFFFFull;
+  double r = u2d(u);
+  const double mx = 0x1.FEp127;
+  return r > mx ? (float)mx : (float)r;
+}
+
+DQ_HD float proj_e8m0(double v) {
+  unsigned long long u = d2u(v);
+  u += 1ull << 51;  // a mantissa >= 1/2 (v >= 1.5 * 2^k) carries into the exponent
+  int e = (int)((u >> 52) & 0x7FFull) - 1023;
+  e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  return exp2i(e);
+}
+
+DQ_HD float proj_e4m3(double v) {
+  double r;
+  if (v >= 448.0) {
+    r = 448.0;
+  } else if (v < 0x1p-6) {
+    r = rint(v * 512.0) * 0x1p-9;
+  } else {
+    unsigned long long u = d2u(v);
+    u += ((1ull << 48) - 1ull) + ((u >> 49) & 1ull);  // keep 3 mantissa bits
+    u &= ~((1ull << 49) - 1ull);
+    r = u2d(u);
+    if (r > 448.0) r = 448.0;
+  }
+  if (r < 0x1p-9) r = 0x1p-9;
+  return (float)r;
+}
+
+DQ_HD float project(int fmt, double v) {
+  if (fmt == kInt4Bf16) return proj_bf16(v);
+  if (fmt == kNvFp4) return proj_e4m3(v);
+  return proj_e8m0(v);
+}
+
+// fl32(1/v), correctly rounded (double quotient rounds innocuously to float)
+DQ_HD float recip32(float v) { return (float)(1.0 / (double)v); }
+
+// ------------------------------------------------------------------- the group quantizer Q
+
+// Per-group quantizer state: divisor d, an approximate reciprocal, the operand rescale
+// for tiny divisors, and the stored scale encoding.
+struct GroupQ {
+  float d;
+  float rd;
+  float sc;
+  uint32_t scode;
+};
+
+// Q's inner-scale rule for one group with absmax mx (finite):
+//   INT4_BF16: s = max(bf16(fl32(mx / 7)), 2^-133), d = s
+//   MXINT4 / MXFP4: d = 2^clamp(floor(log2 mx) - 2, -126, 126) (OCP shared exponent, E2M1 and
+//              INT4-as-1.2-fixed-point both have emax 2 relative to the integer code)
+//   NVFP4: u = fl32(mx / fl32(6 g)), s = max(E4M3(u), 2^-9), d = fl32(s g)
+// An all-zero group takes s = 1 (E8M0 exponent 0).
+template <int FMT>
+DQ_HD GroupQ group_scale(float mx, float g, float sixg) {
+  GroupQ r;
+  r.sc = 1.0f;
+  if (FMT == kInt4Bf16) {
+    float s = 1.0f;
+    if (mx > 0.0f) s = fmaxf(bf16_rne((float)((double)mx / 7.0)), 0x1p-133f);
+    r.d = s;
+    r.scode = f2u(s) >> 16;
+    if (s < 0x1p-100f) r.sc = 0x1p32f;
+    r.rd = (float)(1.0 / (double)(s * r.sc));
+  } else if (FMT == kMxInt4 || FMT == kMxFp4) {
+    int e = 0;
+    if (mx > 0.0f) {
+      int ef = (int)((f2u(mx) >> 23) & 0xFFu);  // 0 for subnormal mx: clamps to -126 below
+      e = ef - 129;
+      e = e < -126 ? -126 : e;  // ef <= 254 keeps e <= 125
+    }
+    r.d = exp2i(e);
+    r.rd = exp2i(-e);
+    r.scode = (uint32_t)(e + 127);
+  } else {
+    float s = 1.0f;
+    if (mx > 0.0f) s = fmaxf(e4m3_rne_sat((float)((double)mx / (double)sixg)), 0x1p-9f);
+    r.d = s * g;
+    r.scode = e4m3_bits(s);
+    if (r.d < 0x1p-100f) r.sc = 0x1p32f;
+    r.rd = (float)(1.0 / (double)(r.d * r.sc));
+  }
+  return r;
+}
+
+// the signed code value of x (a float holding the integer or E2M1 value)
+template <int FMT>
+DQ_HD float code_of(float x, const GroupQ& gq) {
+  const float ax = fabsf(x);
+  float r;
+  if (FMT == kInt4Bf16) {
+    r = rne_quotient_int(ax * gq.sc, gq.d * gq.sc, gq.rd);
+    r = fminf(r, x < 0.0f ? 8.0f : 7.0f);
+  } else if (FMT == kMxInt4) {
+    r = fminf(rintf(ax * gq.rd), 7.0f);  // exact quotient: d is a power of two
+  } else if (FMT == kMxFp4) {
+    r = e2m1_mag(ax * gq.rd);
+  } else {
+    r = e2m1_quotient(ax * gq.sc, gq.d * gq.sc, gq.rd);
+  }
+  return x < 0.0f ? -r : r;
+}
+
+template <int FMT>
+DQ_HD uint32_t nibble_of(float q) {
+  if (FMT == kInt4Bf16 || FMT == kMxInt4) return (uint32_t)((int)q) & 0xFu;
+  const uint32_t idx = e2m1_index(fabsf(q));
+  return idx == 0 ? 0u : ((q < 0.0f ? 8u : 0u) | idx);
+}
+
+// ------------------------------------------------------------------------ cross-lane helpers
+
+__device__ __forceinline__ float lane_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// max over aligned groups of `lanes` lanes (2, 4 or 8)
+__device__ __forceinline__ float group_max(float v, int lanes) {
+  v = lane_xor_max(v, 1);
+  if (lanes > 2) v = lane_xor_max(v, 2);
+  if (lanes > 4) v = lane_xor_max(v, 4);
+  return v;
+}
+
+// butterfly sum over the 64 lanes, the same fixed order in every lane and run
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) v = fmaxf(v, __shfl_xor(v, mask, kWave));
+  return v;
+}
+
+}  // namespace dq

@@ -1,0 +1,105 @@
+// dq_internal.h -- kernel argument blocks and launchers shared by dq_kernels.hip and dq_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+enum Fmt : int { kInt4Bf16 = 0, kMxInt4 = 1, kMxFp4 = 2, kNvFp4 = 3 };
+
+// device status word bits
+enum : int {
+  kStNonFinite = 1,  // W has a NaN / Inf
+  kStRange = 2,      // a scaled value overflowed
+  kStInitArg = 4,    // an init value was not finite and positive
+  kStGauge = 8,      // the MX single-sweep identity could not be guaranteed
+  kStInternal = 16,  // N <= 0 with D > 0 (cannot happen with exact products)
+};
+
+// sweep modes (bit set)
+enum : int { kModeRow = 1, kModeCol = 2, kModeEmit = 4, kModeGauge = 8 };
+
+struct SweepArgs {
+  const void* W;
+  int64_t m, n;
+  int G;
+  const float* ra;  // rows: fl32(1 / a), the synced inner copy
+  const float* rb;  // cols: fl32(1 / b)
+  const float* a;   // rows: outer inverse scales (column sums use a_i * d_ig)
+  const float* b;   // cols: outer inverse scales (row sums use q_ij * b_j)
+  const float* gs;  // NVFP4: gs[0] = g, gs[1] = fl32(6 g)
+  int nct;          // column tiles of 512 columns
+  int nrc;          // row chunks
+  int64_t rpc;      // rows per chunk
+  double2* rowpart;  // [nct][m] (N, D)
+  double2* colpart;  // [nrc][n] (P, Q)
+  uint8_t* codes;
+  void* scales;
+  int* status;
+};
+
+struct RowStatArgs {
+  const void* W;
+  int64_t m, n;
+  const float* ra;
+  const float* rb;
+  double* E;     // rows: sum_j W_ij^2
+  float* amax;   // rows: max_j |X_ij| (may be null)
+  int* status;
+};
+
+struct VecArgs {
+  const float* src;  // may be null: ones
+  float* dst;
+  float* rdst;       // fl32(1 / dst)
+  float* dst2;       // optional second copy of dst
+  int64_t len;
+  int fmt;
+  int project;       // 1: project src onto the format's scale set
+  int* status;
+};
+
+struct ScaleArgs {
+  const float* amax;
+  int64_t m;
+  const float* g_in;  // device pointer to a caller value (> 0 fixes g), may be null
+  float g_fixed;      // host value (> 0 fixes g)
+  float* gs;          // out: g, fl32(6 g)
+  float* g_out;       // out: copy of g for the caller (may be null)
+  int* status;
+};
+
+struct FinArgs {
+  int64_t m, n;
+  int fmt;
+  // rows
+  int nblk_rows;
+  const double2* rowpart;
+  int nct;
+  const double* E;
+  float* a;
+  float* ra;
+  int update_a;
+  int gauge_check;
+  double* msepart;     // [nblk_rows]
+  unsigned* counter;   // zero on entry, left zero on exit
+  double* mse_out;     // one double
+  double inv_mn;
+  // cols
+  int nblk_cols;
+  const double2* colpart;
+  int nrc;
+  float* b;
+  float* rb;
+  int* status;
+};
+
+hipError_t launch_clear(int* words, int count, hipStream_t s);
+hipError_t launch_vec(const VecArgs& a, hipStream_t s);
+hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
+hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);
+hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
+
+}  // namespace dq

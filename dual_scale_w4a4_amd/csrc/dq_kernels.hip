@@ -1,0 +1,403 @@
+// dq_kernels.hip -- gfx950 kernels of the DualQuant dual-scale solver.
+//
+// The hot path is a streaming sweep over W (no contraction, so no MFMA): each workgroup of
+// four 64-lane waves owns a 512-column tile of a contiguous chunk of rows. A lane owns 8
+// consecutive columns (one 128-bit load of bf16, two of fp32) for every row the wave visits,
+// so every wave-row load is one contiguous 1 KiB (bf16) segment. Per row the wave forms the
+// scaled tile X = fl32(fl32(W * rb) * ra), the group absmax (2/4/8-lane butterfly), the
+// inner scale and the codes (recomputed every sweep, never stored until the final emit), and
+// then, depending on the mode:
+//   row mode    N_i = sum_j W_ij R_ij, D_i = sum_j R_ij^2 with R = Qhat D_b (daiwk notes,
+//               "核心公式" eq. 2, left), reduced over the wave and written per column tile;
+//   column mode P_j = sum_i W_ij S_ij, Q_j = sum_i S_ij^2 with S = D_a Qhat (eq. 2, right),
+//               kept per lane over the chunk's rows, combined over the 4 waves through LDS
+//               in fixed order and written per row chunk;
+//   emit        packed codes and encoded inner scales.
+// Every term W * R or S^2 is an exact product in fp64 and is accumulated in fp64, so the
+// sums differ from an exact evaluation only by fp64 rounding; all reductions have a fixed
+// order (no floating-point atomics), so results are bit-reproducible.
+#include <float.h>
+
+#include "dq_device.h"
+#include "dq_internal.h"
+
+namespace dq {
+
+// ------------------------------------------------------------------------------ helpers
+
+template <bool BF>
+__device__ __forceinline__ void load8(const void* W, int64_t off, bool active, float w[8]) {
+  if (!active) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) w[k] = 0.0f;
+    return;
+  }
+  if (BF) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      w[2 * k] = u2f(u[k] << 16);
+      w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + off);
+    const float4 v0 = p[0], v1 = p[1];
+    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  }
+}
+
+__device__ __forceinline__ void atomic_flag(int* status, int flags) {
+  if (flags) atomicOr(status, flags);
+}
+
+// ------------------------------------------------------------------------------ the sweep
+
+template <int FMT, bool BF, int MODE>
+__global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
+  constexpr bool ROW = (MODE & kModeRow) != 0;
+  constexpr bool COL = (MODE & kModeCol) != 0;
+  constexpr bool EMIT = (MODE & kModeEmit) != 0;
+  constexpr bool GAUGE = (MODE & kModeGauge) != 0;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ct = blockIdx.x % p.nct;
+  const int rc = blockIdx.x / p.nct;
+  const int64_t r_begin = (int64_t)rc * p.rpc;
+  const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
+  const int64_t col0 = (int64_t)ct * kTileCols + lane * kEpl;
+  const bool active = col0 < p.n;
+  const int lpg = p.G / kEpl;  // lanes per group: 2, 4 or 8
+
+  float rb[8], bb[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    rb[k] = active ? p.rb[col0 + k] : 1.0f;
+    bb[k] = active ? p.b[col0 + k] : 0.0f;
+  }
+  float g = 1.0f, sixg = 6.0f;
+  if (FMT == kNvFp4) {
+    g = p.gs[0];
+    sixg = p.gs[1];
+  }
+
+  double P[8], Q[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) P[k] = Q[k] = 0.0;
+  int flags = 0;
+
+  for (int64_t i = r_begin + wave; i < r_end; i += kWaves) {
+    float w[8];
+    load8<BF>(p.W, i * p.n + col0, active, w);
+    const float ra = p.ra[i];
+    float x[8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      x[k] = (w[k] * rb[k]) * ra;  // column scale first, then row scale; two fp32 roundings
+      mx = fmaxf(mx, fabsf(x[k]));
+    }
+    mx = group_max(mx, lpg);
+    if (!(mx <= FLT_MAX)) {  // a scaled value overflowed
+      flags |= kStRange;
+      mx = 0.0f;
+    }
+    const GroupQ gq = group_scale<FMT>(mx, g, sixg);
+    if (GAUGE && mx > 0.0f) {
+      // single-sweep MX identity: re-quantizing with a' = 2^k a, |k| <= 1, must scale the
+      // scaled values and the shared exponent exactly and keep the exponent unclamped
+      const int ef = (int)((f2u(mx) >> 23) & 0xFFu);
+      if (ef < 9 || ef > 249) flags |= kStGauge;
+    }
+    float q[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) q[k] = code_of<FMT>(x[k], gq);
+
+    if (ROW) {
+      double nacc = 0.0, dacc = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const double t = (double)q[k] * (double)bb[k];  // R / d, exact
+        nacc = fma((double)w[k], t, nacc);
+        dacc = fma(t, t, dacc);
+      }
+      const double dd = (double)gq.d;
+      nacc *= dd;
+      dacc *= dd * dd;
+      nacc = wave_sum(nacc);
+      dacc = wave_sum(dacc);
+      if (lane == 0) p.rowpart[(int64_t)ct * p.m + i] = make_double2(nacc, dacc);
+    }
+    if (COL) {
+      const double c = (double)p.a[i] * (double)gq.d;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const double s = c * (double)q[k];  // S, exact
+        P[k] = fma((double)w[k], s, P[k]);
+        Q[k] = fma(s, s, Q[k]);
+      }
+    }
+    if (EMIT && active) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) packed |= nibble_of<FMT>(q[k]) << (4 * k);
+      reinterpret_cast<uint32_t*>(p.codes)[(i * p.n + col0) >> 3] = packed;
+      if ((lane % lpg) == 0) {
+        const int64_t si = i * (p.n / p.G) + col0 / p.G;
+        if (FMT == kInt4Bf16)
+          static_cast<uint16_t*>(p.scales)[si] = (uint16_t)gq.scode;
+        else
+          static_cast<uint8_t*>(p.scales)[si] = (uint8_t)gq.scode;
+      }
+    }
+  }
+
+  if (COL) {
+    __shared__ double2 lds[kWaves][kTileCols];
+#pragma unroll
+    for (int k = 0; k < 8; k++) lds[wave][lane * kEpl + k] = make_double2(P[k], Q[k]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < kTileCols; c += kBlock) {
+      double2 s = lds[0][c];
+#pragma unroll
+      for (int v = 1; v < kWaves; v++) {
+        s.x += lds[v][c].x;
+        s.y += lds[v][c].y;
+      }
+      const int64_t col = (int64_t)ct * kTileCols + c;
+      if (col < p.n) p.colpart[(int64_t)rc * p.n + col] = s;
+    }
+  }
+  atomic_flag(p.status, flags);  // rare: only lanes that saw a problem
+}
+
+// ------------------------------------------------------------------------- row statistics
+// E_i = sum_j W_ij^2 (fp64, fixed order), a non-finite check on W, and optionally the row
+// max of |X| at the initial scales (NVFP4 tensor scale). One wave per row.
+template <bool BF>
+__global__ __launch_bounds__(kBlock) void k_rowstat(RowStatArgs p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t i = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (i >= p.m) return;
+  double e = 0.0;
+  float mx = 0.0f;
+  const float ra = p.ra[i];
+  for (int64_t c = (int64_t)lane * kEpl; c < p.n; c += kTileCols) {
+    float w[8];
+    load8<BF>(p.W, i * p.n + c, true, w);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      e = fma((double)w[k], (double)w[k], e);
+      if (p.amax) mx = fmaxf(mx, fabsf((w[k] * p.rb[c + k]) * ra));
+    }
+  }
+  e = wave_sum(e);
+  if (p.amax) mx = wave_max(mx);
+  if (lane == 0) {
+    p.E[i] = e;
+    if (p.amax) p.amax[i] = mx;
+    int f = 0;
+    if (!(e <= DBL_MAX)) f |= kStNonFinite;      // W^2 never overflows fp64: e is finite
+    if (p.amax && !(mx <= FLT_MAX)) f |= kStRange;  // iff W is
+    atomic_flag(p.status, f);
+  }
+}
+
+// ----------------------------------------------------------------------------- small kernels
+
+__global__ void k_clear(int* words, int count) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < count) words[t] = 0;
+}
+
+// outer scales: dst = Pi_F(src) (or src as given, or 1) and its synced inner copy fl32(1/dst)
+__global__ void k_vec(VecArgs p) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= p.len) return;
+  float v = 1.0f;
+  if (p.src) {
+    v = p.src[k];
+    if (!(v > 0.0f) || !(v <= FLT_MAX)) {
+      atomic_flag(p.status, kStInitArg);
+      v = 1.0f;
+    }
+    if (p.project) v = project(p.fmt, (double)v);
+  }
+  p.dst[k] = v;
+  p.rdst[k] = recip32(v);
+  if (p.dst2) p.dst2[k] = v;
+}
+
+// NVFP4 tensor scale g = fl32(A / 2688) (2688 = 6 * 448), at least 2^-126; 1 if A = 0.
+__global__ __launch_bounds__(256) void k_tensor_scale(ScaleArgs p) {
+  __shared__ float red[256];
+  float mx = 0.0f;
+  for (int64_t i = threadIdx.x; i < p.m; i += 256) mx = fmaxf(mx, p.amax[i]);
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float g;
+    const float given = p.g_in ? *p.g_in : p.g_fixed;
+    if (given > 0.0f) {
+      g = given;
+    } else {
+      const float A = red[0];
+      g = A == 0.0f ? 1.0f : fmaxf((float)((double)A / 2688.0), 0x1p-126f);
+    }
+    if (!(g <= FLT_MAX)) {
+      atomic_flag(p.status, kStRange);
+      g = 1.0f;
+    }
+    p.gs[0] = g;
+    p.gs[1] = 6.0f * g;
+    if (p.g_out) *p.g_out = g;
+  }
+}
+
+// Closed-form updates (eq. 2) and projections, plus the mse of the state the row sums were
+// taken at: e_i = E_i - 2 a_i N_i + a_i^2 D_i, summed per block in fixed order and over the
+// blocks by the last block to finish (integer counter; fixed summation order).
+__global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
+  __shared__ double red[256];
+  __shared__ int is_last;
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < p.nblk_rows) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    double err = 0.0;
+    int flags = 0;
+    if (i < p.m) {
+      double N = 0.0, D = 0.0;
+      for (int c = 0; c < p.nct; c++) {
+        const double2 v = p.rowpart[(int64_t)c * p.m + i];
+        N += v.x;
+        D += v.y;
+      }
+      const double ai = (double)p.a[i];
+      err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
+      if (p.update_a) {
+        float an = 1.0f;  // an all-zero code slice keeps scale 1
+        if (D > 0.0) {
+          if (!(N > 0.0)) flags |= kStInternal;
+          an = project(p.fmt, N / D);
+        }
+        if (p.gauge_check) {
+          const float ao = p.a[i];
+          if (!(an == ao || an == 2.0f * ao || an == 0.5f * ao)) flags |= kStGauge;
+        }
+        p.a[i] = an;
+        p.ra[i] = recip32(an);
+      }
+    }
+    red[tid] = err;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    if (flags) atomicOr(p.status, flags);
+    if (tid == 0) {
+      __hip_atomic_store(&p.msepart[blockIdx.x], red[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __threadfence();
+      const unsigned prev = atomicAdd(p.counter, 1u);
+      is_last = prev == (unsigned)(p.nblk_rows - 1);
+    }
+    __syncthreads();
+    if (is_last && tid == 0) {
+      __threadfence();
+      double s = 0.0;
+      for (int k = 0; k < p.nblk_rows; k++)
+        s += __hip_atomic_load(&p.msepart[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *p.mse_out = s * p.inv_mn;
+      __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    const int64_t j = (int64_t)(blockIdx.x - p.nblk_rows) * 256 + tid;
+    if (j >= p.n) return;
+    double N = 0.0, D = 0.0;
+    for (int k = 0; k < p.nrc; k++) {
+      const double2 v = p.colpart[(int64_t)k * p.n + j];
+      N += v.x;
+      D += v.y;
+    }
+    float bn = 1.0f;
+    if (D > 0.0) {
+      if (!(N > 0.0)) atomicOr(p.status, kStInternal);
+      bn = project(p.fmt, N / D);
+    }
+    p.b[j] = bn;
+    p.rb[j] = recip32(bn);
+  }
+}
+
+// ------------------------------------------------------------------------------- launchers
+
+hipError_t launch_clear(int* words, int count, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear, dim3((count + 63) / 64), dim3(64), 0, s, words, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_vec(const VecArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.len + 255) / 256;
+  hipLaunchKernelGGL(k_vec, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.m + kWaves - 1) / kWaves));
+  if (bf16)
+    hipLaunchKernelGGL(k_rowstat<true>, grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_rowstat<false>, grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize, dim3(a.nblk_rows + a.nblk_cols), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, bool BF>
+static hipError_t sweep_mode(int mode, const SweepArgs& a, dim3 grid, hipStream_t s) {
+  switch (mode) {
+    case kModeRow: hipLaunchKernelGGL((k_sweep<FMT, BF, kModeRow>), grid, dim3(kBlock), 0, s, a); break;
+    case kModeCol: hipLaunchKernelGGL((k_sweep<FMT, BF, kModeCol>), grid, dim3(kBlock), 0, s, a); break;
+    case kModeRow | kModeCol | kModeGauge:
+      hipLaunchKernelGGL((k_sweep<FMT, BF, kModeRow | kModeCol | kModeGauge>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case kModeEmit | kModeRow:
+      hipLaunchKernelGGL((k_sweep<FMT, BF, kModeEmit | kModeRow>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case kModeEmit: hipLaunchKernelGGL((k_sweep<FMT, BF, kModeEmit>), grid, dim3(kBlock), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t sweep_dtype(bool bf16, int mode, const SweepArgs& a, dim3 grid, hipStream_t s) {
+  return bf16 ? sweep_mode<FMT, true>(mode, a, grid, s) : sweep_mode<FMT, false>(mode, a, grid, s);
+}
+
+hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nct * a.nrc));
+  switch (fmt) {
+    case kInt4Bf16: return sweep_dtype<kInt4Bf16>(bf16, mode, a, grid, s);
+    case kMxInt4: return sweep_dtype<kMxInt4>(bf16, mode, a, grid, s);
+    case kMxFp4: return sweep_dtype<kMxFp4>(bf16, mode, a, grid, s);
+    case kNvFp4: return sweep_dtype<kNvFp4>(bf16, mode, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dq

@@ -1,0 +1,143 @@
+/*
+ * dq.h -- C ABI of libdq.so, the MI355X (gfx950) DualQuant dual-scale weight-reconstruction
+ * solver.
+ *
+ * The method (DualQuant pages: daiwk reproduction notes, "核心公式" eq. 1-2 and the
+ * conventions under them; trove summary, "How it works"):
+ *   W ~= D_a * Qhat * D_b,   Qhat = Q(D_alpha * W * D_beta),   a = 1/alpha, b = 1/beta,
+ * solved by block-coordinate descent that needs only the static weight: quantize the scaled
+ * tile, update every row's outer inverse scale a_i in closed form (1-D least squares against
+ * R = Qhat D_b) and project it onto the format's scale set, re-quantize with the inner copies
+ * synced (alpha = 1/a), update every column's b_j the same way against S = D_a Qhat, project,
+ * re-quantize; repeat T times. An all-zero slice takes scale 1.
+ *
+ * Conventions shared by every entry point:
+ *  - Array arguments are DEVICE pointers owned by the caller (for example torch tensors).
+ *    The library never frees or retains them. W must be 16-byte aligned, codes 4-byte
+ *    aligned; all arrays are dense and row-major.
+ *  - W is rows x cols: a row is an output channel, a column an input channel (X W^T).
+ *    Groups of `group` consecutive columns share one inner scale. cols % group == 0 and
+ *    group is 16, 32 or 64.
+ *  - Arguments are checked on the host before anything is enqueued; on a failed check the
+ *    call returns DQ_ERR_ARG / DQ_ERR_UNSUPPORTED / DQ_ERR_WORKSPACE and enqueues nothing.
+ *  - Work is enqueued on `stream`; the call then synchronizes `stream` so that errors found
+ *    on the device (non-finite W, non-finite scaled values, invalid init values) can be
+ *    returned. Outputs are unspecified when the call returns an error.
+ *  - Calls keep no state between them: the library holds no global mutable data. Calls
+ *    that share a workspace must not overlap.
+ *  - Results are deterministic: every reduction has a fixed order (no floating-point
+ *    atomics), so the same inputs give bit-identical outputs.
+ *
+ * Codes: two per byte, column 2k in the low nibble and 2k+1 in the high nibble. INT4 and
+ * MXINT4 codes are two's-complement nibbles (INT4 uses [-8, 7], MXINT4 [-7, 7]); E2M1 codes
+ * (MXFP4, NVFP4) are sign in bit 3 and magnitude index 0..7 (0, 0.5, 1, 1.5, 2, 3, 4, 6) in
+ * bits 0..2, and a zero is always stored as 0x0.
+ * Inner scales: rows x (cols/group) entries: u16 bf16 bits (INT4_BF16), u8 E8M0 biased
+ * exponent e + 127 (MXINT4, MXFP4), u8 E4M3FN bits (NVFP4).
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DQ_OK = 0,
+  DQ_ERR_ARG = 1,         /* invalid argument (checked on the host, or invalid init values) */
+  DQ_ERR_UNSUPPORTED = 2, /* unknown format or weight dtype */
+  DQ_ERR_NONFINITE = 3,   /* W holds a NaN or an infinity */
+  DQ_ERR_RANGE = 4,       /* a scaled value D_alpha W D_beta overflowed */
+  DQ_ERR_WORKSPACE = 5,   /* workspace smaller than dq_workspace_bytes() */
+  DQ_ERR_HIP = 6,         /* a HIP runtime call failed */
+  DQ_ERR_INTERNAL = 7     /* a closed-form numerator was not positive (never expected) */
+} dq_status;
+
+/* Formats (daiwk notes Table 1 and "本地复现"; news article's block-format paragraph):
+ *  INT4_BF16: INT4 codes, one bf16 inner scale per group (absmax / 7); BF16 outer scales.
+ *  MXINT4:    INT4 codes in [-7, 7], E8M0 inner scale per group; E8M0 outer scales with
+ *             exponents in [-126, 126].
+ *  MXFP4:     E2M1 codes, E8M0 inner scale per group (group 32 is the OCP block); E8M0 outer.
+ *  NVFP4:     E2M1 codes, E4M3 inner scale per group (group 16 is the NVIDIA block) times one
+ *             fp32 tensor scale g; E4M3 outer scales. */
+typedef enum { DQ_FMT_INT4_BF16 = 0, DQ_FMT_MXINT4 = 1, DQ_FMT_MXFP4 = 2, DQ_FMT_NVFP4 = 3 } dq_format;
+
+typedef enum { DQ_F32 = 0, DQ_BF16 = 1 } dq_dtype;
+
+/* Solver options (dq_init.flags). */
+#define DQ_SOLVE_TWO_SWEEP 1u /* MX formats: always re-read W for the column pass instead of
+                                 reusing the row pass's codes (the general path) */
+
+/* Per-kernel timing, filled by dq_solve when dq_init.timing is not NULL (HIP events recorded
+ * on `stream` around each launch; adds a little overhead). Index by dq_kernel_kind. */
+typedef enum {
+  DQ_K_SETUP = 0,  /* init vectors, row statistics, tensor scale */
+  DQ_K_FUSED = 1,  /* MX single-sweep pass: codes, row sums and column sums */
+  DQ_K_ROW = 2,    /* general row pass */
+  DQ_K_COL = 3,    /* general column pass */
+  DQ_K_FINAL = 4,  /* closed-form updates and projections */
+  DQ_K_EMIT = 5,   /* final codes and inner scales */
+  DQ_K_KINDS = 6
+} dq_kernel_kind;
+
+typedef struct {
+  double ms[DQ_K_KINDS];
+  int64_t launches[DQ_K_KINDS];
+  int used_fused; /* 1 if the MX single-sweep path produced the result */
+} dq_timing;
+
+typedef struct {
+  const float* a0;   /* device, rows values > 0, or NULL for ones; projected onto the scale set */
+  const float* b0;   /* device, cols values > 0, or NULL for ones; projected onto the scale set */
+  float g0;          /* NVFP4: > 0 fixes the tensor scale; <= 0 computes it from the initial
+                        scaled tile as fl32(max|X| / 2688), at least 2^-126 (1 if X == 0) */
+  unsigned flags;    /* DQ_SOLVE_* */
+  dq_timing* timing; /* HOST pointer or NULL */
+} dq_init;
+
+/* Bytes of device workspace dq_solve / dq_quantize need for this shape (0 on invalid
+ * arguments). The workspace is scratch: no contents are expected on entry or kept on exit. */
+size_t dq_workspace_bytes(int64_t rows, int64_t cols, dq_format fmt, int group);
+
+/* T >= 0 iterations of the dual-scale block-coordinate descent (daiwk notes, "核心公式"
+ * eq. 2; trove summary, "How it works").
+ *  W:            rows x cols, fp32 or bf16 (wt).
+ *  init:         may be NULL (ones, computed g, default path).
+ *  codes:        out, rows*cols/2 bytes, Q(X(a_T, b_T)) packed as described above.
+ *  inner_scales: out, rows*(cols/group) entries (u16 or u8, see above).
+ *  tensor_scale: out, 1 float: NVFP4's g; ignored (may be NULL) for other formats.
+ *  a, b:         out, rows / cols floats: the final outer inverse scales, each exactly a value
+ *                of the format's scale set (bf16 normal, 2^k with |k| <= 126, or E4M3FN >= 2^-9).
+ *  mse:          out, T+1 doubles: mse[t] = mean (W - D_a Qhat D_b)^2 of the synced state after
+ *                t iterations; mse[0] is single-scale round-to-nearest quantization.
+ *  workspace:    device scratch of at least dq_workspace_bytes(...) bytes, or NULL to let the
+ *                library allocate it with hipMallocAsync / hipFreeAsync on `stream`.
+ * Returns DQ_ERR_ARG also when an a0 / b0 value is not finite and positive. */
+dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                   int group, int T, const dq_init* init, uint8_t* codes, void* inner_scales,
+                   float* tensor_scale, float* a, float* b, double* mse, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* One pass of the group quantizer Q on X = fl32(fl32(W * fl32(1/b)) * fl32(1/a)) (daiwk
+ * notes, "原始论文总结": Q is a black-box group quantizer of the scaled tile).
+ *  a, b: device, rows / cols values > 0 (used as given), or NULL for ones.
+ *  tensor_scale_inout: NVFP4 only (else may be NULL): if the stored value is > 0 it is used
+ *                      as g, otherwise g is computed from max|X| and written back.
+ *  codes, inner_scales: out, as for dq_solve.
+ *  workspace: as for dq_solve. */
+dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                      int group, const float* a, const float* b, float* tensor_scale_inout,
+                      uint8_t* codes, void* inner_scales, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Static string for a status code. */
+const char* dq_status_str(dq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DQ_H */

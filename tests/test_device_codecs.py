@@ -1,0 +1,129 @@
+"""CPU checks of the HIP library's codec header (dual_scale_w4a4_amd/csrc/dq_device.h),
+built for the host: rounding to bf16 / E4M3 / E2M1, the projections of the outer scales and
+the per-group quantizer, against brute-force enumeration, torch's conversions and the oracle.
+These run without a GPU, so a codec bug shows up before any kernel launch."""
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import fmt_brute as fb
+from cases import adversarial_w, rand_w
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(BUILD, "libdq_codec_host.so")
+SRC = [os.path.join(HERE, "codec_host.hip"),
+       os.path.join(os.path.dirname(HERE), "dual_scale_w4a4_amd", "csrc", "dq_device.h"),
+       os.path.join(os.path.dirname(HERE), "dual_scale_w4a4_amd", "csrc", "dq_internal.h")]
+
+
+@pytest.fixture(scope="module")
+def H():
+    os.makedirs(BUILD, exist_ok=True)
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(s) for s in SRC):
+        subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O2", "-std=c++17",
+                        "-fPIC", "-shared", "-ffp-contract=off", SRC[0], "-o", LIB + ".tmp"],
+                       check=True, capture_output=True)
+        os.replace(LIB + ".tmp", LIB)
+    return ctypes.CDLL(LIB)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _map(H, name, x, out_dtype=np.float32):
+    x = np.ascontiguousarray(x)
+    y = np.zeros(x.shape, out_dtype)
+    getattr(H, name)(_p(x), _p(y), ctypes.c_int64(x.size))
+    return y
+
+
+def test_bf16_rne_all_upper_halves(H):
+    hi = np.arange(0, 0x7F7F, dtype=np.uint32)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234], np.uint32)
+    x = (hi[:, None] << 16 | lows[None, :]).reshape(-1).view(np.float32)
+    assert np.array_equal(_map(H, "h_bf16_rne", x).astype(np.float64), fb.torch_bf16(x))
+
+
+def test_e4m3_rne_sat_against_enumeration(H):
+    pos = fb.E4M3_POS_VALS
+    vals = set(pos.tolist()) | set(((pos[1:] + pos[:-1]) / 2).tolist()) | {456.0, 464.0, 1e6, 1e-30}
+    x = np.array(sorted(vals), np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0))])
+    rng = np.random.default_rng(0)
+    x = np.concatenate([x, np.exp(rng.uniform(-12, 7, 4000)).astype(np.float32)])
+    got = _map(H, "h_e4m3_rne_sat", x)
+    want = np.array([fb.e4m3_nearest_sat(float(v)) for v in x])
+    assert np.array_equal(got.astype(np.float64), want)
+    codes = _map(H, "h_e4m3_bits", pos[1:].astype(np.float32), np.uint32)
+    assert np.array_equal(codes, np.arange(1, 0x7F))
+
+
+def test_e2m1_mag_against_enumeration(H):
+    rng = np.random.default_rng(1)
+    grid = np.array(sorted(set(abs(v) for v in fb.E2M1_TABLE)))
+    mids = (grid[1:] + grid[:-1]) / 2
+    x = np.concatenate([grid, mids, rng.uniform(0, 8, 20000), [7.0, 7.99, 1e-40, 0.0]]).astype(np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(8)), np.nextafter(x, np.float32(0))])
+    x = x[x < 8]
+    assert np.array_equal(_map(H, "h_e2m1_mag", x).astype(np.float64), fb.e2m1_nearest(x.astype(np.float64)))
+
+
+@pytest.mark.parametrize("fmt,fid", [("int4_bf16", 0), ("mxfp4", 2), ("nvfp4", 3)])
+def test_projections_against_enumeration(H, fmt, fid):
+    rng = np.random.default_rng(2)
+    v = list(np.exp(rng.uniform(math.log(1e-4), math.log(1e4), 400)))
+    if fmt == "int4_bf16":
+        base = fb.bf16_decode(rng.integers(0x3000, 0x5000, 200).astype(np.uint16)).astype(np.float64)
+        step = np.ldexp(1.0, np.frexp(base)[1] - 8)
+        m = base + step / 2  # exact midpoints
+        v += list(m) + [math.nextafter(t, 0) for t in m] + [math.nextafter(t, 9) for t in m]
+        v += [1e-300, 1e-39, 3.5e38, 1e300]
+    elif fmt == "mxfp4":
+        m = 1.5 * np.ldexp(1.0, np.arange(-128, 129))
+        v += list(m) + [math.nextafter(t, 0) for t in m] + [1e-300, 1e300]
+    else:
+        pos = fb.E4M3_POS_VALS[1:]
+        m = (pos[1:] + pos[:-1]) / 2
+        v += list(m) + [math.nextafter(t, 0) for t in m] + [math.nextafter(t, 999) for t in m]
+        v += [1e-7, 1000.0]
+    x = np.array(v, np.float64)
+    y = np.zeros(len(x), np.float32)
+    H.h_project(ctypes.c_int(fid), _p(x), _p(y), ctypes.c_int64(len(x)))
+    want = np.array([fb.project(fmt, float(t)) for t in x])
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+def test_recip32_is_correctly_rounded(H):
+    rng = np.random.default_rng(3)
+    x = np.exp(rng.uniform(-80, 80, 20000)).astype(np.float32)
+    want = (np.float32(1.0) / x).astype(np.float32)  # numpy: IEEE division
+    assert np.array_equal(_map(H, "h_recip32", x), want)
+
+
+@pytest.mark.parametrize("fmt,fid,group", [("int4_bf16", 0, 32), ("mxint4", 1, 32), ("mxfp4", 2, 32),
+                                            ("nvfp4", 3, 16), ("int4_bf16", 0, 64), ("nvfp4", 3, 64)])
+def test_group_quantizer_matches_oracle(H, oracle_lib, fmt, fid, group):
+    rng = np.random.default_rng(4)
+    for W, a, b in [
+        (adversarial_w(fmt, group, 60, seed=5), None, None),
+        (rand_w(50, 8 * group, seed=6, outliers=9),
+         rng.uniform(0.1, 5, 50).astype(np.float32), rng.uniform(0.1, 5, 8 * group).astype(np.float32)),
+    ]:
+        rows, cols = W.shape
+        A = np.ones(rows, np.float32) if a is None else a
+        B = np.ones(cols, np.float32) if b is None else b
+        X = fb.scaled_tile(W, A, B)
+        ref = oracle_lib.quantize(W, "f32", fmt, group, a, b)
+        q = np.zeros((rows, cols), np.float32)
+        sc = np.zeros((rows, cols // group), np.uint32)
+        H.h_quantize(ctypes.c_int(fid), _p(X), ctypes.c_int64(rows), ctypes.c_int64(cols),
+                     ctypes.c_int(group), ctypes.c_float(ref["g"] if fmt == "nvfp4" else 1.0),
+                     _p(q), _p(sc))
+        assert np.array_equal(q.astype(np.float64), fb.unpack_codes(ref["codes"], fmt))
+        assert np.array_equal(sc, ref["scales"].astype(np.uint32))

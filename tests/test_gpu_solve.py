@@ -1,0 +1,175 @@
+"""GPU parity of the full solver (dq_solve) against the oracle, plus properties that need
+no oracle: determinism, resume, the MX single-sweep path against the two-sweep path, zero
+slices, the fallback when the single-sweep identity cannot be guaranteed, and every error
+status forced from the host."""
+import os
+
+import numpy as np
+import pytest
+
+import fmt_brute as fb
+import workloads
+from cases import rand_w
+from parity import assert_parity, compare_solve, host, scales_np, to_device
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import torch
+
+    assert torch.cuda.is_available()
+    import dual_scale_w4a4_amd
+
+    dual_scale_w4a4_amd.lib()
+    return dual_scale_w4a4_amd
+
+
+@pytest.fixture(scope="module")
+def par_oracle(oracle_lib):
+    oracle_lib.set_threads(THREADS)  # bit-identical to one thread (pinned)
+    yield oracle_lib
+    oracle_lib.set_threads(1)
+
+
+def _run_pair(dq, oracle, w, T=None, exact_if_margin=1e-9):
+    T = w.T if T is None else T
+    print(f"[solve] {w.name} {w.fmt} G={w.group} T={T}", flush=True)
+    ref = oracle.solve(w.W, w.dtype, w.fmt, w.group, T, diag=True)
+    gpu = dq.solve(to_device(w.W, w.dtype), w.fmt, w.group, T)
+    res = compare_solve(gpu, ref, w.fmt, w.rows, w.cols)
+    exact = T == 0 or float(ref["margin"].min()) > exact_if_margin
+    assert_parity(res, exact=exact, name=w.name)
+    if w.fmt == "nvfp4":
+        assert host(gpu["g"])[0] == np.float32(ref["g"])
+    return gpu, ref, res
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_reduced_workloads_match_oracle(dq, par_oracle, cfg):
+    for w in workloads.reduced(cfg):
+        _run_pair(dq, par_oracle, w)
+
+
+def test_workload2_full_size(dq, par_oracle):
+    _run_pair(dq, par_oracle, workloads.config2())
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_workload3_full_size(dq, par_oracle, which):
+    # 8B-shaped MLP matrices, MXFP4, T = 20: the whole trajectory against the oracle
+    gpu, ref, res = _run_pair(dq, par_oracle, workloads.config3(which))
+    print(f"[solve] {which}: mse[0]/mse[T] = {ref['mse'][0] / ref['mse'][-1]:.3f} {res}", flush=True)
+
+
+def test_workload4_full_size(dq, par_oracle):
+    gpu, ref, res = _run_pair(dq, par_oracle, workloads.config4())
+    print(f"[solve] cfg4: {res}", flush=True)
+
+
+def test_workload5_first_layer_full_size(dq, par_oracle):
+    for w in workloads.config5_layer(0):
+        _run_pair(dq, par_oracle, w)
+
+
+@pytest.mark.parametrize("fmt", ["int4_bf16", "mxint4", "mxfp4", "nvfp4"])
+def test_deterministic_and_resumable(dq, fmt):
+    group = 16 if fmt == "nvfp4" else 32
+    W = to_device(rand_w(300, 1568, seed=9, dtype="bf16", outliers=15), "bf16")
+    one = dq.solve(W, fmt, group, 9)
+    two = dq.solve(W, fmt, group, 9)
+    for k in ("a", "b", "codes", "scales", "mse", "g"):
+        assert np.array_equal(host(one[k]), host(two[k])), k
+    first = dq.solve(W, fmt, group, 4)
+    rest = dq.solve(W, fmt, group, 5, a0=first["a"], b0=first["b"], g0=float(host(first["g"])[0]))
+    for k in ("a", "b", "codes", "scales"):
+        assert np.array_equal(host(rest[k]), host(one[k])), k
+    assert np.array_equal(np.concatenate([host(first["mse"])[:4], host(rest["mse"])]),
+                          host(one["mse"]))
+
+
+@pytest.mark.parametrize("fmt", ["mxint4", "mxfp4"])
+def test_single_sweep_equals_two_sweep(dq, fmt):
+    for w in workloads.reduced(3):
+        W = to_device(w.W, w.dtype)
+        fused = dq.solve(W, fmt, 32, 12, timing=True)
+        general = dq.solve(W, fmt, 32, 12, two_sweep=True, timing=True)
+        assert fused["used_fused"] and not general["used_fused"]
+        for k in ("a", "b", "codes", "scales", "mse"):
+            assert np.array_equal(host(fused[k]), host(general[k])), (w.name, k)
+
+
+def test_single_sweep_falls_back_outside_its_range(dq, oracle_lib):
+    # a few groups scaled far down: their shared exponent lies outside the range where the
+    # single-sweep identity is guaranteed, so the solver must re-run on the two-sweep path
+    W = rand_w(64, 512, seed=4)
+    W[5, 64:96] *= np.float32(2.0 ** -118)
+    W[9, :32] *= np.float32(2.0 ** -140)
+    w = workloads.Workload("extreme", W.astype(np.float32), "f32", "mxfp4", 32, 6)
+    gpu = dq.solve(to_device(w.W, "f32"), "mxfp4", 32, 6, timing=True)
+    assert not gpu["used_fused"]
+    ref = oracle_lib.solve(w.W, "f32", "mxfp4", 32, 6)
+    assert_parity(compare_solve(gpu, ref, "mxfp4", 64, 512), exact=True, name="extreme")
+
+
+def test_zero_slices(dq, oracle_lib):
+    for fmt in ("int4_bf16", "mxfp4", "nvfp4"):
+        group = 16
+        W = rand_w(40, 1040, seed=12)
+        W[3, :] = 0
+        W[:, 17] = 0
+        W[8, 32:48] = 0
+        gpu = dq.solve(to_device(W, "f32"), fmt, group, 5)
+        ref = oracle_lib.solve(W, "f32", fmt, group, 5)
+        assert_parity(compare_solve(gpu, ref, fmt, 40, 1040), exact=True, name=fmt)
+        assert host(gpu["a"])[3] == 1.0 and host(gpu["b"])[17] == 1.0
+        s = fb.decode_scales(scales_np(gpu["scales"], fmt), fmt)
+        assert np.all(s[3] == 1.0) and s[8, 2] == 1.0
+
+
+def test_on_grid_weight_is_a_fixed_point(dq):
+    rng = np.random.default_rng(61)
+    q = rng.integers(-7, 8, (64, 1024)).astype(np.float64)
+    q[:, ::32] = 7.0
+    s = fb.bf16_decode(rng.integers(0x3B00, 0x3D00, (64, 32)).astype(np.uint16)).astype(np.float64)
+    W = (q * np.repeat(s, 32, axis=1)).astype(np.float32)
+    out = dq.solve(to_device(W, "f32"), "int4_bf16", 32, 5)
+    assert np.all(host(out["a"]) == 1.0) and np.all(host(out["b"]) == 1.0)
+    mse = host(out["mse"])
+    assert np.all(mse <= 1e-14 * np.mean(W.astype(np.float64) ** 2))
+
+
+def test_error_statuses(dq):
+    import torch
+
+    W = rand_w(64, 512, seed=2)
+    bad = W.copy()
+    bad[7, 100] = np.inf
+    with pytest.raises(dq.DQError) as e:
+        dq.solve(to_device(bad, "f32"), "mxfp4", 32, 3)
+    assert e.value.status == 3
+    bad[7, 100] = np.nan
+    with pytest.raises(dq.DQError) as e:
+        dq.quantize(to_device(bad, "f32"), "nvfp4", 16)
+    assert e.value.status == 3
+    with pytest.raises(dq.DQError) as e:  # scaled tile overflows
+        dq.solve(to_device(W * np.float32(1e30), "f32"), "int4_bf16", 32, 2,
+                 b0=np.full(512, 1e-30, np.float32))
+    assert e.value.status == 4
+    with pytest.raises(dq.DQError) as e:  # non-positive init value
+        a0 = np.ones(64, np.float32)
+        a0[3] = -1
+        dq.solve(to_device(W, "f32"), "int4_bf16", 32, 2, a0=a0)
+    assert e.value.status == 1
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dq.DQError) as e:
+        dq.solve(to_device(W, "f32"), "mxfp4", 32, 2, workspace=ws)
+    assert e.value.status == 5
+    # a caller-provided workspace of the right size works and matches the allocating call
+    ws = torch.empty(dq.workspace_bytes(64, 512, "mxfp4", 32), dtype=torch.uint8, device="cuda")
+    x = dq.solve(to_device(W, "f32"), "mxfp4", 32, 3, workspace=ws)
+    y = dq.solve(to_device(W, "f32"), "mxfp4", 32, 3)
+    assert np.array_equal(host(x["codes"]), host(y["codes"]))

@@ -1,0 +1,89 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point the header
+declares, and rejects invalid arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dq_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def dqlib():
+    import dual_scale_w4a4_amd as dq
+
+    if not os.path.exists(dq.LIB_PATH):
+        from dual_scale_w4a4_amd import build
+
+        build.build()
+    return dq
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == ["dq_quantize", "dq_solve", "dq_status_str", "dq_workspace_bytes"]
+
+
+def test_library_exports_every_declared_symbol(dqlib):
+    lib = dqlib.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dqlib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950(dqlib):
+    out = subprocess.run(["strings", dqlib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+def test_status_strings(dqlib):
+    for code, name in dqlib.STATUS.items():
+        assert dqlib.status_str(code).startswith(name)
+
+
+def test_workspace_bytes_validates_shape(dqlib):
+    assert dqlib.workspace_bytes(128, 256, "int4_bf16", 32) > 0
+    assert dqlib.workspace_bytes(128, 250, "int4_bf16", 32) == 0  # cols % group
+    assert dqlib.workspace_bytes(128, 256, "int4_bf16", 48) == 0  # group
+    assert dqlib.workspace_bytes(0, 256, "mxfp4", 32) == 0
+    big = dqlib.workspace_bytes(14336, 4096, "mxfp4", 32)
+    assert 0 < big < 64 << 20  # partial sums stay a few percent of W
+
+
+def test_invalid_arguments_are_rejected_on_the_host(dqlib):
+    L = dqlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
+    init = dqlib._Init(None, None, 0.0, 0, None)
+    args = dict(W=fake, wt=1, rows=128, cols=256, fmt=2, group=32, T=4)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dq_solve(a["W"], a["wt"], a["rows"], a["cols"], a["fmt"], a["group"], a["T"],
+                          ctypes.byref(init), fake, fake, fake, fake, fake, fake, None, 0, None)
+
+    assert call(W=None) == 1
+    assert call(rows=0) == 1
+    assert call(cols=250) == 1
+    assert call(group=8) == 1
+    assert call(T=-1) == 1
+    assert call(fmt=9) == 2
+    assert call(wt=5) == 2
+    assert call(W=ctypes.c_void_p(0x1004)) == 1  # W not 16-byte aligned
+    # workspace too small: rejected before any launch
+    st = L.dq_solve(fake, 1, 128, 256, 2, 32, 4, ctypes.byref(init), fake, fake, fake, fake,
+                    fake, fake, fake, 16, None)
+    assert st == 5
+    st = L.dq_quantize(fake, 1, 128, 256, 3, 32, None, None, None, fake, fake, None, 0, None)
+    assert st == 1  # NVFP4 needs the tensor-scale pointer
