@@ -1,0 +1,205 @@
+"""Throughput of the dual-scale solver on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is one full dq_solve (setup, T block-coordinate-descent iterations, emit) on every
+matrix of the workload, with W already resident in HBM. The default workload is the
+Llama-3.1-8B-shaped MLP pair (up 14336x4096 and down 4096x14336, bf16, MXFP4, group 32,
+T = 20). `value` is whole-job throughput in weight elements x iterations per second:
+sum over matrices of rows*cols*T, divided by the time of a step.
+
+Also reported: the marginal time per iteration from solves with T and T = 0; the dominant
+kernel's average duration from HIP events recorded on the solve's stream (a second,
+instrumented pass over the same steps) against the HBM roofline; and the CPU oracle timed
+on a bounded row sample of the same workload, with the GPU result on that sample checked
+against it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
+
+
+def _load(workload: int):
+    import workloads
+
+    if workload == 3:
+        return workloads.full(3), "llama3.1-8b MLP up 14336x4096 + down 4096x14336, bf16, MXFP4 G32, T=20"
+    if workload == 4:
+        return workloads.full(4), "llama3.1-70b MLP 28672x8192, bf16, NVFP4 G16, T=20"
+    if workload == 2:
+        return workloads.full(2), "2048x2048 bf16 Student-t, MXINT4 G32, T=15"
+    if workload == 1:
+        return workloads.full(1), "128x256 fp32 tile, INT4/BF16 G32, T=15"
+    if workload == 5:
+        return workloads.config5_layer(0), "llama3.1-8b decoder layer 0 (q,k,v,o,gate,up,down), bf16, INT4/BF16 G64, T=15"
+    raise SystemExit(f"unknown workload {workload}")
+
+
+def to_device(w_np, dtype: str):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(w_np).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(w_np)).cuda()
+
+
+def _dominant_kind(fmt: str) -> str:
+    return "fused" if fmt in ("mxint4", "mxfp4") else "row"
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the solver runs each matrix on a single device "
+              "(sharding across GPUs is by matrix, with no communication); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dual_scale_w4a4_amd as dq
+
+    mats, desc = _load(args.workload)
+    dev_w = [to_device(w.W, w.dtype) for w in mats]
+    work = [dq.workspace_bytes(w.rows, w.cols, w.fmt, w.group) for w in mats]
+    ws = torch.empty(max(work), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(T=None, timing=False):
+        outs = []
+        for w, W in zip(mats, dev_w):
+            outs.append(dq.solve(W, w.fmt, w.group, w.T if T is None else T, workspace=ws,
+                                 timing=timing))
+        return outs
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        outs = step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    # marginal per-iteration time: solves with T = 0 (setup + emit only)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(T=0)
+    torch.cuda.synchronize()
+    t_step0 = (time.perf_counter() - t0) / args.steps
+
+    # instrumented pass over the same steps: per-kernel HIP events on the solve's stream
+    kind = _dominant_kind(mats[0].fmt)
+    ms_all, used_fused = {}, True
+    for _ in range(args.steps):
+        for o in step(timing=True):
+            used_fused = used_fused and o["used_fused"]
+            for k, (ms, n) in o["timing"].items():
+                acc = ms_all.setdefault(k, [0.0, 0])
+                acc[0] += ms
+                acc[1] += n
+    ms_kind, n_kind = ms_all[kind]
+
+    elems = sum(w.rows * w.cols for w in mats)
+    elem_iters = sum(w.rows * w.cols * w.T for w in mats)
+    T_mean = elem_iters / elems
+    bytes_per_elem = 2 if mats[0].dtype == "bf16" else 4
+    value = elem_iters / t_step
+    t_iter = (t_step - t_step0) / T_mean  # per iteration over all matrices of the step
+    iter_gbs = elems * bytes_per_elem / t_iter / 1e9
+    # dominant kernel: each launch reads every weight of its matrix once, T launches per solve
+    bytes_total = args.steps * sum(w.rows * w.cols * bytes_per_elem * w.T for w in mats)
+    avg_launch_ms = ms_kind / max(n_kind, 1)
+    launch_bytes = bytes_total / max(n_kind, 1)
+    achieved = bytes_total / (ms_kind * 1e-3) / 1e9
+
+    mse_final = [float(o["mse"][-1].item()) for o in outs]
+    mse_first = [float(o["mse"][0].item()) for o in outs]
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "weight-elements x iterations / s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators in workloads/, no checkpoint)",
+        "config": {"workload": desc, "matrices": [w.name for w in mats],
+                   "format": mats[0].fmt, "group": mats[0].group, "T": mats[0].T,
+                   "weights": mats[0].dtype, "sums": "f64"},
+        "per_iteration": {"ms": t_iter * 1e3, "elems_per_s": elems / t_iter,
+                          "GBps_one_read_of_W": iter_gbs, "frac_hbm_peak": iter_gbs / HBM_PEAK_GBS,
+                          "ms_per_step_T0": t_step0 * 1e3},
+        "roofline": {"bound": "hbm", "kernel": f"k_sweep ({kind})", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_us": avg_launch_ms * 1e3,
+                     "launches": n_kind, "bytes_per_launch": launch_bytes,
+                     "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}},
+        "mse": {"first": mse_first, "final": mse_final,
+                "ratio_first_over_final": [a / b for a, b in zip(mse_first, mse_final)]},
+        "single_sweep_path": used_fused if kind == "fused" else None,
+    }
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(mats[0], dq, to_device)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, dq, to_device):
+    """The oracle on a bounded row sample of the first matrix (same T), all host cores up to
+    16, and the GPU on the same sample checked against it."""
+    import numpy as np
+
+    import oracle
+
+    rows = min(w.rows, max(64, (2048 * 4096) // w.cols))
+    sample = np.ascontiguousarray(w.W[:rows])
+    threads = oracle.set_threads(min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ref = oracle.solve(sample, w.dtype, w.fmt, w.group, w.T)
+    dt = time.perf_counter() - t0
+    oracle.set_threads(1)
+    gpu = dq.solve(to_device(sample, w.dtype), w.fmt, w.group, w.T)
+    mse_g = gpu["mse"].cpu().numpy()
+    a_eq = bool(np.array_equal(gpu["a"].cpu().numpy(), ref["a"]))
+    b_eq = bool(np.array_equal(gpu["b"].cpu().numpy(), ref["b"]))
+    codes_eq = bool(np.array_equal(gpu["codes"].cpu().numpy(), ref["codes"]))
+    return {
+        "value": rows * w.cols * w.T / dt,
+        "unit": "weight-elements x iterations / s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of {w.name} ({rows}x{w.cols}), {w.fmt}, T={w.T}",
+        "seconds": dt,
+        "gpu_vs_oracle_on_sample": {"mse_final_rel": float(abs(mse_g[-1] - ref["mse"][-1]) / ref["mse"][-1]),
+                                    "a_identical": a_eq, "b_identical": b_eq,
+                                    "codes_identical": codes_eq},
+    }
+
+
+if __name__ == "__main__":
+    main()

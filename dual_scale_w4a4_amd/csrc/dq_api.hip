@@ -25,7 +25,19 @@
 namespace {
 
 constexpr int kTileCols = 512;
+constexpr int kFusedCols = 1024;
 constexpr int kTargetBlocks = 512;  // two 4-wave workgroups per CU on 256 CUs
+
+// Workgroup target for the sweeps; DQ_TARGET_WGS overrides it (launch-shape tuning only:
+// results do not depend on it beyond the fixed summation order it implies).
+int target_blocks() {
+  const char* env = getenv("DQ_TARGET_WGS");
+  if (env) {
+    int v = atoi(env);
+    if (v >= 1 && v <= 65536) return v;
+  }
+  return kTargetBlocks;
+}
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -34,10 +46,12 @@ struct Plan {
   int G = 0, fmt = 0;
   int nct = 0, nrc = 0;
   int64_t rpc = 0;
+  int f_nct = 0, f_nrc = 0;  // single-sweep MX pass: 1024-column tiles, rows in multiples of 32
+  int64_t f_rpc = 0;
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
-  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, total = 0;
+  size_t off_rowpart = 0, off_rowerr = 0, off_colpart = 0, off_msepart = 0, total = 0;
 };
 
 bool shape_ok(int64_t rows, int64_t cols, int group) {
@@ -56,12 +70,19 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.n = n;
   p.G = G;
   p.fmt = fmt;
+  const int target = target_blocks();
   p.nct = (int)((n + kTileCols - 1) / kTileCols);
-  int64_t want = (kTargetBlocks + p.nct - 1) / p.nct;
+  int64_t want = (target + p.nct - 1) / p.nct;
   int64_t max_rc = (m + 3) / 4;  // at least one row per wave
   p.nrc = (int)(want < 1 ? 1 : (want > max_rc ? max_rc : want));
   p.rpc = (m + p.nrc - 1) / p.nrc;
   p.nrc = (int)((m + p.rpc - 1) / p.rpc);  // drop empty trailing chunks
+  p.f_nct = (int)((n + kFusedCols - 1) / kFusedCols);
+  int64_t f_want = (target + p.f_nct - 1) / p.f_nct;
+  if (f_want < 1) f_want = 1;
+  p.f_rpc = (m + f_want - 1) / f_want;
+  p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
+  p.f_nrc = (int)((m + p.f_rpc - 1) / p.f_rpc);
   p.nblk_rows = (int)((m + 255) / 256);
   p.nblk_cols = (int)((n + 255) / 256);
   size_t o = 0;
@@ -73,8 +94,11 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.off_E = o; o = align_up(o + sizeof(double) * m);
   p.off_amax = o; o = align_up(o + sizeof(float) * m);
   p.off_gs = o; o = align_up(o + 16);
-  p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * (size_t)p.nct * m);
-  p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * (size_t)p.nrc * n);
+  const size_t rc_parts = (size_t)(p.nct > p.f_nct ? p.nct : p.f_nct);
+  const size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
+  p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
+  p.off_rowerr = o; o = align_up(o + sizeof(double) * (size_t)p.f_nct * m);
+  p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
   p.off_msepart = o; o = align_up(o + sizeof(double) * p.nblk_rows);
   p.total = o;
   return p;
@@ -199,9 +223,10 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   float* b0s = at<float>(ws, p.off_b0);
   const float* a_src = again ? a0s : (io.init ? io.init->a0 : nullptr);
   const float* b_src = again ? b0s : (io.init ? io.init->b0 : nullptr);
-  VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, status};
+  const bool fast = fused && io.bf16;  // the single-sweep kernel for bf16 weights
+  VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(va, s));
-  VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, status};
+  VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(vb, s));
   RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
   DQ_TRY(launch_rowstat(io.bf16, rs, s));
@@ -248,9 +273,40 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fa.rb = rb;
   fa.status = status;
 
+  FusedArgs fu{};
+  fu.W = static_cast<const uint16_t*>(io.W);
+  fu.m = p.m;
+  fu.n = p.n;
+  fu.G = p.G;
+  fu.rb = rb;
+  fu.b = io.b;
+  fu.nct = p.f_nct;
+  fu.nrc = p.f_nrc;
+  fu.rpc = p.f_rpc;
+  fu.rowpart = rowpart;
+  fu.rowerr = at<double>(ws, p.off_rowerr);
+  fu.colpart = colpart;
+  fu.status = status;
+
   for (int t = 0; t < io.T; t++) {
     fa.mse_out = io.mse + t;
-    if (fused) {
+    if (fast) {
+      tm.before(DQ_K_FUSED);
+      DQ_TRY(launch_fused(p.fmt, fu, s));
+      tm.after();
+      fa.nct = p.f_nct;
+      fa.nrc = p.f_nrc;
+      fa.nblk_rows = p.nblk_rows;
+      fa.update_a = 1;
+      fa.gauge_check = 0;
+      fa.row_ra = 1;
+      fa.envelope = 1;
+      fa.rowerr = fu.rowerr;
+      fa.nblk_cols = p.nblk_cols;
+      tm.before(DQ_K_FINAL);
+      DQ_TRY(launch_finalize(fa, s));
+      tm.after();
+    } else if (fused) {
       tm.before(DQ_K_FUSED);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow | kModeCol | kModeGauge, sw, s));
       tm.after();
@@ -285,6 +341,11 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   tm.before(DQ_K_EMIT);
   DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeEmit | kModeRow, sw, s));
   tm.after();
+  fa.nct = p.nct;
+  fa.nrc = p.nrc;
+  fa.row_ra = 0;
+  fa.envelope = 0;
+  fa.rowerr = nullptr;
   fa.mse_out = io.mse + io.T;
   fa.nblk_rows = p.nblk_rows;
   fa.update_a = 0;
@@ -406,9 +467,9 @@ dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq
   const bool nv = fmt == DQ_FMT_NVFP4;
 
   DQ_TRY(launch_clear(status, 16, stream));
-  VecArgs va{a, acopy, ra, nullptr, rows, fmt, 0, status};
+  VecArgs va{a, acopy, ra, nullptr, rows, fmt, 0, 0, status};
   DQ_TRY(launch_vec(va, stream));
-  VecArgs vb{b, bcopy, rb, nullptr, cols, fmt, 0, status};
+  VecArgs vb{b, bcopy, rb, nullptr, cols, fmt, 0, 0, status};
   DQ_TRY(launch_vec(vb, stream));
   RowStatArgs rs{W, rows, cols, ra, rb, at<double>(base, p.off_E), nv ? amax : nullptr, status};
   DQ_TRY(launch_rowstat(wt == DQ_BF16, rs, stream));

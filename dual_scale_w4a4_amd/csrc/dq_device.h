@@ -240,6 +240,41 @@ __device__ __forceinline__ float group_max(float v, int lanes) {
   return v;
 }
 
+// DPP lane permutations (within quads / 16-lane rows; every source lane exists)
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// max over aligned groups of LANES lanes (2, 4 or 8) with DPP
+template <int LANES>
+__device__ __forceinline__ float group_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  if (LANES > 2) v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  if (LANES > 4) v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  return v;
+}
+
+// sum over aligned groups of 8 lanes, fixed order, result in all 8 lanes
+__device__ __forceinline__ double sum8_dpp(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowHalfMirror>(v);
+  return v;
+}
+
 // butterfly sum over the 64 lanes, the same fixed order in every lane and run
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

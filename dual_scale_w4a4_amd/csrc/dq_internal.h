@@ -39,6 +39,22 @@ struct SweepArgs {
   int* status;
 };
 
+// Single-sweep MX pass on bf16 weights (see k_fused_mx).
+struct FusedArgs {
+  const uint16_t* W;
+  int64_t m, n;
+  int G;
+  const float* rb;
+  const float* b;
+  int nct;          // column tiles of 1024 columns
+  int nrc;          // row chunks
+  int64_t rpc;      // rows per chunk
+  double2* rowpart;  // [nct][m] (sum_j W t, sum_j t^2) with t = S b: R = ra * t
+  double* rowerr;    // [nct][m] sum_j (W - t)^2
+  double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
+  int* status;
+};
+
 struct RowStatArgs {
   const void* W;
   int64_t m, n;
@@ -57,6 +73,7 @@ struct VecArgs {
   int64_t len;
   int fmt;
   int project;       // 1: project src onto the format's scale set
+  int envelope;      // 1: flag kStGauge if a value leaves [2^-24, 2^24] (single-sweep range)
   int* status;
 };
 
@@ -76,12 +93,15 @@ struct FinArgs {
   // rows
   int nblk_rows;
   const double2* rowpart;
+  const double* rowerr;  // per-tile row errors (single-sweep pass) or null: use E - 2aN + a^2 D
   int nct;
   const double* E;
   float* a;
   float* ra;
   int update_a;
   int gauge_check;
+  int row_ra;          // row sums lack the ra_i factor (single-sweep MX pass)
+  int envelope;        // flag kStGauge if a new a or b leaves [2^-24, 2^24]
   double* msepart;     // [nblk_rows]
   unsigned* counter;   // zero on entry, left zero on exit
   double* mse_out;     // one double
@@ -101,5 +121,6 @@ hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
+hipError_t launch_fused(int fmt, const FusedArgs& a, hipStream_t s);
 
 }  // namespace dq

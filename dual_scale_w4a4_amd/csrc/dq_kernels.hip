@@ -173,6 +173,195 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
   atomic_flag(p.status, flags);  // rare: only lanes that saw a problem
 }
 
+// --------------------------------------------------------------- single-sweep MX pass
+// For MXINT4 / MXFP4 on bf16 weights. With E8M0 outer scales the inner scale of a group is
+// fixed by y = fl32(W * rb) alone: the group's shared exponent is e = floor(log2 max|y|) - 2 +
+// log2(ra), so c = a_i * d_ig = 2^(floor(log2 max|y|) - 2) and the codes are those of y / c.
+// Consequently the re-quantization after the row update reproduces the same codes and the
+// same S = a d q (daiwk notes, "核心公式": row update, re-quantize, column update), and one
+// read of W gives both closed-form updates:
+//   row i:    N'_i = sum_j W_ij t_ij,  D'_i = sum_j t_ij^2,  t = S b  (R = ra_i t)
+//             e_i = sum_j (W_ij - t_ij)^2, the row's reconstruction error (t = a d q b)
+//   column j: P_j = sum_i W_ij S_ij,   Q_j = sum_i S_ij^2
+// This holds while every value stays in fp32's normal range with exact products, which is
+// guaranteed when every nonzero group max |y| lies in [2^-32, 2^32) and every a, b in
+// [2^-24, 2^24]; otherwise the pass raises kStGauge and the solve is redone on the general
+// two-sweep path. MXFP4 codes come from gfx950's scaled FP4 conversion, which rounds y / c
+// to the nearest E2M1 value (ties to even, saturating) exactly for power-of-two c; the
+// matching decode returns S = code * c directly.
+//
+// Layout: a lane owns 16 columns of a 1024-column tile (two 512-column halves, each one
+// 128-bit load per row, contiguous across the wave). Products are exact in fp32; per-lane
+// sums run over 16 columns (rows) or over the chunk's rows (columns) in fp32; every sum
+// above that is fp64 in a fixed order: a row's 64 lane partials are transposed through LDS
+// in batches of 8 rows and added by 8 lanes per row, and the 4 waves' column partials are
+// added through LDS at the end.
+constexpr int kFusedCols = 1024;
+constexpr int kFusedBatch = 8;  // rows per wave between row reductions
+constexpr int kFusedLoad = 2;   // rows per (double-buffered) load step
+
+template <int FMT, int G>
+__global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
+  constexpr int LPG = G / kEpl;  // lanes per group
+  __shared__ float4 smem4[kWaves * kFusedBatch * kWave];  // 32 KiB, two views
+  float2* smem = reinterpret_cast<float2*>(smem4);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ct = blockIdx.x % p.nct;
+  const int rc = blockIdx.x / p.nct;
+  const int64_t r_begin = (int64_t)rc * p.rpc;
+  const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
+  const int64_t col[2] = {(int64_t)ct * kFusedCols + lane * kEpl,
+                          (int64_t)ct * kFusedCols + kTileCols + lane * kEpl};
+  const bool act[2] = {col[0] < p.n, col[1] < p.n};
+
+  float rb[16], bb[16], P[16], Q[16];
+#pragma unroll
+  for (int h = 0; h < 2; h++)
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      rb[8 * h + k] = act[h] ? p.rb[col[h] + k] : 1.0f;
+      bb[8 * h + k] = act[h] ? p.b[col[h] + k] : 0.0f;
+      P[8 * h + k] = Q[8 * h + k] = 0.0f;
+    }
+  int flags = 0;
+
+  // this wave's rows: batches of 8 consecutive rows, 32 rows apart across the workgroup
+  const int64_t first = r_begin + (int64_t)wave * kFusedBatch;
+  const int64_t nbatch = first < r_end ? (r_end - first + kWaves * kFusedBatch - 1) /
+                                             (kWaves * kFusedBatch) : 0;
+  constexpr int kSteps = kFusedBatch / kFusedLoad;  // load steps per batch
+  const int64_t nsteps = nbatch * kSteps;
+  auto row_of = [&](int64_t step, int r) -> int64_t {
+    return first + (step / kSteps) * (kWaves * kFusedBatch) + (step % kSteps) * kFusedLoad + r;
+  };
+  auto load_step = [&](int64_t step, uint4 (&buf)[kFusedLoad][2]) {
+#pragma unroll
+    for (int r = 0; r < kFusedLoad; r++) {
+      const int64_t i = row_of(step, r);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        if (i < r_end && act[h])
+          buf[r][h] = *reinterpret_cast<const uint4*>(p.W + i * p.n + col[h]);
+        else
+          buf[r][h] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  uint4 cur[kFusedLoad][2], nxt[kFusedLoad][2];
+  if (nsteps > 0) load_step(0, cur);
+  float nl[kFusedBatch], dl[kFusedBatch], el[kFusedBatch];
+  for (int64_t step = 0; step < nsteps; step++) {
+    if (step + 1 < nsteps) load_step(step + 1, nxt);
+#pragma unroll
+    for (int r = 0; r < kFusedLoad; r++) {
+      float nacc = 0.0f, dacc = 0.0f, eacc = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const uint32_t u[4] = {cur[r][h].x, cur[r][h].y, cur[r][h].z, cur[r][h].w};
+        float w[8], y[8];
+        float mx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          w[2 * k] = u2f(u[k] << 16);
+          w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          y[k] = w[k] * rb[8 * h + k];
+          mx = fmaxf(mx, fabsf(y[k]));
+        }
+        mx = group_max_dpp<LPG>(mx);
+        const uint32_t ey = (f2u(mx) >> 23) & 0xFFu;
+        if (mx != 0.0f && (ey < 95u || ey > 158u)) flags |= kStGauge;
+        const uint32_t ec = ey < 3u ? 1u : ey - 2u;  // c = 2^(floor(log2 mx) - 2)
+        const float c = mx != 0.0f ? u2f(ec << 23) : 1.0f;
+        float S[8];
+        if (FMT == kMxFp4) {
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[2 * k], y[2 * k + 1], c, 0);
+            const auto s2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 0);
+            S[2 * k] = s2[0];
+            S[2 * k + 1] = s2[1];
+          }
+        } else {
+          const float ic = mx != 0.0f ? u2f((254u - ec) << 23) : 1.0f;  // 1 / c
+#pragma unroll
+          for (int k = 0; k < 8; k++) S[k] = fminf(fmaxf(rintf(y[k] * ic), -7.0f), 7.0f) * c;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const int e = 8 * h + k;
+          const float t = S[k] * bb[e];  // the reconstruction a d q b of W_ij, exact
+          const float df = w[k] - t;      // exact: both have at most 8 significant bits
+          nacc = fmaf(w[k], t, nacc);
+          dacc = fmaf(t, t, dacc);
+          eacc = fmaf(df, df, eacc);
+          P[e] = fmaf(w[k], S[k], P[e]);
+          Q[e] = fmaf(S[k], S[k], Q[e]);
+        }
+      }
+      nl[(step % kSteps) * kFusedLoad + r] = nacc;
+      dl[(step % kSteps) * kFusedLoad + r] = dacc;
+      el[(step % kSteps) * kFusedLoad + r] = eacc;
+    }
+    if (step % kSteps == kSteps - 1) {
+      // 8 rows done: transpose the 64 lane partials of each row through LDS; 8 lanes per
+      // row add 8 partials each in fp64, then across the 8 lanes in a fixed order
+      float4* R = smem4 + wave * (kFusedBatch * kWave);
+#pragma unroll
+      for (int r = 0; r < kFusedBatch; r++) R[r * kWave + lane] = make_float4(nl[r], dl[r], el[r], 0.0f);
+      __builtin_amdgcn_wave_barrier();
+      const float4* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
+      double N = 0.0, D = 0.0, Er = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const float4 v = src[k];
+        N += (double)v.x;
+        D += (double)v.y;
+        Er += (double)v.z;
+      }
+      N = sum8_dpp(N);
+      D = sum8_dpp(D);
+      Er = sum8_dpp(Er);
+      const int64_t i = row_of(step - (kSteps - 1), 0) + (lane >> 3);  // the batch's 8 rows
+      if ((lane & 7) == 0 && i < r_end) {
+        p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, D);
+        p.rowerr[(int64_t)ct * p.m + i] = Er;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedLoad; r++) {
+      cur[r][0] = nxt[r][0];
+      cur[r][1] = nxt[r][1];
+    }
+  }
+
+  // column partials: the 4 waves' fp32 sums added in fp64 in wave order
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; h++)
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      smem[wave * kFusedCols + h * kTileCols + lane * kEpl + k] = make_float2(P[8 * h + k], Q[8 * h + k]);
+  __syncthreads();
+  for (int c = threadIdx.x; c < kFusedCols; c += kBlock) {
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int v = 0; v < kWaves; v++) {
+      sp += (double)smem[v * kFusedCols + c].x;
+      sq += (double)smem[v * kFusedCols + c].y;
+    }
+    const int64_t j = (int64_t)ct * kFusedCols + c;
+    if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
+  }
+  atomic_flag(p.status, flags);
+}
+
 // ------------------------------------------------------------------------- row statistics
 // E_i = sum_j W_ij^2 (fp64, fixed order), a non-finite check on W, and optionally the row
 // max of |X| at the initial scales (NVFP4 tensor scale). One wave per row.
@@ -225,6 +414,7 @@ __global__ void k_vec(VecArgs p) {
     }
     if (p.project) v = project(p.fmt, (double)v);
   }
+  if (p.envelope && !(v >= 0x1p-24f && v <= 0x1p24f)) atomic_flag(p.status, kStGauge);
   p.dst[k] = v;
   p.rdst[k] = recip32(v);
   if (p.dst2) p.dst2[k] = v;
@@ -278,8 +468,17 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
         N += v.x;
         D += v.y;
       }
+      if (p.row_ra) {  // single-sweep row sums: R = ra_i * t
+        const double r = (double)p.ra[i];
+        N *= r;
+        D *= r * r;
+      }
       const double ai = (double)p.a[i];
-      err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
+      if (p.rowerr) {  // summed directly: no cancellation
+        for (int c = 0; c < p.nct; c++) err += p.rowerr[(int64_t)c * p.m + i];
+      } else {
+        err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
+      }
       if (p.update_a) {
         float an = 1.0f;  // an all-zero code slice keeps scale 1
         if (D > 0.0) {
@@ -290,6 +489,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
           const float ao = p.a[i];
           if (!(an == ao || an == 2.0f * ao || an == 0.5f * ao)) flags |= kStGauge;
         }
+        if (p.envelope && !(an >= 0x1p-24f && an <= 0x1p24f)) flags |= kStGauge;
         p.a[i] = an;
         p.ra[i] = recip32(an);
       }
@@ -330,6 +530,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
       if (!(N > 0.0)) atomicOr(p.status, kStInternal);
       bn = project(p.fmt, N / D);
     }
+    if (p.envelope && !(bn >= 0x1p-24f && bn <= 0x1p24f)) atomicOr(p.status, kStGauge);
     p.b[j] = bn;
     p.rb[j] = recip32(bn);
   }
@@ -365,6 +566,24 @@ hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s) {
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_finalize, dim3(a.nblk_rows + a.nblk_cols), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.G) {
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64>), grid, dim3(kBlock), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(int fmt, const FusedArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nct * a.nrc));
+  if (fmt == kMxFp4) return fused_group<kMxFp4>(a, grid, s);
+  if (fmt == kMxInt4) return fused_group<kMxInt4>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, bool BF>

@@ -74,4 +74,6 @@ def assert_parity(res: dict, exact: bool = False, name: str = "") -> None:
     if exact:
         assert res["a_flips"] == 0 and res["b_flips"] == 0 and res["code_diffs"] == 0, msg
         assert res["scales_equal"], msg
-        assert np.all(res["mse_rel"] <= 1e-9), msg
+        # every per-row error is a sum of nonnegative terms: fp32 over at most 16 exact
+        # squares per lane (relative error <= 15 u < 1e-6), fp64 above
+        assert np.all(res["mse_rel"] <= 1e-6), msg

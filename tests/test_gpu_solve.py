@@ -98,8 +98,11 @@ def test_single_sweep_equals_two_sweep(dq, fmt):
         fused = dq.solve(W, fmt, 32, 12, timing=True)
         general = dq.solve(W, fmt, 32, 12, two_sweep=True, timing=True)
         assert fused["used_fused"] and not general["used_fused"]
-        for k in ("a", "b", "codes", "scales", "mse"):
+        for k in ("a", "b", "codes", "scales"):
             assert np.array_equal(host(fused[k]), host(general[k])), (w.name, k)
+        # same errors summed in a different precision order (fp32 lane sums vs fp64)
+        mf, mg = host(fused["mse"]), host(general["mse"])
+        assert np.all(np.abs(mf - mg) <= 1e-6 * mg), (w.name, mf, mg)
 
 
 def test_single_sweep_falls_back_outside_its_range(dq, oracle_lib):
