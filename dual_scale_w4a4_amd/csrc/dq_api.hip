@@ -51,7 +51,7 @@ struct Plan {
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
-  size_t off_rowpart = 0, off_rowerr = 0, off_colpart = 0, off_msepart = 0, total = 0;
+  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, total = 0;
 };
 
 bool shape_ok(int64_t rows, int64_t cols, int group) {
@@ -84,7 +84,7 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
   p.f_nrc = (int)((m + p.f_rpc - 1) / p.f_rpc);
   p.nblk_rows = (int)((m + 255) / 256);
-  p.nblk_cols = (int)((n + 255) / 256);
+  p.nblk_cols = (int)((n + 31) / 32);  // finalize: 8 lanes per column
   size_t o = 0;
   p.off_status = o; o = align_up(o + 64);
   p.off_ra = o; o = align_up(o + sizeof(float) * m);
@@ -97,7 +97,6 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   const size_t rc_parts = (size_t)(p.nct > p.f_nct ? p.nct : p.f_nct);
   const size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
   p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
-  p.off_rowerr = o; o = align_up(o + sizeof(double) * (size_t)p.f_nct * m);
   p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
   p.off_msepart = o; o = align_up(o + sizeof(double) * p.nblk_rows);
   p.total = o;
@@ -284,7 +283,6 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.nrc = p.f_nrc;
   fu.rpc = p.f_rpc;
   fu.rowpart = rowpart;
-  fu.rowerr = at<double>(ws, p.off_rowerr);
   fu.colpart = colpart;
   fu.status = status;
 
@@ -301,7 +299,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       fa.gauge_check = 0;
       fa.row_ra = 1;
       fa.envelope = 1;
-      fa.rowerr = fu.rowerr;
+      fa.col_terms = (int)((p.f_rpc + 31) / 32 * 8);  // 8-row batches, 32 rows apart
       fa.nblk_cols = p.nblk_cols;
       tm.before(DQ_K_FINAL);
       DQ_TRY(launch_finalize(fa, s));
@@ -345,7 +343,6 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fa.nrc = p.nrc;
   fa.row_ra = 0;
   fa.envelope = 0;
-  fa.rowerr = nullptr;
   fa.mse_out = io.mse + io.T;
   fa.nblk_rows = p.nblk_rows;
   fa.update_a = 0;

@@ -267,6 +267,21 @@ __device__ __forceinline__ float group_max_dpp(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// max over aligned groups of LANES lanes of non-negative float bit patterns (for those the
+// unsigned order is the float order), no NaN canonicalization needed
+template <int LANES>
+__device__ __forceinline__ uint32_t group_max_bits(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  if (LANES > 2) v = max(v, dpp_u32<kDppQuadXor2>(v));
+  if (LANES > 4) v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  return v;
+}
+
 // sum over aligned groups of 8 lanes, fixed order, result in all 8 lanes
 __device__ __forceinline__ double sum8_dpp(double v) {
   v += dpp_f64<kDppQuadXor1>(v);

@@ -49,8 +49,7 @@ struct FusedArgs {
   int nct;          // column tiles of 1024 columns
   int nrc;          // row chunks
   int64_t rpc;      // rows per chunk
-  double2* rowpart;  // [nct][m] (sum_j W t, sum_j t^2) with t = S b: R = ra * t
-  double* rowerr;    // [nct][m] sum_j (W - t)^2
+  double2* rowpart;  // [nct][m] (sum_j W t, sum_j (W - t)^2) with t = S b: R = ra * t
   double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
   int* status;
 };
@@ -93,21 +92,21 @@ struct FinArgs {
   // rows
   int nblk_rows;
   const double2* rowpart;
-  const double* rowerr;  // per-tile row errors (single-sweep pass) or null: use E - 2aN + a^2 D
   int nct;
   const double* E;
   float* a;
   float* ra;
   int update_a;
   int gauge_check;
-  int row_ra;          // row sums lack the ra_i factor (single-sweep MX pass)
+  int row_ra;          // single-sweep MX sums: rowpart holds (N', e) with R = ra_i t
   int envelope;        // flag kStGauge if a new a or b leaves [2^-24, 2^24]
+  int col_terms;       // single-sweep: most rows one lane adds in fp32 for a column sum
   double* msepart;     // [nblk_rows]
   unsigned* counter;   // zero on entry, left zero on exit
   double* mse_out;     // one double
   double inv_mn;
   // cols
-  int nblk_cols;
+  int nblk_cols;        // blocks of 32 columns
   const double2* colpart;
   int nrc;
   float* b;

@@ -180,31 +180,101 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
 // Consequently the re-quantization after the row update reproduces the same codes and the
 // same S = a d q (daiwk notes, "核心公式": row update, re-quantize, column update), and one
 // read of W gives both closed-form updates:
-//   row i:    N'_i = sum_j W_ij t_ij,  D'_i = sum_j t_ij^2,  t = S b  (R = ra_i t)
-//             e_i = sum_j (W_ij - t_ij)^2, the row's reconstruction error (t = a d q b)
+//   row i:    N'_i = sum_j W_ij t_ij  with t = S b = a d q b, the reconstruction (R = ra_i t)
+//             e_i  = sum_j (W_ij - t_ij)^2, the row's reconstruction error; the finalize
+//                    recovers D'_i = sum_j t_ij^2 = e_i - E_i + 2 N'_i
 //   column j: P_j = sum_i W_ij S_ij,   Q_j = sum_i S_ij^2
 // This holds while every value stays in fp32's normal range with exact products, which is
 // guaranteed when every nonzero group max |y| lies in [2^-32, 2^32) and every a, b in
 // [2^-24, 2^24]; otherwise the pass raises kStGauge and the solve is redone on the general
-// two-sweep path. MXFP4 codes come from gfx950's scaled FP4 conversion, which rounds y / c
-// to the nearest E2M1 value (ties to even, saturating) exactly for power-of-two c; the
-// matching decode returns S = code * c directly.
+// two-sweep path (so does the finalize when a projection decision lies closer to a boundary
+// than the error bound of these sums). MXFP4 codes come from gfx950's scaled FP4
+// conversion, which rounds y / c to the nearest E2M1 value (ties to even, saturating) exactly
+// for power-of-two c; the matching decode returns S = code * c directly.
 //
 // Layout: a lane owns 16 columns of a 1024-column tile (two 512-column halves, each one
-// 128-bit load per row, contiguous across the wave). Products are exact in fp32; per-lane
-// sums run over 16 columns (rows) or over the chunk's rows (columns) in fp32; every sum
-// above that is fp64 in a fixed order: a row's 64 lane partials are transposed through LDS
+// 128-bit load per row, contiguous across the wave). Products and W - t are exact in fp32;
+// per-lane sums run over 16 columns (rows) or over the chunk's rows (columns) in fp32; every
+// sum above that is fp64 in a fixed order: a row's 64 lane partials are transposed through LDS
 // in batches of 8 rows and added by 8 lanes per row, and the 4 waves' column partials are
 // added through LDS at the end.
 constexpr int kFusedCols = 1024;
-constexpr int kFusedBatch = 8;  // rows per wave between row reductions
-constexpr int kFusedLoad = 2;   // rows per (double-buffered) load step
+constexpr int kFusedBatch = 8;  // rows per wave between row reductions (4 load steps of 2)
 
-template <int FMT, int G>
+struct FusedLane {
+  float rb[16], bb[16], P[16], Q[16];
+};
+
+// one row of 16 elements: codes, the row's partial sums, the column accumulators
+// One row of 16 elements: codes, the row's partial sums and the column accumulators.
+// PARTIAL: the tile extends past column n; amask[h] zeroes a half that lies past it.
+// gmax / gmin track the largest group max and the smallest nonzero one (as bit patterns,
+// gmin offset by one so that a zero group never counts) for the range check.
+template <int FMT, int LPG, bool PARTIAL>
+__device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, float& nacc,
+                                          float& eacc, uint32_t& gmax, uint32_t& gmin,
+                                          const uint32_t (&amask)[2]) {
+  nacc = 0.0f;
+  eacc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t u[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+    if (PARTIAL) {
+#pragma unroll
+      for (int k = 0; k < 4; k++) u[k] &= amask[h];
+    }
+    float w[8], y[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      w[2 * k] = u2f(u[k] << 16);
+      w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      y[k] = w[k] * L.rb[8 * h + k];
+      mx = fmaxf(mx, fabsf(y[k]));
+    }
+    const uint32_t mb = group_max_bits<LPG>(f2u(mx));
+    gmax = max(gmax, mb);
+    gmin = min(gmin, mb - 1u);  // a zero group wraps to 0xFFFFFFFF
+    // c = 2^(floor(log2 mx) - 2); an all-zero group gets a harmless normal c
+    const uint32_t cb = max(mb & 0x7F800000u, 3u << 23) - (2u << 23);
+    const float c = u2f(cb);
+    float S[8];
+    if (FMT == kMxFp4) {
+      uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], c, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[2], y[3], c, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[4], y[5], c, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[6], y[7], c, 3);
+      const auto s0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 0);
+      const auto s1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 1);
+      const auto s2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 2);
+      const auto s3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 3);
+      S[0] = s0[0]; S[1] = s0[1]; S[2] = s1[0]; S[3] = s1[1];
+      S[4] = s2[0]; S[5] = s2[1]; S[6] = s3[0]; S[7] = s3[1];
+    } else {
+      const float ic = u2f((254u << 23) - cb);  // 1 / c
+#pragma unroll
+      for (int k = 0; k < 8; k++) S[k] = fminf(fmaxf(rintf(y[k] * ic), -7.0f), 7.0f) * c;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int e = 8 * h + k;
+      const float t = S[k] * L.bb[e];  // the reconstruction a d q b of W_ij, exact
+      const float df = w[k] - t;       // exact: both have at most 8 significant bits
+      nacc = fmaf(w[k], t, nacc);
+      eacc = fmaf(df, df, eacc);
+      L.P[e] = fmaf(w[k], S[k], L.P[e]);
+      L.Q[e] = fmaf(S[k], S[k], L.Q[e]);
+    }
+  }
+}
+
+template <int FMT, int G, bool PARTIAL>
 __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   constexpr int LPG = G / kEpl;  // lanes per group
-  __shared__ float4 smem4[kWaves * kFusedBatch * kWave];  // 32 KiB, two views
-  float2* smem = reinterpret_cast<float2*>(smem4);
+  __shared__ float2 smem[kWaves * kFusedCols];  // 32 KiB: row transposes, then column sums
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -215,130 +285,94 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   const int64_t col[2] = {(int64_t)ct * kFusedCols + lane * kEpl,
                           (int64_t)ct * kFusedCols + kTileCols + lane * kEpl};
   const bool act[2] = {col[0] < p.n, col[1] < p.n};
+  const int64_t lcol[2] = {act[0] ? col[0] : 0, act[1] ? col[1] : 0};  // in-bounds addresses
 
-  float rb[16], bb[16], P[16], Q[16];
+  FusedLane L;
 #pragma unroll
-  for (int h = 0; h < 2; h++)
+  for (int h = 0; h < 2; h++) {
+    const float4* rbp = reinterpret_cast<const float4*>(p.rb + lcol[h]);
+    const float4* bbp = reinterpret_cast<const float4*>(p.b + lcol[h]);
+    const float4 r0 = rbp[0], r1 = rbp[1], b0 = bbp[0], b1 = bbp[1];
+    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      rb[8 * h + k] = act[h] ? p.rb[col[h] + k] : 1.0f;
-      bb[8 * h + k] = act[h] ? p.b[col[h] + k] : 0.0f;
-      P[8 * h + k] = Q[8 * h + k] = 0.0f;
+      L.rb[8 * h + k] = act[h] ? rr[k] : 1.0f;
+      L.bb[8 * h + k] = act[h] ? bv[k] : 0.0f;
+      L.P[8 * h + k] = L.Q[8 * h + k] = 0.0f;
     }
-  int flags = 0;
+  }
+  uint32_t gmax = 0u, gmin = 0xFFFFFFFFu;
 
   // this wave's rows: batches of 8 consecutive rows, 32 rows apart across the workgroup
   const int64_t first = r_begin + (int64_t)wave * kFusedBatch;
-  const int64_t nbatch = first < r_end ? (r_end - first + kWaves * kFusedBatch - 1) /
-                                             (kWaves * kFusedBatch) : 0;
-  constexpr int kSteps = kFusedBatch / kFusedLoad;  // load steps per batch
-  const int64_t nsteps = nbatch * kSteps;
-  auto row_of = [&](int64_t step, int r) -> int64_t {
-    return first + (step / kSteps) * (kWaves * kFusedBatch) + (step % kSteps) * kFusedLoad + r;
+  const int64_t nbatch =
+      first < r_end ? (r_end - first + kWaves * kFusedBatch - 1) / (kWaves * kFusedBatch) : 0;
+  // loads of rows i, i+1 from in-bounds addresses (rows past the chunk reload its first row
+  // and are skipped below; columns past n are masked in fused_row)
+  auto load2 = [&](int64_t i, uint4 (&buf)[2][2]) {
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      const int64_t row = i + r < r_end ? i + r : r_begin;
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        buf[r][h] = *reinterpret_cast<const uint4*>(p.W + row * p.n + lcol[h]);
+    }
   };
-  auto load_step = [&](int64_t step, uint4 (&buf)[kFusedLoad][2]) {
-#pragma unroll
-    for (int r = 0; r < kFusedLoad; r++) {
-      const int64_t i = row_of(step, r);
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        if (i < r_end && act[h])
-          buf[r][h] = *reinterpret_cast<const uint4*>(p.W + i * p.n + col[h]);
-        else
-          buf[r][h] = make_uint4(0u, 0u, 0u, 0u);
-      }
+  const uint32_t amask[2] = {act[0] ? 0xFFFFFFFFu : 0u, act[1] ? 0xFFFFFFFFu : 0u};
+  // one row, skipped (uniformly) when it lies past the chunk
+  auto row_step = [&](const uint4 (&v)[2], int64_t i, float& n_out, float& e_out) {
+    if (i < r_end) {
+      fused_row<FMT, LPG, PARTIAL>(v, L, n_out, e_out, gmax, gmin, amask);
+    } else {
+      n_out = 0.0f;
+      e_out = 0.0f;
     }
   };
 
-  uint4 cur[kFusedLoad][2], nxt[kFusedLoad][2];
-  if (nsteps > 0) load_step(0, cur);
-  float nl[kFusedBatch], dl[kFusedBatch], el[kFusedBatch];
-  for (int64_t step = 0; step < nsteps; step++) {
-    if (step + 1 < nsteps) load_step(step + 1, nxt);
+  uint4 bufA[2][2], bufB[2][2];
+  if (nbatch > 0) load2(first, bufA);
+  for (int64_t bt = 0; bt < nbatch; bt++) {
+    const int64_t row0 = first + bt * (kWaves * kFusedBatch);
+    float nl[kFusedBatch], el[kFusedBatch];
+    // each step issues the next two rows' loads, then computes two rows; the scheduling
+    // barriers keep the compiler from interleaving steps (register pressure)
+    load2(row0 + 2, bufB);
+    row_step(bufA[0], row0 + 0, nl[0], el[0]);
+    row_step(bufA[1], row0 + 1, nl[1], el[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load2(row0 + 4, bufA);
+    row_step(bufB[0], row0 + 2, nl[2], el[2]);
+    row_step(bufB[1], row0 + 3, nl[3], el[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    load2(row0 + 6, bufB);
+    row_step(bufA[0], row0 + 4, nl[4], el[4]);
+    row_step(bufA[1], row0 + 5, nl[5], el[5]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (bt + 1 < nbatch) load2(row0 + kWaves * kFusedBatch, bufA);
+    row_step(bufB[0], row0 + 6, nl[6], el[6]);
+    row_step(bufB[1], row0 + 7, nl[7], el[7]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 8 rows done: transpose the 64 lane partials of each row through LDS; 8 lanes per row
+    // add 8 partials each in fp64, then across the 8 lanes in a fixed order
+    float2* R = smem + wave * (kFusedBatch * kWave);
 #pragma unroll
-    for (int r = 0; r < kFusedLoad; r++) {
-      float nacc = 0.0f, dacc = 0.0f, eacc = 0.0f;
+    for (int r = 0; r < kFusedBatch; r++) R[r * kWave + lane] = make_float2(nl[r], el[r]);
+    __builtin_amdgcn_wave_barrier();
+    const float2* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
+    double N = 0.0, Er = 0.0;
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const uint32_t u[4] = {cur[r][h].x, cur[r][h].y, cur[r][h].z, cur[r][h].w};
-        float w[8], y[8];
-        float mx = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          w[2 * k] = u2f(u[k] << 16);
-          w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          y[k] = w[k] * rb[8 * h + k];
-          mx = fmaxf(mx, fabsf(y[k]));
-        }
-        mx = group_max_dpp<LPG>(mx);
-        const uint32_t ey = (f2u(mx) >> 23) & 0xFFu;
-        if (mx != 0.0f && (ey < 95u || ey > 158u)) flags |= kStGauge;
-        const uint32_t ec = ey < 3u ? 1u : ey - 2u;  // c = 2^(floor(log2 mx) - 2)
-        const float c = mx != 0.0f ? u2f(ec << 23) : 1.0f;
-        float S[8];
-        if (FMT == kMxFp4) {
-#pragma unroll
-          for (int k = 0; k < 4; k++) {
-            const uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[2 * k], y[2 * k + 1], c, 0);
-            const auto s2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 0);
-            S[2 * k] = s2[0];
-            S[2 * k + 1] = s2[1];
-          }
-        } else {
-          const float ic = mx != 0.0f ? u2f((254u - ec) << 23) : 1.0f;  // 1 / c
-#pragma unroll
-          for (int k = 0; k < 8; k++) S[k] = fminf(fmaxf(rintf(y[k] * ic), -7.0f), 7.0f) * c;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const int e = 8 * h + k;
-          const float t = S[k] * bb[e];  // the reconstruction a d q b of W_ij, exact
-          const float df = w[k] - t;      // exact: both have at most 8 significant bits
-          nacc = fmaf(w[k], t, nacc);
-          dacc = fmaf(t, t, dacc);
-          eacc = fmaf(df, df, eacc);
-          P[e] = fmaf(w[k], S[k], P[e]);
-          Q[e] = fmaf(S[k], S[k], Q[e]);
-        }
-      }
-      nl[(step % kSteps) * kFusedLoad + r] = nacc;
-      dl[(step % kSteps) * kFusedLoad + r] = dacc;
-      el[(step % kSteps) * kFusedLoad + r] = eacc;
+    for (int k = 0; k < 8; k++) {
+      const float2 v = src[k];
+      N += (double)v.x;
+      Er += (double)v.y;
     }
-    if (step % kSteps == kSteps - 1) {
-      // 8 rows done: transpose the 64 lane partials of each row through LDS; 8 lanes per
-      // row add 8 partials each in fp64, then across the 8 lanes in a fixed order
-      float4* R = smem4 + wave * (kFusedBatch * kWave);
-#pragma unroll
-      for (int r = 0; r < kFusedBatch; r++) R[r * kWave + lane] = make_float4(nl[r], dl[r], el[r], 0.0f);
-      __builtin_amdgcn_wave_barrier();
-      const float4* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
-      double N = 0.0, D = 0.0, Er = 0.0;
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const float4 v = src[k];
-        N += (double)v.x;
-        D += (double)v.y;
-        Er += (double)v.z;
-      }
-      N = sum8_dpp(N);
-      D = sum8_dpp(D);
-      Er = sum8_dpp(Er);
-      const int64_t i = row_of(step - (kSteps - 1), 0) + (lane >> 3);  // the batch's 8 rows
-      if ((lane & 7) == 0 && i < r_end) {
-        p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, D);
-        p.rowerr[(int64_t)ct * p.m + i] = Er;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int r = 0; r < kFusedLoad; r++) {
-      cur[r][0] = nxt[r][0];
-      cur[r][1] = nxt[r][1];
-    }
+    N = sum8_dpp(N);
+    Er = sum8_dpp(Er);
+    const int64_t i = row0 + (lane >> 3);
+    if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, Er);
+    __builtin_amdgcn_wave_barrier();
   }
 
   // column partials: the 4 waves' fp32 sums added in fp64 in wave order
@@ -347,7 +381,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   for (int h = 0; h < 2; h++)
 #pragma unroll
     for (int k = 0; k < 8; k++)
-      smem[wave * kFusedCols + h * kTileCols + lane * kEpl + k] = make_float2(P[8 * h + k], Q[8 * h + k]);
+      smem[wave * kFusedCols + h * kTileCols + lane * kEpl + k] =
+          make_float2(L.P[8 * h + k], L.Q[8 * h + k]);
   __syncthreads();
   for (int c = threadIdx.x; c < kFusedCols; c += kBlock) {
     double sp = 0.0, sq = 0.0;
@@ -359,7 +394,9 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     const int64_t j = (int64_t)ct * kFusedCols + c;
     if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
   }
-  atomic_flag(p.status, flags);
+  // range check: every nonzero group max in [2^-32, 2^32)
+  const bool bad = gmax >= 0x4F800000u || (gmin != 0xFFFFFFFFu && gmin + 1u < 0x2F800000u);
+  atomic_flag(p.status, bad ? kStGauge : 0);
 }
 
 // ------------------------------------------------------------------------- row statistics
@@ -450,9 +487,44 @@ __global__ __launch_bounds__(256) void k_tensor_scale(ScaleArgs p) {
   }
 }
 
+// Relative distance of v > 0 from the nearest decision point of the E8M0 projection
+// (1.5 * 2^k). The single-sweep sums are trusted only where it exceeds twice their error
+// bound, so that the decision is the one exact sums would give.
+__device__ __forceinline__ double e8m0_margin(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const double f = __builtin_bit_cast(double, (u & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull);
+  return fabs(f - 1.5) / f;  // f in [1, 2): the mantissa of v
+}
+// Worst-case relative error of one fp32 sum of k nonnegative terms is k * 2^-24; the
+// single-sweep lane sums run over 16 columns (row sums) and FinArgs::col_terms rows
+// (column sums).
+constexpr double kRowSumErr = 16.0 * 0x1p-24;
+
+// sum of cnt double2 partials at base, base + stride, ... in index order, loads issued first
+__device__ __forceinline__ double2 sum_parts(const double2* base, int64_t stride, int first,
+                                             int step, int cnt) {
+  double N = 0.0, D = 0.0;
+  constexpr int kU = 8;
+  for (int k0 = first; k0 < cnt; k0 += kU * step) {
+    double2 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int k = k0 + u * step;
+      v[u] = k < cnt ? base[(int64_t)k * stride] : make_double2(0.0, 0.0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      N += v[u].x;
+      D += v[u].y;
+    }
+  }
+  return make_double2(N, D);
+}
+
 // Closed-form updates (eq. 2) and projections, plus the mse of the state the row sums were
-// taken at: e_i = E_i - 2 a_i N_i + a_i^2 D_i, summed per block in fixed order and over the
-// blocks by the last block to finish (integer counter; fixed summation order).
+// taken at, e_i = E_i - 2 a_i N_i + a_i^2 D_i (or the directly summed row error). Per block
+// the row errors are added in a fixed tree order; the blocks' sums are added by the last
+// block to finish (integer counter), again in a fixed order.
 __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
   __shared__ double red[256];
   __shared__ int is_last;
@@ -462,20 +534,19 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
     double err = 0.0;
     int flags = 0;
     if (i < p.m) {
-      double N = 0.0, D = 0.0;
-      for (int c = 0; c < p.nct; c++) {
-        const double2 v = p.rowpart[(int64_t)c * p.m + i];
-        N += v.x;
-        D += v.y;
-      }
-      if (p.row_ra) {  // single-sweep row sums: R = ra_i * t
-        const double r = (double)p.ra[i];
-        N *= r;
-        D *= r * r;
-      }
+      const double2 nd = sum_parts(p.rowpart + i, p.m, 0, 1, p.nct);
+      double N = nd.x, D = nd.y;
+      double rel_err = 0.0;  // error bound of N / D (single-sweep sums only)
       const double ai = (double)p.a[i];
-      if (p.rowerr) {  // summed directly: no cancellation
-        for (int c = 0; c < p.nct; c++) err += p.rowerr[(int64_t)c * p.m + i];
+      if (p.row_ra) {
+        // single-sweep sums: (N', e) with R = ra_i t; D' = e - E + 2 N' (all terms >= 0)
+        const double e = D, Np = N;
+        err = e;
+        const double Dp = fmax(e - p.E[i] + 2.0 * Np, 0.0);
+        const double r = (double)p.ra[i];
+        N = Np * r;
+        D = Np > 0.0 ? Dp * r * r : 0.0;  // N' = 0 exactly when every code is 0
+        rel_err = kRowSumErr * (1.0 + (e + p.E[i] + 2.0 * Np) / fmax(Dp, 1e-300));
       } else {
         err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
       }
@@ -484,6 +555,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
         if (D > 0.0) {
           if (!(N > 0.0)) flags |= kStInternal;
           an = project(p.fmt, N / D);
+          if (p.row_ra && e8m0_margin(N / D) < 2.0 * rel_err) flags |= kStGauge;
         }
         if (p.gauge_check) {
           const float ao = p.a[i];
@@ -508,27 +580,37 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
       is_last = prev == (unsigned)(p.nblk_rows - 1);
     }
     __syncthreads();
-    if (is_last && tid == 0) {
+    if (is_last) {  // block-uniform
       __threadfence();
       double s = 0.0;
-      for (int k = 0; k < p.nblk_rows; k++)
+      for (int k = tid; k < p.nblk_rows; k += 256)  // each thread: blocks tid, tid + 256, ...
         s += __hip_atomic_load(&p.msepart[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *p.mse_out = s * p.inv_mn;
-      __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      red[tid] = s;
+      __syncthreads();
+      for (int st = 128; st > 0; st >>= 1) {
+        if (tid < st) red[tid] += red[tid + st];
+        __syncthreads();
+      }
+      if (tid == 0) {
+        *p.mse_out = red[0] * p.inv_mn;
+        __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   } else {
-    const int64_t j = (int64_t)(blockIdx.x - p.nblk_rows) * 256 + tid;
-    if (j >= p.n) return;
-    double N = 0.0, D = 0.0;
-    for (int k = 0; k < p.nrc; k++) {
-      const double2 v = p.colpart[(int64_t)k * p.n + j];
-      N += v.x;
-      D += v.y;
-    }
+    // 8 lanes per column: lane s adds partials s, s + 8, ... in order, then a fixed tree
+    const int64_t j = (int64_t)(blockIdx.x - p.nblk_rows) * 32 + tid / 8;
+    const int sub = tid & 7;
+    double2 nd = make_double2(0.0, 0.0);
+    if (j < p.n) nd = sum_parts(p.colpart + j, p.n, sub, 8, p.nrc);
+    const double N = sum8_dpp(nd.x);
+    const double D = sum8_dpp(nd.y);
+    if (j >= p.n || sub != 0) return;
     float bn = 1.0f;
     if (D > 0.0) {
       if (!(N > 0.0)) atomicOr(p.status, kStInternal);
       bn = project(p.fmt, N / D);
+      // N and D each carry at most col_terms * 2^-24 relative error
+      if (p.row_ra && e8m0_margin(N / D) < 4.0 * p.col_terms * 0x1p-24) atomicOr(p.status, kStGauge);
     }
     if (p.envelope && !(bn >= 0x1p-24f && bn <= 0x1p24f)) atomicOr(p.status, kStGauge);
     p.b[j] = bn;
@@ -568,12 +650,12 @@ hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool PARTIAL>
 static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
   switch (a.G) {
-    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -581,8 +663,11 @@ static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_fused(int fmt, const FusedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.nct * a.nrc));
-  if (fmt == kMxFp4) return fused_group<kMxFp4>(a, grid, s);
-  if (fmt == kMxInt4) return fused_group<kMxInt4>(a, grid, s);
+  const bool partial = a.n % kFusedCols != 0;  // masking only when some tile is partial
+  if (fmt == kMxFp4)
+    return partial ? fused_group<kMxFp4, true>(a, grid, s) : fused_group<kMxFp4, false>(a, grid, s);
+  if (fmt == kMxInt4)
+    return partial ? fused_group<kMxInt4, true>(a, grid, s) : fused_group<kMxInt4, false>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
