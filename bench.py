@@ -65,6 +65,9 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 512 MiB device-to-device copies (the reference that "
+                         "scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the solver runs each matrix on a single device "
@@ -74,6 +77,16 @@ def main() -> None:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 512 << 20, "copies": args.steps}), flush=True)
+        return
 
     import dual_scale_w4a4_amd as dq
 

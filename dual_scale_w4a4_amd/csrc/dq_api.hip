@@ -98,12 +98,12 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   const size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
   p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
   p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
-  p.off_msepart = o; o = align_up(o + sizeof(double) * p.nblk_rows);
+  p.off_msepart = o; o = align_up(o + 2 * sizeof(double) * p.nblk_rows);
   p.total = o;
   return p;
 }
 
-// workspace status words: [0] device flags, [1] mse block counter
+// workspace status word [0]: device flags
 template <class T>
 T* at(char* base, size_t off) {
   return reinterpret_cast<T*>(base + off);
@@ -205,7 +205,6 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
                         Timer& tm, hipStream_t s) {
   using namespace dq;
   int* status = at<int>(ws, p.off_status);
-  unsigned* counter = reinterpret_cast<unsigned*>(status + 1);
   float* ra = at<float>(ws, p.off_ra);
   float* rb = at<float>(ws, p.off_rb);
   double* E = at<double>(ws, p.off_E);
@@ -213,7 +212,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   float* gs = at<float>(ws, p.off_gs);
   double2* rowpart = at<double2>(ws, p.off_rowpart);
   double2* colpart = at<double2>(ws, p.off_colpart);
-  double* msepart = at<double>(ws, p.off_msepart);
+  double* msepart = at<double>(ws, p.off_msepart);  // two sets of per-block error sums
   const bool nv = p.fmt == kNvFp4;
 
   tm.before(DQ_K_SETUP);
@@ -259,18 +258,15 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fa.n = p.n;
   fa.fmt = p.fmt;
   fa.rowpart = rowpart;
-  fa.nct = p.nct;
   fa.E = E;
   fa.a = io.a;
   fa.ra = ra;
-  fa.msepart = msepart;
-  fa.counter = counter;
   fa.inv_mn = 1.0 / ((double)p.m * (double)p.n);
   fa.colpart = colpart;
-  fa.nrc = p.nrc;
   fa.b = io.b;
   fa.rb = rb;
   fa.status = status;
+  fa.prev_count = p.nblk_rows;
 
   FusedArgs fu{};
   fu.W = static_cast<const uint16_t*>(io.W);
@@ -284,72 +280,83 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.rpc = p.f_rpc;
   fu.rowpart = rowpart;
   fu.colpart = colpart;
+  fu.codes = io.codes;
+  fu.scales = static_cast<uint8_t*>(io.scales);
+  fu.a = io.a;
   fu.status = status;
 
+  // mse[t]: a finalize that takes row sums writes per-block error sums into one of two
+  // buffers; the next finalize (or the final collect) adds them up into mse[t]
+  int produced = 0, pend_idx = -1;
+  auto finalize = [&](bool rows, bool cols, bool update) -> dq_status {
+    fa.nblk_rows = rows ? p.nblk_rows : 0;
+    fa.nblk_cols = cols ? p.nblk_cols : 0;
+    fa.update_a = update ? 1 : 0;
+    fa.prev_part = pend_idx >= 0 ? msepart + (size_t)(pend_idx % 2) * p.nblk_rows : nullptr;
+    fa.prev_out = pend_idx >= 0 ? io.mse + pend_idx : nullptr;
+    pend_idx = -1;
+    fa.part_out = nullptr;
+    if (rows) {
+      fa.part_out = msepart + (size_t)(produced % 2) * p.nblk_rows;
+      pend_idx = produced++;
+    }
+    tm.before(DQ_K_FINAL);
+    DQ_TRY(launch_finalize(fa, s));
+    tm.after();
+    return DQ_OK;
+  };
+  dq_status st = DQ_OK;
+
   for (int t = 0; t < io.T; t++) {
-    fa.mse_out = io.mse + t;
     if (fast) {
       tm.before(DQ_K_FUSED);
-      DQ_TRY(launch_fused(p.fmt, fu, s));
+      DQ_TRY(launch_fused(p.fmt, false, fu, s));
       tm.after();
       fa.nct = p.f_nct;
       fa.nrc = p.f_nrc;
-      fa.nblk_rows = p.nblk_rows;
-      fa.update_a = 1;
       fa.gauge_check = 0;
       fa.row_ra = 1;
       fa.envelope = 1;
       fa.col_terms = (int)((p.f_rpc + 31) / 32 * 8);  // 8-row batches, 32 rows apart
-      fa.nblk_cols = p.nblk_cols;
-      tm.before(DQ_K_FINAL);
-      DQ_TRY(launch_finalize(fa, s));
-      tm.after();
+      if ((st = finalize(true, true, true)) != DQ_OK) return st;
     } else if (fused) {
       tm.before(DQ_K_FUSED);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow | kModeCol | kModeGauge, sw, s));
       tm.after();
-      fa.nblk_rows = p.nblk_rows;
-      fa.update_a = 1;
+      fa.nct = p.nct;
+      fa.nrc = p.nrc;
       fa.gauge_check = 1;
-      fa.nblk_cols = p.nblk_cols;
-      tm.before(DQ_K_FINAL);
-      DQ_TRY(launch_finalize(fa, s));
-      tm.after();
+      if ((st = finalize(true, true, true)) != DQ_OK) return st;
     } else {
       tm.before(DQ_K_ROW);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow, sw, s));
       tm.after();
-      fa.nblk_rows = p.nblk_rows;
-      fa.update_a = 1;
-      fa.gauge_check = 0;
-      fa.nblk_cols = 0;
-      tm.before(DQ_K_FINAL);
-      DQ_TRY(launch_finalize(fa, s));
-      tm.after();
+      fa.nct = p.nct;
+      fa.nrc = p.nrc;
+      if ((st = finalize(true, false, true)) != DQ_OK) return st;
       tm.before(DQ_K_COL);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeCol, sw, s));
       tm.after();
-      fa.nblk_rows = 0;
-      fa.nblk_cols = p.nblk_cols;
-      tm.before(DQ_K_FINAL);
-      DQ_TRY(launch_finalize(fa, s));
-      tm.after();
+      if ((st = finalize(false, true, false)) != DQ_OK) return st;
     }
   }
   tm.before(DQ_K_EMIT);
-  DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeEmit | kModeRow, sw, s));
+  if (fast) {
+    DQ_TRY(launch_fused(p.fmt, true, fu, s));
+    fa.nct = p.f_nct;
+    fa.row_ra = 1;
+  } else {
+    DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeEmit | kModeRow, sw, s));
+    fa.nct = p.nct;
+    fa.row_ra = 0;
+  }
   tm.after();
-  fa.nct = p.nct;
-  fa.nrc = p.nrc;
-  fa.row_ra = 0;
   fa.envelope = 0;
-  fa.mse_out = io.mse + io.T;
-  fa.nblk_rows = p.nblk_rows;
-  fa.update_a = 0;
   fa.gauge_check = 0;
-  fa.nblk_cols = 0;
+  if ((st = finalize(true, false, false)) != DQ_OK) return st;
   tm.before(DQ_K_FINAL);
-  DQ_TRY(launch_finalize(fa, s));
+  DQ_TRY(launch_mse_collect(msepart + (size_t)(pend_idx % 2) * p.nblk_rows, p.nblk_rows,
+                            io.mse + pend_idx, fa.inv_mn, s));
   tm.after();
   return DQ_OK;
 }

@@ -51,6 +51,10 @@ struct FusedArgs {
   int64_t rpc;      // rows per chunk
   double2* rowpart;  // [nct][m] (sum_j W t, sum_j (W - t)^2) with t = S b: R = ra * t
   double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
+  // final pass only: packed codes, E8M0 inner scales, the outer row scales
+  uint8_t* codes;
+  uint8_t* scales;
+  const float* a;
   int* status;
 };
 
@@ -101,9 +105,10 @@ struct FinArgs {
   int row_ra;          // single-sweep MX sums: rowpart holds (N', e) with R = ra_i t
   int envelope;        // flag kStGauge if a new a or b leaves [2^-24, 2^24]
   int col_terms;       // single-sweep: most rows one lane adds in fp32 for a column sum
-  double* msepart;     // [nblk_rows]
-  unsigned* counter;   // zero on entry, left zero on exit
-  double* mse_out;     // one double
+  double* part_out;         // per-block row-error sums of this launch, or null
+  const double* prev_part;  // a previous launch's block sums to finish, or null
+  int prev_count;
+  double* prev_out;         // where their mean goes
   double inv_mn;
   // cols
   int nblk_cols;        // blocks of 32 columns
@@ -120,6 +125,8 @@ hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
-hipError_t launch_fused(int fmt, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);
+hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,
+                              hipStream_t s);
 
 }  // namespace dq

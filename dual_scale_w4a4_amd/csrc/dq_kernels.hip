@@ -210,10 +210,13 @@ struct FusedLane {
 // PARTIAL: the tile extends past column n; amask[h] zeroes a half that lies past it.
 // gmax / gmin track the largest group max and the smallest nonzero one (as bit patterns,
 // gmin offset by one so that a zero group never counts) for the range check.
-template <int FMT, int LPG, bool PARTIAL>
+// EMIT: the final pass; instead of the sums for the updates it stores the packed codes and
+// the E8M0 inner-scale bytes of the row (ka = log2 a_i) and keeps only the row error.
+template <int FMT, int LPG, bool PARTIAL, bool EMIT>
 __device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, float& nacc,
                                           float& eacc, uint32_t& gmax, uint32_t& gmin,
-                                          const uint32_t (&amask)[2]) {
+                                          const uint32_t (&amask)[2], uint32_t* codes_row,
+                                          uint8_t* scales_row, uint32_t abits) {
   nacc = 0.0f;
   eacc = 0.0f;
 #pragma unroll
@@ -242,6 +245,7 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, flo
     const uint32_t cb = max(mb & 0x7F800000u, 3u << 23) - (2u << 23);
     const float c = u2f(cb);
     float S[8];
+    uint32_t packed = 0;  // the 8 codes as nibbles, column 2k low (EMIT)
     if (FMT == kMxFp4) {
       uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], c, 0);
       pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[2], y[3], c, 1);
@@ -253,25 +257,44 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, flo
       const auto s3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, c, 3);
       S[0] = s0[0]; S[1] = s0[1]; S[2] = s1[0]; S[3] = s1[1];
       S[4] = s2[0]; S[5] = s2[1]; S[6] = s3[0]; S[7] = s3[1];
+      if (EMIT) {  // keep the sign bit only where the magnitude is nonzero (no -0 code)
+        const uint32_t mag = pk & 0x77777777u;
+        const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
+        packed = mag | (pk & nz);
+      }
     } else {
       const float ic = u2f((254u << 23) - cb);  // 1 / c
 #pragma unroll
-      for (int k = 0; k < 8; k++) S[k] = fminf(fmaxf(rintf(y[k] * ic), -7.0f), 7.0f) * c;
+      for (int k = 0; k < 8; k++) {
+        const float q = fminf(fmaxf(rintf(y[k] * ic), -7.0f), 7.0f);
+        S[k] = q * c;
+        if (EMIT) packed |= ((uint32_t)(int)q & 0xFu) << (4 * k);
+      }
+    }
+    if (EMIT && (!PARTIAL || amask[h] != 0u)) {  // store inside the matrix only
+      codes_row[h * (kTileCols / 8)] = packed;  // this lane's 8 columns of half h
+      if ((__lane_id() % LPG) == 0) {
+        // E8M0 byte e + 127 with e = floor(log2(mx * ra_i)) - 2 = E(mx) - 129 - log2 a_i
+        const uint32_t ey = (mb >> 23) & 0xFFu;
+        scales_row[h * (kTileCols / (8 * LPG))] = (uint8_t)(mb == 0u ? 127u : ey + 125u - (abits >> 23));
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       const int e = 8 * h + k;
       const float t = S[k] * L.bb[e];  // the reconstruction a d q b of W_ij, exact
       const float df = w[k] - t;       // exact: both have at most 8 significant bits
-      nacc = fmaf(w[k], t, nacc);
       eacc = fmaf(df, df, eacc);
-      L.P[e] = fmaf(w[k], S[k], L.P[e]);
-      L.Q[e] = fmaf(S[k], S[k], L.Q[e]);
+      if (!EMIT) {
+        nacc = fmaf(w[k], t, nacc);
+        L.P[e] = fmaf(w[k], S[k], L.P[e]);
+        L.Q[e] = fmaf(S[k], S[k], L.Q[e]);
+      }
     }
   }
 }
 
-template <int FMT, int G, bool PARTIAL>
+template <int FMT, int G, bool PARTIAL, bool EMIT>
 __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   constexpr int LPG = G / kEpl;  // lanes per group
   __shared__ float2 smem[kWaves * kFusedCols];  // 32 KiB: row transposes, then column sums
@@ -323,7 +346,16 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   // one row, skipped (uniformly) when it lies past the chunk
   auto row_step = [&](const uint4 (&v)[2], int64_t i, float& n_out, float& e_out) {
     if (i < r_end) {
-      fused_row<FMT, LPG, PARTIAL>(v, L, n_out, e_out, gmax, gmin, amask);
+      uint32_t* codes_row = nullptr;
+      uint8_t* scales_row = nullptr;
+      uint32_t abits = 0u;
+      if (EMIT) {
+        codes_row = reinterpret_cast<uint32_t*>(p.codes) + ((i * p.n + col[0]) >> 3);
+        scales_row = p.scales + i * (p.n / G) + col[0] / G;
+        abits = f2u(p.a[i]);
+      }
+      fused_row<FMT, LPG, PARTIAL, EMIT>(v, L, n_out, e_out, gmax, gmin, amask, codes_row,
+                                         scales_row, abits);
     } else {
       n_out = 0.0f;
       e_out = 0.0f;
@@ -376,6 +408,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   }
 
   // column partials: the 4 waves' fp32 sums added in fp64 in wave order
+  if (!EMIT) {
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; h++)
@@ -393,6 +426,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     }
     const int64_t j = (int64_t)ct * kFusedCols + c;
     if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
+  }
   }
   // range check: every nonzero group max in [2^-32, 2^32)
   const bool bad = gmax >= 0x4F800000u || (gmin != 0xFFFFFFFFu && gmin + 1u < 0x2F800000u);
@@ -521,14 +555,39 @@ __device__ __forceinline__ double2 sum_parts(const double2* base, int64_t stride
   return make_double2(N, D);
 }
 
-// Closed-form updates (eq. 2) and projections, plus the mse of the state the row sums were
+// mean of the per-block error sums: thread k adds blocks k, k + 256, ..., then a fixed tree
+__device__ void mse_collect(const double* part, int count, double* out, double inv_mn,
+                            double* red) {
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  for (int k = tid; k < count; k += 256) s += part[k];
+  red[tid] = s;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) *out = red[0] * inv_mn;
+}
+
+__global__ __launch_bounds__(256) void k_mse_collect(const double* part, int count, double* out,
+                                                     double inv_mn) {
+  __shared__ double red[256];
+  mse_collect(part, count, out, inv_mn, red);
+}
+
+// Closed-form updates (eq. 2) and projections, plus the error of the state the row sums were
 // taken at, e_i = E_i - 2 a_i N_i + a_i^2 D_i (or the directly summed row error). Per block
-// the row errors are added in a fixed tree order; the blocks' sums are added by the last
-// block to finish (integer counter), again in a fixed order.
+// the row errors are added in a fixed tree order into part_out; the next finalize (or a
+// final collect kernel) adds the block sums in a fixed order.
 __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
   __shared__ double red[256];
-  __shared__ int is_last;
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && p.prev_out) {
+    // the previous finalize's per-block error sums (visible across the kernel boundary)
+    mse_collect(p.prev_part, p.prev_count, p.prev_out, p.inv_mn, red);
+    __syncthreads();
+  }
   if ((int)blockIdx.x < p.nblk_rows) {
     const int64_t i = (int64_t)blockIdx.x * 256 + tid;
     double err = 0.0;
@@ -573,29 +632,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
       __syncthreads();
     }
     if (flags) atomicOr(p.status, flags);
-    if (tid == 0) {
-      __hip_atomic_store(&p.msepart[blockIdx.x], red[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
-      const unsigned prev = atomicAdd(p.counter, 1u);
-      is_last = prev == (unsigned)(p.nblk_rows - 1);
-    }
-    __syncthreads();
-    if (is_last) {  // block-uniform
-      __threadfence();
-      double s = 0.0;
-      for (int k = tid; k < p.nblk_rows; k += 256)  // each thread: blocks tid, tid + 256, ...
-        s += __hip_atomic_load(&p.msepart[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      red[tid] = s;
-      __syncthreads();
-      for (int st = 128; st > 0; st >>= 1) {
-        if (tid < st) red[tid] += red[tid + st];
-        __syncthreads();
-      }
-      if (tid == 0) {
-        *p.mse_out = red[0] * p.inv_mn;
-        __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    if (tid == 0 && p.part_out) p.part_out[blockIdx.x] = red[0];
   } else {
     // 8 lanes per column: lane s adds partials s, s + 8, ... in order, then a fixed tree
     const int64_t j = (int64_t)(blockIdx.x - p.nblk_rows) * 32 + tid / 8;
@@ -645,29 +682,39 @@ hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_mse_collect, dim3(1), dim3(256), 0, s, part, count, out, inv_mn);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_finalize, dim3(a.nblk_rows + a.nblk_cols), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, bool PARTIAL>
+template <int FMT, bool PARTIAL, bool EMIT>
 static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
   switch (a.G) {
-    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fused(int fmt, const FusedArgs& a, hipStream_t s) {
+template <int FMT, bool EMIT>
+static hipError_t fused_fmt(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  // masking only when some tile extends past the last column
+  return a.n % kFusedCols != 0 ? fused_group<FMT, true, EMIT>(a, grid, s)
+                               : fused_group<FMT, false, EMIT>(a, grid, s);
+}
+
+hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.nct * a.nrc));
-  const bool partial = a.n % kFusedCols != 0;  // masking only when some tile is partial
-  if (fmt == kMxFp4)
-    return partial ? fused_group<kMxFp4, true>(a, grid, s) : fused_group<kMxFp4, false>(a, grid, s);
-  if (fmt == kMxInt4)
-    return partial ? fused_group<kMxInt4, true>(a, grid, s) : fused_group<kMxInt4, false>(a, grid, s);
+  if (fmt == kMxFp4) return emit ? fused_fmt<kMxFp4, true>(a, grid, s) : fused_fmt<kMxFp4, false>(a, grid, s);
+  if (fmt == kMxInt4) return emit ? fused_fmt<kMxInt4, true>(a, grid, s) : fused_fmt<kMxInt4, false>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
