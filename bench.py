@@ -65,6 +65,9 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sequential", action="store_true",
+                    help="solve the matrices of a step one after another on one stream "
+                         "(default: each on its own stream, concurrently)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 512 MiB device-to-device copies (the reference that "
                          "scales HBM byte counters)")
@@ -79,11 +82,11 @@ def main() -> None:
     import torch
 
     if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel that reads 512 MiB and writes 512 MiB
+        src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        src.fill_(1)
         for _ in range(args.steps):
-            dst.copy_(src)
+            torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 512 << 20, "copies": args.steps}), flush=True)
         return
@@ -93,15 +96,27 @@ def main() -> None:
     mats, desc = _load(args.workload)
     dev_w = [to_device(w.W, w.dtype) for w in mats]
     work = [dq.workspace_bytes(w.rows, w.cols, w.fmt, w.group) for w in mats]
-    ws = torch.empty(max(work), dtype=torch.uint8, device="cuda")
+    wss = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in work]
+    streams = [torch.cuda.Stream() for _ in mats]  # default priority
     torch.cuda.synchronize()
+    pool = None
+    if not args.sequential and len(mats) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        pool = ThreadPoolExecutor(max_workers=len(mats))
+
+    def solve_one(k, T, timing, stream):
+        w = mats[k]
+        return dq.solve(dev_w[k], w.fmt, w.group, w.T if T is None else T, workspace=wss[k],
+                        timing=timing, stream=stream)
 
     def step(T=None, timing=False):
-        outs = []
-        for w, W in zip(mats, dev_w):
-            outs.append(dq.solve(W, w.fmt, w.group, w.T if T is None else T, workspace=ws,
-                                 timing=timing))
-        return outs
+        # dq_solve returns when its stream is done; concurrent calls use separate streams
+        # and workspaces (the library keeps no global state)
+        if pool is None or timing:
+            return [solve_one(k, T, timing, None) for k in range(len(mats))]
+        futs = [pool.submit(solve_one, k, T, False, streams[k]) for k in range(len(mats))]
+        return [f.result() for f in futs]
 
     for _ in range(args.warmup):
         step()
@@ -175,6 +190,7 @@ def main() -> None:
         "mse": {"first": mse_first, "final": mse_final,
                 "ratio_first_over_final": [a / b for a, b in zip(mse_first, mse_final)]},
         "single_sweep_path": used_fused if kind == "fused" else None,
+        "concurrent_matrices": pool is not None,
     }
 
     if not args.no_cpu:

@@ -14,6 +14,7 @@
 //   emit    Q(X(a_T, b_T)): packed codes, inner scales, and the sums for mse[T].
 // If the MX single-sweep check fails anywhere, the solve is re-run on the two-sweep path,
 // which always re-quantizes; both give the same result whenever the check passes.
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -25,8 +26,31 @@
 namespace {
 
 constexpr int kTileCols = 512;
-constexpr int kFusedCols = 1024;
 constexpr int kTargetBlocks = 512;  // two 4-wave workgroups per CU on 256 CUs
+
+// Single-sweep launch shape: 512-column halves per lane, rows per load step and the
+// workgroup target (measured best on MI355X for the 8B MLP shapes: one half, two rows,
+// about three 4-wave workgroups per CU). DQ_FUSED_SHAPE="halves,step_rows,target"
+// overrides it (launch-shape tuning only).
+struct FusedShape {
+  int halves = 1;
+  int step_rows = 2;
+  int target = 768;
+};
+FusedShape fused_shape() {
+  FusedShape f;
+  const char* env = getenv("DQ_FUSED_SHAPE");
+  if (env) {
+    int h = 0, r = 0, t = 0;
+    if (sscanf(env, "%d,%d,%d", &h, &r, &t) == 3 && (h == 1 || h == 2) && (r == 2 || r == 4) &&
+        t >= 1 && t <= 65536) {
+      f.halves = h;
+      f.step_rows = r;
+      f.target = t;
+    }
+  }
+  return f;
+}
 
 // Workgroup target for the sweeps; DQ_TARGET_WGS overrides it (launch-shape tuning only:
 // results do not depend on it beyond the fixed summation order it implies).
@@ -46,8 +70,9 @@ struct Plan {
   int G = 0, fmt = 0;
   int nct = 0, nrc = 0;
   int64_t rpc = 0;
-  int f_nct = 0, f_nrc = 0;  // single-sweep MX pass: 1024-column tiles, rows in multiples of 32
+  int f_nct = 0, f_nrc = 0;  // single-sweep MX pass: 512 * halves columns, rows in multiples of 32
   int64_t f_rpc = 0;
+  FusedShape f_shape;
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
@@ -77,8 +102,10 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.nrc = (int)(want < 1 ? 1 : (want > max_rc ? max_rc : want));
   p.rpc = (m + p.nrc - 1) / p.nrc;
   p.nrc = (int)((m + p.rpc - 1) / p.rpc);  // drop empty trailing chunks
-  p.f_nct = (int)((n + kFusedCols - 1) / kFusedCols);
-  int64_t f_want = (target + p.f_nct - 1) / p.f_nct;
+  p.f_shape = fused_shape();
+  const int64_t f_cols = (int64_t)kTileCols * p.f_shape.halves;
+  p.f_nct = (int)((n + f_cols - 1) / f_cols);
+  int64_t f_want = (p.f_shape.target + p.f_nct - 1) / p.f_nct;
   if (f_want < 1) f_want = 1;
   p.f_rpc = (m + f_want - 1) / f_want;
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
@@ -278,6 +305,8 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.nct = p.f_nct;
   fu.nrc = p.f_nrc;
   fu.rpc = p.f_rpc;
+  fu.halves = p.f_shape.halves;
+  fu.step_rows = p.f_shape.step_rows;
   fu.rowpart = rowpart;
   fu.colpart = colpart;
   fu.codes = io.codes;
@@ -317,7 +346,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       fa.gauge_check = 0;
       fa.row_ra = 1;
       fa.envelope = 1;
-      fa.col_terms = (int)((p.f_rpc + 31) / 32 * 8);  // 8-row batches, 32 rows apart
+      fa.col_terms = 8 + (int)((p.f_rpc + 31) / 32);  // 8 rows per batch, then the batches
       if ((st = finalize(true, true, true)) != DQ_OK) return st;
     } else if (fused) {
       tm.before(DQ_K_FUSED);

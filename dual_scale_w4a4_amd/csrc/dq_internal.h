@@ -46,9 +46,11 @@ struct FusedArgs {
   int G;
   const float* rb;
   const float* b;
-  int nct;          // column tiles of 1024 columns
+  int nct;          // column tiles of 512 * halves columns
   int nrc;          // row chunks
   int64_t rpc;      // rows per chunk
+  int halves;       // 512-column halves per lane: 1 or 2
+  int step_rows;    // rows per load step: 2 or 4
   double2* rowpart;  // [nct][m] (sum_j W t, sum_j (W - t)^2) with t = S b: R = ra * t
   double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
   // final pass only: packed codes, E8M0 inner scales, the outer row scales
@@ -104,7 +106,7 @@ struct FinArgs {
   int gauge_check;
   int row_ra;          // single-sweep MX sums: rowpart holds (N', e) with R = ra_i t
   int envelope;        // flag kStGauge if a new a or b leaves [2^-24, 2^24]
-  int col_terms;       // single-sweep: most rows one lane adds in fp32 for a column sum
+  int col_terms;       // single-sweep: bound on the fp32 additions behind one column sum
   double* part_out;         // per-block row-error sums of this launch, or null
   const double* prev_part;  // a previous launch's block sums to finish, or null
   int prev_count;

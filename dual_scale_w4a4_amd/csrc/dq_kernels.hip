@@ -198,29 +198,30 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
 // sum above that is fp64 in a fixed order: a row's 64 lane partials are transposed through LDS
 // in batches of 8 rows and added by 8 lanes per row, and the 4 waves' column partials are
 // added through LDS at the end.
-constexpr int kFusedCols = 1024;
-constexpr int kFusedBatch = 8;  // rows per wave between row reductions (4 load steps of 2)
+constexpr int kFusedBatch = 8;  // rows per wave between row reductions
 
+// Column sums run in two levels to keep their error small: Pb / Qb over the 8 rows of a
+// batch, then P / Q over the batches (a worst case of (7 + batches) * 2^-24 relative).
+template <int NH>
 struct FusedLane {
-  float rb[16], bb[16], P[16], Q[16];
+  float rb[8 * NH], bb[8 * NH], P[8 * NH], Q[8 * NH], Pb[8 * NH], Qb[8 * NH];
 };
 
-// one row of 16 elements: codes, the row's partial sums, the column accumulators
-// One row of 16 elements: codes, the row's partial sums and the column accumulators.
-// PARTIAL: the tile extends past column n; amask[h] zeroes a half that lies past it.
-// gmax / gmin track the largest group max and the smallest nonzero one (as bit patterns,
-// gmin offset by one so that a zero group never counts) for the range check.
+// One row of 8 * NH elements (NH 512-column halves of the tile): codes, the row's partial
+// sums and the column accumulators. PARTIAL: the tile extends past column n; amask[h]
+// zeroes a half that lies past it. gmax / gmin track the largest group max and the smallest
+// nonzero one (bit patterns, gmin offset by one so that a zero group never counts).
 // EMIT: the final pass; instead of the sums for the updates it stores the packed codes and
-// the E8M0 inner-scale bytes of the row (ka = log2 a_i) and keeps only the row error.
-template <int FMT, int LPG, bool PARTIAL, bool EMIT>
-__device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, float& nacc,
+// the E8M0 inner-scale bytes of the row (abits = bits of a_i) and keeps only the row error.
+template <int FMT, int LPG, int NH, bool PARTIAL, bool EMIT>
+__device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L, float& nacc,
                                           float& eacc, uint32_t& gmax, uint32_t& gmin,
-                                          const uint32_t (&amask)[2], uint32_t* codes_row,
+                                          const uint32_t (&amask)[NH], uint32_t* codes_row,
                                           uint8_t* scales_row, uint32_t abits) {
   nacc = 0.0f;
   eacc = 0.0f;
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
+  for (int h = 0; h < NH; h++) {
     uint32_t u[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
     if (PARTIAL) {
 #pragma unroll
@@ -287,17 +288,20 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[2], FusedLane& L, flo
       eacc = fmaf(df, df, eacc);
       if (!EMIT) {
         nacc = fmaf(w[k], t, nacc);
-        L.P[e] = fmaf(w[k], S[k], L.P[e]);
-        L.Q[e] = fmaf(S[k], S[k], L.Q[e]);
+        L.Pb[e] = fmaf(w[k], S[k], L.Pb[e]);
+        L.Qb[e] = fmaf(S[k], S[k], L.Qb[e]);
       }
     }
   }
 }
 
-template <int FMT, int G, bool PARTIAL, bool EMIT>
+// The pass. NH: 512-column halves per lane (the tile is 512 * NH columns); S: rows per load
+// step (loads run one step ahead of the rows being computed).
+template <int FMT, int G, bool PARTIAL, bool EMIT, int NH, int S>
 __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   constexpr int LPG = G / kEpl;  // lanes per group
-  __shared__ float2 smem[kWaves * kFusedCols];  // 32 KiB: row transposes, then column sums
+  constexpr int kCols = kTileCols * NH;
+  __shared__ float2 smem[kWaves * (kCols > kFusedBatch * kWave ? kCols : kFusedBatch * kWave)];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -305,14 +309,20 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   const int rc = blockIdx.x / p.nct;
   const int64_t r_begin = (int64_t)rc * p.rpc;
   const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
-  const int64_t col[2] = {(int64_t)ct * kFusedCols + lane * kEpl,
-                          (int64_t)ct * kFusedCols + kTileCols + lane * kEpl};
-  const bool act[2] = {col[0] < p.n, col[1] < p.n};
-  const int64_t lcol[2] = {act[0] ? col[0] : 0, act[1] ? col[1] : 0};  // in-bounds addresses
-
-  FusedLane L;
+  int64_t col[NH], lcol[NH];
+  bool act[NH];
+  uint32_t amask[NH];
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
+  for (int h = 0; h < NH; h++) {
+    col[h] = (int64_t)ct * kCols + h * kTileCols + lane * kEpl;
+    act[h] = col[h] < p.n;
+    lcol[h] = act[h] ? col[h] : 0;  // in-bounds address
+    amask[h] = act[h] ? 0xFFFFFFFFu : 0u;
+  }
+
+  FusedLane<NH> L;
+#pragma unroll
+  for (int h = 0; h < NH; h++) {
     const float4* rbp = reinterpret_cast<const float4*>(p.rb + lcol[h]);
     const float4* bbp = reinterpret_cast<const float4*>(p.b + lcol[h]);
     const float4 r0 = rbp[0], r1 = rbp[1], b0 = bbp[0], b1 = bbp[1];
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     for (int k = 0; k < 8; k++) {
       L.rb[8 * h + k] = act[h] ? rr[k] : 1.0f;
       L.bb[8 * h + k] = act[h] ? bv[k] : 0.0f;
-      L.P[8 * h + k] = L.Q[8 * h + k] = 0.0f;
+      L.P[8 * h + k] = L.Q[8 * h + k] = L.Pb[8 * h + k] = L.Qb[8 * h + k] = 0.0f;
     }
   }
   uint32_t gmax = 0u, gmin = 0xFFFFFFFFu;
@@ -331,20 +341,21 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   const int64_t first = r_begin + (int64_t)wave * kFusedBatch;
   const int64_t nbatch =
       first < r_end ? (r_end - first + kWaves * kFusedBatch - 1) / (kWaves * kFusedBatch) : 0;
-  // loads of rows i, i+1 from in-bounds addresses (rows past the chunk reload its first row
-  // and are skipped below; columns past n are masked in fused_row)
-  auto load2 = [&](int64_t i, uint4 (&buf)[2][2]) {
+  // loads of rows i .. i+S-1 from in-bounds addresses (rows past the chunk reload its first
+  // row and are skipped below; columns past n are masked in fused_row)
+  auto load = [&](int64_t i, uint4 (&buf)[S][NH]) {
 #pragma unroll
-    for (int r = 0; r < 2; r++) {
+    for (int r = 0; r < S; r++) {
       const int64_t row = i + r < r_end ? i + r : r_begin;
 #pragma unroll
-      for (int h = 0; h < 2; h++)
+      for (int h = 0; h < NH; h++)
         buf[r][h] = *reinterpret_cast<const uint4*>(p.W + row * p.n + lcol[h]);
     }
   };
-  const uint32_t amask[2] = {act[0] ? 0xFFFFFFFFu : 0u, act[1] ? 0xFFFFFFFFu : 0u};
-  // one row, skipped (uniformly) when it lies past the chunk
-  auto row_step = [&](const uint4 (&v)[2], int64_t i, float& n_out, float& e_out) {
+  float2* R = smem + wave * (kFusedBatch * kWave);  // this wave's [8 rows][64 lanes] partials
+  // one row, skipped (uniformly) when it lies past the chunk; its lane partials go to LDS
+  auto row_step = [&](const uint4 (&v)[NH], int64_t i, int r) {
+    float n_out = 0.0f, e_out = 0.0f;
     if (i < r_end) {
       uint32_t* codes_row = nullptr;
       uint8_t* scales_row = nullptr;
@@ -354,43 +365,46 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         scales_row = p.scales + i * (p.n / G) + col[0] / G;
         abits = f2u(p.a[i]);
       }
-      fused_row<FMT, LPG, PARTIAL, EMIT>(v, L, n_out, e_out, gmax, gmin, amask, codes_row,
-                                         scales_row, abits);
-    } else {
-      n_out = 0.0f;
-      e_out = 0.0f;
+      fused_row<FMT, LPG, NH, PARTIAL, EMIT>(v, L, n_out, e_out, gmax, gmin, amask, codes_row,
+                                             scales_row, abits);
     }
+    R[r * kWave + lane] = make_float2(n_out, e_out);
   };
 
-  uint4 bufA[2][2], bufB[2][2];
-  if (nbatch > 0) load2(first, bufA);
+  // a batch is kFusedBatch / S load steps; buffers alternate so that each step's loads
+  // were issued one step earlier
+  constexpr int kSteps = kFusedBatch / S;
+  static_assert(kSteps % 2 == 0, "an even number of steps per batch");
+  uint4 bufA[S][NH], bufB[S][NH];
+  if (nbatch > 0) load(first, bufA);
   for (int64_t bt = 0; bt < nbatch; bt++) {
     const int64_t row0 = first + bt * (kWaves * kFusedBatch);
-    float nl[kFusedBatch], el[kFusedBatch];
-    // each step issues the next two rows' loads, then computes two rows; the scheduling
-    // barriers keep the compiler from interleaving steps (register pressure)
-    load2(row0 + 2, bufB);
-    row_step(bufA[0], row0 + 0, nl[0], el[0]);
-    row_step(bufA[1], row0 + 1, nl[1], el[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    load2(row0 + 4, bufA);
-    row_step(bufB[0], row0 + 2, nl[2], el[2]);
-    row_step(bufB[1], row0 + 3, nl[3], el[3]);
-    __builtin_amdgcn_sched_barrier(0);
-    load2(row0 + 6, bufB);
-    row_step(bufA[0], row0 + 4, nl[4], el[4]);
-    row_step(bufA[1], row0 + 5, nl[5], el[5]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (bt + 1 < nbatch) load2(row0 + kWaves * kFusedBatch, bufA);
-    row_step(bufB[0], row0 + 6, nl[6], el[6]);
-    row_step(bufB[1], row0 + 7, nl[7], el[7]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 8 rows done: transpose the 64 lane partials of each row through LDS; 8 lanes per row
-    // add 8 partials each in fp64, then across the 8 lanes in a fixed order
-    float2* R = smem + wave * (kFusedBatch * kWave);
 #pragma unroll
-    for (int r = 0; r < kFusedBatch; r++) R[r * kWave + lane] = make_float2(nl[r], el[r]);
+    for (int st = 0; st < kSteps; st += 2) {
+      load(row0 + (st + 1) * S, bufB);
+#pragma unroll
+      for (int r = 0; r < S; r++) row_step(bufA[r], row0 + st * S + r, st * S + r);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < kSteps)
+        load(row0 + (st + 2) * S, bufA);
+      else if (bt + 1 < nbatch)
+        load(row0 + kWaves * kFusedBatch, bufA);
+#pragma unroll
+      for (int r = 0; r < S; r++) row_step(bufB[r], row0 + (st + 1) * S + r, (st + 1) * S + r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (!EMIT) {
+#pragma unroll
+      for (int e = 0; e < 8 * NH; e++) {
+        L.P[e] += L.Pb[e];
+        L.Q[e] += L.Qb[e];
+        L.Pb[e] = L.Qb[e] = 0.0f;
+      }
+    }
+
+    // 8 rows done: 8 lanes per row add 8 lane partials each in fp64 (transposed through
+    // LDS), then across the 8 lanes in a fixed order
     __builtin_amdgcn_wave_barrier();
     const float2* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
     double N = 0.0, Er = 0.0;
@@ -409,24 +423,23 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
 
   // column partials: the 4 waves' fp32 sums added in fp64 in wave order
   if (!EMIT) {
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; h++)
+    for (int h = 0; h < NH; h++)
 #pragma unroll
-    for (int k = 0; k < 8; k++)
-      smem[wave * kFusedCols + h * kTileCols + lane * kEpl + k] =
-          make_float2(L.P[8 * h + k], L.Q[8 * h + k]);
-  __syncthreads();
-  for (int c = threadIdx.x; c < kFusedCols; c += kBlock) {
-    double sp = 0.0, sq = 0.0;
+      for (int k = 0; k < 8; k++)
+        smem[wave * kCols + h * kTileCols + lane * kEpl + k] = make_float2(L.P[8 * h + k], L.Q[8 * h + k]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < kCols; c += kBlock) {
+      double sp = 0.0, sq = 0.0;
 #pragma unroll
-    for (int v = 0; v < kWaves; v++) {
-      sp += (double)smem[v * kFusedCols + c].x;
-      sq += (double)smem[v * kFusedCols + c].y;
+      for (int v = 0; v < kWaves; v++) {
+        sp += (double)smem[v * kCols + c].x;
+        sq += (double)smem[v * kCols + c].y;
+      }
+      const int64_t j = (int64_t)ct * kCols + c;
+      if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
     }
-    const int64_t j = (int64_t)ct * kFusedCols + c;
-    if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
-  }
   }
   // range check: every nonzero group max in [2^-32, 2^32)
   const bool bad = gmax >= 0x4F800000u || (gmin != 0xFFFFFFFFu && gmin + 1u < 0x2F800000u);
@@ -529,9 +542,9 @@ __device__ __forceinline__ double e8m0_margin(double v) {
   const double f = __builtin_bit_cast(double, (u & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull);
   return fabs(f - 1.5) / f;  // f in [1, 2): the mantissa of v
 }
-// Worst-case relative error of one fp32 sum of k nonnegative terms is k * 2^-24; the
-// single-sweep lane sums run over 16 columns (row sums) and FinArgs::col_terms rows
-// (column sums).
+// Worst-case relative error of an fp32 sum of k nonnegative terms is (k - 1) * 2^-24; the
+// single-sweep lane sums run over at most 16 columns (row sums), and FinArgs::col_terms
+// bounds the additions behind a column sum.
 constexpr double kRowSumErr = 16.0 * 0x1p-24;
 
 // sum of cnt double2 partials at base, base + stride, ... in index order, loads issued first
@@ -693,28 +706,36 @@ hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, bool PARTIAL, bool EMIT>
+template <int FMT, bool PARTIAL, bool EMIT, int NH, int S>
 static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
   switch (a.G) {
-    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, bool EMIT>
-static hipError_t fused_fmt(const FusedArgs& a, dim3 grid, hipStream_t s) {
+template <int FMT, bool EMIT, int NH, int S>
+static hipError_t fused_shape(const FusedArgs& a, dim3 grid, hipStream_t s) {
   // masking only when some tile extends past the last column
-  return a.n % kFusedCols != 0 ? fused_group<FMT, true, EMIT>(a, grid, s)
-                               : fused_group<FMT, false, EMIT>(a, grid, s);
+  return a.n % (kTileCols * NH) != 0 ? fused_group<FMT, true, EMIT, NH, S>(a, grid, s)
+                                     : fused_group<FMT, false, EMIT, NH, S>(a, grid, s);
+}
+
+template <int FMT, bool EMIT>
+static hipError_t fused_variant(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  if (a.halves == 1) return a.step_rows == 4 ? fused_shape<FMT, EMIT, 1, 4>(a, grid, s)
+                                             : fused_shape<FMT, EMIT, 1, 2>(a, grid, s);
+  return a.step_rows == 4 ? fused_shape<FMT, EMIT, 2, 4>(a, grid, s)
+                          : fused_shape<FMT, EMIT, 2, 2>(a, grid, s);
 }
 
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.nct * a.nrc));
-  if (fmt == kMxFp4) return emit ? fused_fmt<kMxFp4, true>(a, grid, s) : fused_fmt<kMxFp4, false>(a, grid, s);
-  if (fmt == kMxInt4) return emit ? fused_fmt<kMxInt4, true>(a, grid, s) : fused_fmt<kMxInt4, false>(a, grid, s);
+  if (fmt == kMxFp4) return emit ? fused_variant<kMxFp4, true>(a, grid, s) : fused_variant<kMxFp4, false>(a, grid, s);
+  if (fmt == kMxInt4) return emit ? fused_variant<kMxInt4, true>(a, grid, s) : fused_variant<kMxInt4, false>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
