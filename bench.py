@@ -26,6 +26,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_amd/csrc/dq_device.h",
+                  "dual_scale_w4a4_amd/csrc/dq_internal.h")
+# HBM bytes per launch of the single-sweep MXFP4 kernel on the 8B MLP pair, from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch), each scaled by what the same
+# counter reads for an elementwise kernel of known size (fetch reports half of a 512 MiB
+# read: x2; write is exact: x1). They hold only for the kernel sources they were taken on.
+COUNTERS = {
+    "workload": 3,
+    "kernel": "k_fused_mx<MXFP4, 32, no emit>",
+    "fetch_kib": 57469.0, "fetch_scale": 2.0,
+    "write_kib": 7584.0, "write_scale": 1.0,
+    "sources_sha256": "f165a313bdab1db07820477a5c3b86b5cc9d8cee2f151cdea10a755b58cbb0cd",
+}
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
 
@@ -43,6 +56,25 @@ def _load(workload: int):
     if workload == 5:
         return workloads.config5_layer(0), "llama3.1-8b decoder layer 0 (q,k,v,o,gate,up,down), bf16, INT4/BF16 G64, T=15"
     raise SystemExit(f"unknown workload {workload}")
+
+
+def sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: int, fused: bool):
+    """HBM bytes per launch of the dominant kernel from the stored counter runs, or None when
+    they do not apply (another workload, another path, or changed kernel sources)."""
+    c = COUNTERS
+    if not fused or workload != c["workload"] or sources_sha256() != c["sources_sha256"]:
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 
 
 def to_device(w_np, dtype: str):
@@ -137,25 +169,31 @@ def main() -> None:
 
     # instrumented pass over the same steps: per-kernel HIP events on the solve's stream
     kind = _dominant_kind(mats[0].fmt)
+    bytes_per_elem = 2 if mats[0].dtype == "bf16" else 4
     ms_all, used_fused = {}, True
+    iso = [0.0, 0, 0.0]  # ms, launches, bytes of the isolated back-to-back runs
     for _ in range(args.steps):
-        for o in step(timing=True):
+        for w, o in zip(mats, step(timing=True)):
             used_fused = used_fused and o["used_fused"]
             for k, (ms, n) in o["timing"].items():
                 acc = ms_all.setdefault(k, [0.0, 0])
                 acc[0] += ms
                 acc[1] += n
+            iso[0] += o["isolated"][0]
+            iso[1] += o["isolated"][1]
+            iso[2] += o["isolated"][1] * w.rows * w.cols * bytes_per_elem
     ms_kind, n_kind = ms_all[kind]
+    # dominant kernel: each launch reads every weight of its matrix once, T launches per solve
+    bytes_total = args.steps * sum(w.rows * w.cols * bytes_per_elem * w.T for w in mats)
+    if iso[1] > 0:  # back-to-back launches between one event pair: no per-launch overhead
+        ms_kind, n_kind, bytes_total = iso
 
     elems = sum(w.rows * w.cols for w in mats)
     elem_iters = sum(w.rows * w.cols * w.T for w in mats)
     T_mean = elem_iters / elems
-    bytes_per_elem = 2 if mats[0].dtype == "bf16" else 4
     value = elem_iters / t_step
     t_iter = (t_step - t_step0) / T_mean  # per iteration over all matrices of the step
     iter_gbs = elems * bytes_per_elem / t_iter / 1e9
-    # dominant kernel: each launch reads every weight of its matrix once, T launches per solve
-    bytes_total = args.steps * sum(w.rows * w.cols * bytes_per_elem * w.T for w in mats)
     avg_launch_ms = ms_kind / max(n_kind, 1)
     launch_bytes = bytes_total / max(n_kind, 1)
     achieved = bytes_total / (ms_kind * 1e-3) / 1e9
@@ -182,10 +220,12 @@ def main() -> None:
         "per_iteration": {"ms": t_iter * 1e3, "elems_per_s": elems / t_iter,
                           "GBps_one_read_of_W": iter_gbs, "frac_hbm_peak": iter_gbs / HBM_PEAK_GBS,
                           "ms_per_step_T0": t_step0 * 1e3},
-        "roofline": {"bound": "hbm", "kernel": f"k_sweep ({kind})", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_fused_mx" if kind == "fused" else "k_sweep (row mode)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": avg_launch_ms * 1e3,
+                     "traffic": counted_traffic(args.workload, kind == "fused" and used_fused),
+                     "traffic_unit": "bytes per launch", "avg_launch_us": avg_launch_ms * 1e3,
                      "launches": n_kind, "bytes_per_launch": launch_bytes,
+                     "timing": "isolated back-to-back launches" if iso[1] else "per-launch events",
                      "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}},
         "mse": {"first": mse_first, "final": mse_final,
                 "ratio_first_over_final": [a / b for a, b in zip(mse_first, mse_final)]},

@@ -34,7 +34,8 @@ class DQError(RuntimeError):
 
 class _Timing(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
-                ("used_fused", ctypes.c_int)]
+                ("used_fused", ctypes.c_int), ("isolated_ms", ctypes.c_double),
+                ("isolated_launches", ctypes.c_int)]
 
 
 class _Init(ctypes.Structure):
@@ -152,6 +153,7 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
     if tm is not None:
         out["timing"] = {k: (tm.ms[i], tm.launches[i]) for i, k in enumerate(KERNEL_KINDS)}
         out["used_fused"] = bool(tm.used_fused)
+        out["isolated"] = (tm.isolated_ms, tm.isolated_launches)
     return out
 
 

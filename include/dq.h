@@ -88,6 +88,10 @@ typedef struct {
   double ms[DQ_K_KINDS];
   int64_t launches[DQ_K_KINDS];
   int used_fused; /* 1 if the MX single-sweep path produced the result */
+  /* single-sweep path only: after the solve, the pass is re-run isolated_launches times
+     back to back between one pair of events (results unchanged); this is its time */
+  double isolated_ms;
+  int isolated_launches;
 } dq_timing;
 
 typedef struct {
