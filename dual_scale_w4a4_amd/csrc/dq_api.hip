@@ -52,6 +52,17 @@ FusedShape fused_shape() {
   return f;
 }
 
+// Workgroup target of the two-sweep pass for bf16 weights; DQ_PASS_TARGET overrides it
+// (launch-shape tuning only, like the others below).
+int pass_target() {
+  const char* env = getenv("DQ_PASS_TARGET");
+  if (env) {
+    int v = atoi(env);
+    if (v >= 1 && v <= 65536) return v;
+  }
+  return 768;
+}
+
 // Workgroup target for the sweeps; DQ_TARGET_WGS overrides it (launch-shape tuning only:
 // results do not depend on it beyond the fixed summation order it implies).
 int target_blocks() {
@@ -73,6 +84,8 @@ struct Plan {
   int f_nct = 0, f_nrc = 0;  // single-sweep MX pass: 512 * halves columns, rows in multiples of 32
   int64_t f_rpc = 0;
   FusedShape f_shape;
+  int g_nct = 0, g_nrc = 0;  // two-sweep pass for bf16 weights: 512 columns, rows in 32s
+  int64_t g_rpc = 0;
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
@@ -110,6 +123,12 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.f_rpc = (m + f_want - 1) / f_want;
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
   p.f_nrc = (int)((m + p.f_rpc - 1) / p.f_rpc);
+  p.g_nct = p.nct;
+  int64_t g_want = (pass_target() + p.g_nct - 1) / p.g_nct;
+  if (g_want < 1) g_want = 1;
+  p.g_rpc = (m + g_want - 1) / g_want;
+  p.g_rpc = (p.g_rpc + 31) / 32 * 32;
+  p.g_nrc = (int)((m + p.g_rpc - 1) / p.g_rpc);
   p.nblk_rows = (int)((m + 255) / 256);
   p.nblk_cols = (int)((n + 31) / 32);  // finalize: 8 lanes per column
   size_t o = 0;
@@ -122,7 +141,8 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.off_amax = o; o = align_up(o + sizeof(float) * m);
   p.off_gs = o; o = align_up(o + 16);
   const size_t rc_parts = (size_t)(p.nct > p.f_nct ? p.nct : p.f_nct);
-  const size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
+  size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
+  if ((size_t)p.g_nrc > cc_parts) cc_parts = (size_t)p.g_nrc;
   p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
   p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
   p.off_msepart = o; o = align_up(o + 2 * sizeof(double) * p.nblk_rows);
@@ -280,6 +300,11 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   sw.scales = io.scales;
   sw.status = status;
 
+  SweepArgs sp = sw;  // the two-sweep pass for bf16 weights
+  sp.nct = p.g_nct;
+  sp.nrc = p.g_nrc;
+  sp.rpc = p.g_rpc;
+
   FinArgs fa{};
   fa.m = p.m;
   fa.n = p.n;
@@ -356,6 +381,17 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       fa.nrc = p.nrc;
       fa.gauge_check = 1;
       if ((st = finalize(true, true, true)) != DQ_OK) return st;
+    } else if (io.bf16) {
+      tm.before(DQ_K_ROW);
+      DQ_TRY(launch_pass(p.fmt, kModeRow, sp, s));
+      tm.after();
+      fa.nct = p.g_nct;
+      fa.nrc = p.g_nrc;
+      if ((st = finalize(true, false, true)) != DQ_OK) return st;
+      tm.before(DQ_K_COL);
+      DQ_TRY(launch_pass(p.fmt, kModeCol, sp, s));
+      tm.after();
+      if ((st = finalize(false, true, false)) != DQ_OK) return st;
     } else {
       tm.before(DQ_K_ROW);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow, sw, s));
@@ -374,6 +410,10 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
     DQ_TRY(launch_fused(p.fmt, true, fu, s));
     fa.nct = p.f_nct;
     fa.row_ra = 1;
+  } else if (io.bf16) {
+    DQ_TRY(launch_pass(p.fmt, kModeEmit | kModeRow, sp, s));
+    fa.nct = p.g_nct;
+    fa.row_ra = 0;
   } else {
     DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeEmit | kModeRow, sw, s));
     fa.nct = p.nct;

@@ -76,17 +76,17 @@ DQ_HD uint32_t e2m1_index(float r) {
   return (uint32_t)k;
 }
 
-// nearest integer to the exact quotient ax / d (ax >= 0, d > 0), ties to even. k0 comes from
-// the rounded product ax * rd and is at most one off; the two fused multiply-adds give the
-// exact signs of ax - (k0 +- 1/2) d, which settle the neighbour and the tie.
-DQ_HD float rne_quotient_int(float ax, float d, float rd) {
-  float k0 = rintf(ax * rd);
-  float dh = fmaf(-(k0 + 0.5f), d, ax);
-  float dl = fmaf(-(k0 - 0.5f), d, ax);
-  bool odd = ((int)k0 & 1) != 0;
-  float up = (dh > 0.0f || (dh == 0.0f && odd)) ? 1.0f : 0.0f;
-  float dn = (dl < 0.0f || (dl == 0.0f && odd)) ? 1.0f : 0.0f;
-  return k0 + up - dn;
+// nearest integer to the exact quotient x / d (d > 0, |x / d| < 16), ties to even, from an
+// approximate reciprocal rd (a few ulp from 1 / d). k = rint(x rd) is at most one off, so
+// e = x - k d is exactly representable and the fused multiply-add returns it exactly: |e| >
+// d / 2 moves k one step towards e, and |e| = d / 2 is a tie, settled by the hardware's
+// round-to-nearest-even of the exact half-integer k +- 1/2.
+DQ_HD float rne_quotient_int(float x, float d, float hd, float rd) {
+  const float k = rintf(x * rd);
+  const float e = fmaf(-k, d, x);
+  const float ae = fabsf(e);
+  const float adj = ae > hd ? 1.0f : (ae == hd ? 0.5f : 0.0f);
+  return rintf(k + copysignf(adj, e));
 }
 
 // nearest E2M1 magnitude to the exact quotient ax / d (ax >= 0, d > 0, rd ~ 1/d). The caller
@@ -152,14 +152,33 @@ DQ_HD float project(int fmt, double v) {
 // fl32(1/v), correctly rounded (double quotient rounds innocuously to float)
 DQ_HD float recip32(float v) { return (float)(1.0 / (double)v); }
 
+// fl32(m / 7) for finite m >= 0 with one double product. If 7 divides m's integer
+// significand the quotient is a float; otherwise its significand (or its subnormal multiple
+// of 2^-149) has a fractional part k / 7, k in 1..6, at least 1/14 of a unit from the
+// rounding midpoint, while the product is within 2^-52 (relative) of m / 7: both round alike.
+DQ_HD float div7(float m) { return (float)((double)m * (1.0 / 7.0)); }
+
+// an approximate reciprocal (within a few ulp) of a positive normal float whose reciprocal
+// is normal; only used to find a candidate that an exact fix-up step then corrects
+DQ_HD float approx_recip(float v) {
+#ifdef __HIP_DEVICE_COMPILE__
+  return __builtin_amdgcn_rcpf(v);
+#else
+  return 1.0f / v;
+#endif
+}
+
 // ------------------------------------------------------------------- the group quantizer Q
 
-// Per-group quantizer state: divisor d, an approximate reciprocal, the operand rescale
-// for tiny divisors, and the stored scale encoding.
+// Per-group quantizer state: divisor d, the operand rescale sc for tiny divisors (a power of
+// two; sc = 1 otherwise) with the rescaled divisor ds = d sc, half of it hds and an
+// approximate reciprocal rd ~ 1 / ds, and the stored scale encoding.
 struct GroupQ {
   float d;
   float rd;
   float sc;
+  float ds;
+  float hds;
   uint32_t scode;
 };
 
@@ -175,11 +194,13 @@ DQ_HD GroupQ group_scale(float mx, float g, float sixg) {
   r.sc = 1.0f;
   if (FMT == kInt4Bf16) {
     float s = 1.0f;
-    if (mx > 0.0f) s = fmaxf(bf16_rne((float)((double)mx / 7.0)), 0x1p-133f);
+    if (mx > 0.0f) s = fmaxf(bf16_rne(div7(mx)), 0x1p-133f);
     r.d = s;
     r.scode = f2u(s) >> 16;
     if (s < 0x1p-100f) r.sc = 0x1p32f;
-    r.rd = (float)(1.0 / (double)(s * r.sc));
+    r.ds = s * r.sc;
+    r.hds = 0.5f * r.ds;
+    r.rd = approx_recip(r.ds);
   } else if (FMT == kMxInt4 || FMT == kMxFp4) {
     int e = 0;
     if (mx > 0.0f) {
@@ -189,6 +210,8 @@ DQ_HD GroupQ group_scale(float mx, float g, float sixg) {
     }
     r.d = exp2i(e);
     r.rd = exp2i(-e);
+    r.ds = r.d;
+    r.hds = 0.5f * r.d;
     r.scode = (uint32_t)(e + 127);
   } else {
     float s = 1.0f;
@@ -196,7 +219,9 @@ DQ_HD GroupQ group_scale(float mx, float g, float sixg) {
     r.d = s * g;
     r.scode = e4m3_bits(s);
     if (r.d < 0x1p-100f) r.sc = 0x1p32f;
-    r.rd = (float)(1.0 / (double)(r.d * r.sc));
+    r.ds = r.d * r.sc;
+    r.hds = 0.5f * r.ds;
+    r.rd = (float)(1.0 / (double)r.ds);
   }
   return r;
 }
@@ -204,19 +229,70 @@ DQ_HD GroupQ group_scale(float mx, float g, float sixg) {
 // the signed code value of x (a float holding the integer or E2M1 value)
 template <int FMT>
 DQ_HD float code_of(float x, const GroupQ& gq) {
+  if (FMT == kInt4Bf16) {
+    const float r = rne_quotient_int(x * gq.sc, gq.ds, gq.hds, gq.rd);
+    return fminf(fmaxf(r, -8.0f), 7.0f);
+  }
   const float ax = fabsf(x);
   float r;
-  if (FMT == kInt4Bf16) {
-    r = rne_quotient_int(ax * gq.sc, gq.d * gq.sc, gq.rd);
-    r = fminf(r, x < 0.0f ? 8.0f : 7.0f);
-  } else if (FMT == kMxInt4) {
+  if (FMT == kMxInt4) {
     r = fminf(rintf(ax * gq.rd), 7.0f);  // exact quotient: d is a power of two
   } else if (FMT == kMxFp4) {
     r = e2m1_mag(ax * gq.rd);
   } else {
-    r = e2m1_quotient(ax * gq.sc, gq.d * gq.sc, gq.rd);
+    r = e2m1_quotient(ax * gq.sc, gq.ds, gq.rd);
   }
   return x < 0.0f ? -r : r;
+}
+
+// ------------------------------------------------------- codes through a double quotient
+// For fp32 x and the divisors Q produces (a bf16 value for INT4, an fp32 value for NVFP4, a
+// power of two for MX), the quotient x / d either lies exactly on a rounding boundary of
+// the code grid (a half-integer, or an E2M1 midpoint 1/4, 3/4, ..., 5) or at least 2^-29
+// away from every boundary: x - h d is a nonzero multiple of min(ulp(x), ulp(d)) / 4 and
+// x ~ h d bounds how small that is against d. A double quotient p = x * r with r within
+// 2^-48 of 1 / d (relative) is within 2^-44 of x / d, so snapping p onto the multiples of
+// 2^-32 keeps it on the same side of every boundary and makes it equal at a tie; the
+// hardware's round-to-nearest-even of the snapped value then gives the exact code.
+
+// 1 / v in double, relative error below 2^-48 (the hardware estimate and two Newton steps)
+DQ_HD double recip64(float v) {
+  const double d = (double)v;
+#ifdef __HIP_DEVICE_COMPILE__
+  double r = __builtin_amdgcn_rcp(d);
+  double e = fma(-d, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-d, r, 1.0);
+  return fma(r, e, r);
+#else
+  return 1.0 / d;
+#endif
+}
+
+// p (|p| < 2^19) rounded onto the multiples of 2^-32
+DQ_HD double snap_quotient(double p) { return (p + 0x1.8p20) - 0x1.8p20; }
+
+// E2M1 magnitude nearest to a snapped quotient v >= 0, ties to the even index, saturating:
+// adding C = 2^51 * max(1, 2^floor(log2 v)) puts the double ulp at the grid spacing of v's
+// binade (0.5, 1, 2), as e2m1_mag does in fp32
+DQ_HD double e2m1_grid64(double v) {
+  const uint32_t hi = (uint32_t)(d2u(v) >> 32);
+  const uint32_t base = (hi & 0x7FF00000u) > 0x3FF00000u ? (hi & 0x7FF00000u) : 0x3FF00000u;
+  const double c = u2d((unsigned long long)(base + (51u << 20)) << 32);
+  const double r = (v + c) - c;
+  return r < 6.0 ? r : 6.0;
+}
+
+// the signed code of x given r ~ 1 / d (see above); for INT4 the clamp to [-8, 7] never
+// acts, because |x| <= mx and s >= (mx / 7)(1 - 2^-8) keep |x / s| below 7.03
+template <int FMT>
+DQ_HD double code64(float x, double r, const GroupQ& gq) {
+  if (FMT == kInt4Bf16) return rint(snap_quotient((double)x * r));
+  if (FMT == kNvFp4) {
+    const double m = e2m1_grid64(snap_quotient((double)fabsf(x) * r));
+    return x < 0.0f ? -m : m;
+  }
+  return (double)code_of<FMT>(x, gq);  // MX: d is a power of two, the fp32 quotient is exact
 }
 
 template <int FMT>

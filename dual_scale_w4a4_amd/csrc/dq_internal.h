@@ -126,6 +126,8 @@ hipError_t launch_vec(const VecArgs& a, hipStream_t s);
 hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s);
+// two-sweep pass for bf16 weights (dq_pass.hip): mode kModeRow, kModeCol or kModeRow | kModeEmit
+hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,

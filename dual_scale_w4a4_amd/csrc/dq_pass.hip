@@ -1,0 +1,298 @@
+// dq_pass.hip -- the two-sweep iteration pass for bf16 weights.
+//
+// With BF16 or E4M3 outer scales (INT4_BF16, NVFP4) the row update changes the codes, so an
+// iteration quantizes every element twice (daiwk notes, "核心公式": quantize, row update,
+// re-quantize with the inner copies synced, column update): a row pass with the current
+// row scales gives N_i = sum_j W_ij R_ij and D_i = sum_j R_ij^2 with R = Qhat D_b, and after
+// the row finalize a column pass with the updated scales gives P_j = sum_i W_ij S_ij and
+// Q_j = sum_i S_ij^2 with S = D_a Qhat. The MX formats take this pass too when the
+// single-sweep identity is not used.
+//
+// Layout (as the single-sweep pass): a workgroup of four 64-lane waves owns a 512-column
+// tile of a chunk of rows; a lane owns 8 consecutive columns, loaded with one 128-bit load
+// per row, so a wave-row is one contiguous 1 KiB segment. A wave takes its rows in batches
+// of 8 consecutive rows, 32 rows apart across the workgroup, with the loads of the next
+// step issued before the current rows are computed.
+//
+// Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact product
+// in fp64 and is accumulated in fp64 in a fixed order; a row's 64 lane partials are
+// transposed through LDS every 8 rows and added by 8 lanes per row, and the four waves'
+// column partials are added through LDS at the end. No floating-point atomics.
+#include <float.h>
+
+#include "dq_device.h"
+#include "dq_internal.h"
+
+namespace dq {
+
+constexpr int kPassBatch = 8;  // rows per wave between row reductions
+
+// One row of 8 elements of this lane: Q, and then (ROW) the lane's contribution to the
+// row sums, (COL) the column accumulators, (EMIT) the packed codes and the scale codes.
+template <int FMT, int LPG, int MODE, bool PARTIAL>
+__device__ __forceinline__ void pass_row(uint4 v, const float (&rb)[8], const double (&bbd)[8],
+                                         float ra, float ai, float g, float sixg, uint32_t amask,
+                                         double& nacc, double& dacc, double (&P)[8],
+                                         double (&Q)[8], int& flags, uint32_t* code_word,
+                                         void* scale_ptr) {
+  constexpr bool ROW = (MODE & kModeRow) != 0;
+  constexpr bool COL = (MODE & kModeCol) != 0;
+  constexpr bool EMIT = (MODE & kModeEmit) != 0;
+  uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  if (PARTIAL) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) u[k] &= amask;
+  }
+  float w[8], x[8];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    w[2 * k] = u2f(u[k] << 16);
+    w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
+  }
+  float mx = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    x[k] = (w[k] * rb[k]) * ra;  // column scale first, then row scale; two fp32 roundings
+    mx = fmaxf(mx, fabsf(x[k]));
+  }
+  float gm = u2f(group_max_bits<LPG>(f2u(mx)));
+  if (!(gm <= FLT_MAX)) {  // a scaled value overflowed
+    flags |= kStRange;
+    gm = 0.0f;
+  }
+  const GroupQ gq = group_scale<FMT>(gm, g, sixg);
+  const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
+  double q[8];  // the codes as values, through the snapped double quotient
+#pragma unroll
+  for (int k = 0; k < 8; k++) q[k] = code64<FMT>(x[k], r, gq);
+
+  if (ROW) {
+    double nl = 0.0, dl = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const double t = q[k] * bbd[k];  // R / d, exact
+      nl = fma((double)w[k], t, nl);
+      dl = fma(t, t, dl);
+    }
+    const double dd = (double)gq.d;
+    nacc = nl * dd;
+    dacc = dl * (dd * dd);
+  }
+  if (COL) {
+    const double c = (double)ai * (double)gq.d;  // exact
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const double s = c * q[k];  // S, exact
+      P[k] = fma((double)w[k], s, P[k]);
+      Q[k] = fma(s, s, Q[k]);
+    }
+  }
+  if (EMIT && (!PARTIAL || amask != 0u)) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) packed |= nibble_of<FMT>((float)q[k]) << (4 * k);
+    *code_word = packed;
+    if ((__lane_id() % LPG) == 0) {
+      if (FMT == kInt4Bf16)
+        *static_cast<uint16_t*>(scale_ptr) = (uint16_t)gq.scode;
+      else
+        *static_cast<uint8_t*>(scale_ptr) = (uint8_t)gq.scode;
+    }
+  }
+}
+
+// The pass. MODE: kModeRow, kModeCol or kModeRow | kModeEmit (the final Q with the row sums
+// of its error). S: rows per load step.
+template <int FMT, int G, int MODE, bool PARTIAL, int S>
+__global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
+  constexpr bool ROW = (MODE & kModeRow) != 0;
+  constexpr bool COL = (MODE & kModeCol) != 0;
+  constexpr bool EMIT = (MODE & kModeEmit) != 0;
+  constexpr int LPG = G / kEpl;
+  static_assert(kWaves * kPassBatch * kWave == kWaves * kTileCols, "one LDS buffer serves both");
+  __shared__ double2 smem[kWaves * kTileCols];
+
+  const uint16_t* W = static_cast<const uint16_t*>(p.W);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ct = blockIdx.x % p.nct;
+  const int rc = blockIdx.x / p.nct;
+  const int64_t r_begin = (int64_t)rc * p.rpc;
+  const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
+  const int64_t col = (int64_t)ct * kTileCols + lane * kEpl;
+  const bool act = col < p.n;
+  const int64_t lcol = act ? col : 0;  // in-bounds address
+  const uint32_t amask = act ? 0xFFFFFFFFu : 0u;
+
+  float rb[8];
+  double bbd[8];
+  {
+    const float4* rbp = reinterpret_cast<const float4*>(p.rb + lcol);
+    const float4* bbp = reinterpret_cast<const float4*>(p.b + lcol);
+    const float4 r0 = rbp[0], r1 = rbp[1], b0 = bbp[0], b1 = bbp[1];
+    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      rb[k] = act ? rr[k] : 1.0f;
+      bbd[k] = act ? (double)bv[k] : 0.0;
+    }
+  }
+  float g = 1.0f, sixg = 6.0f;
+  if (FMT == kNvFp4) {
+    g = p.gs[0];
+    sixg = p.gs[1];
+  }
+  double P[8], Q[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) P[k] = Q[k] = 0.0;
+  int flags = 0;
+
+  const int64_t first = r_begin + (int64_t)wave * kPassBatch;
+  const int64_t nbatch =
+      first < r_end ? (r_end - first + kWaves * kPassBatch - 1) / (kWaves * kPassBatch) : 0;
+  // loads of rows i .. i+S-1 from in-bounds addresses (rows past the chunk reload its first
+  // row and are skipped below; columns past n are masked in pass_row)
+  auto load = [&](int64_t i, uint4 (&buf)[S]) {
+#pragma unroll
+    for (int r = 0; r < S; r++) {
+      const int64_t row = i + r < r_end ? i + r : r_begin;
+      buf[r] = *reinterpret_cast<const uint4*>(W + row * p.n + lcol);
+    }
+  };
+  // the row scales of a batch: lane l holds those of row row0 + (l & 7) (clamped into the
+  // chunk), loaded one batch ahead, so that no row waits on a load of its own; a row takes
+  // them with a readlane
+  auto load_rows = [&](int64_t row0, float& ra_v, float& a_v) {
+    int64_t i = row0 + (lane & 7);
+    i = i < r_end ? i : r_begin;
+    ra_v = p.ra[i];
+    if (COL) a_v = p.a[i];
+  };
+  double2* R = smem + wave * (kPassBatch * kWave);  // this wave's [8 rows][64 lanes] partials
+  float ra_cur = 0.0f, a_cur = 0.0f, ra_nxt = 0.0f, a_nxt = 0.0f;
+  auto row_step = [&](uint4 v, int64_t i, int r) {
+    double nacc = 0.0, dacc = 0.0;
+    if (i < r_end) {  // uniform across the wave
+      const float ra = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_cur), r));
+      const float ai = COL ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a_cur), r)) : 0.0f;
+      uint32_t* code_word = nullptr;
+      void* scale_ptr = nullptr;
+      if (EMIT) {
+        code_word = reinterpret_cast<uint32_t*>(p.codes) + ((i * p.n + lcol) >> 3);
+        const int64_t si = i * (p.n / G) + lcol / G;
+        scale_ptr = FMT == kInt4Bf16 ? (void*)(static_cast<uint16_t*>(p.scales) + si)
+                                     : (void*)(static_cast<uint8_t*>(p.scales) + si);
+      }
+      pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, amask, nacc, dacc, P, Q,
+                                        flags, code_word, scale_ptr);
+    }
+    if (ROW) R[r * kWave + lane] = make_double2(nacc, dacc);
+  };
+
+  constexpr int kSteps = kPassBatch / S;
+  static_assert(kSteps % 2 == 0, "an even number of steps per batch");
+  uint4 bufA[S], bufB[S];
+  if (nbatch > 0) {
+    load_rows(first, ra_cur, a_cur);
+    load(first, bufA);
+  }
+  for (int64_t bt = 0; bt < nbatch; bt++) {
+    const int64_t row0 = first + bt * (kWaves * kPassBatch);
+    load_rows(row0 + kWaves * kPassBatch, ra_nxt, a_nxt);  // clamped past the last batch
+#pragma unroll
+    for (int st = 0; st < kSteps; st += 2) {
+      load(row0 + (st + 1) * S, bufB);
+#pragma unroll
+      for (int r = 0; r < S; r++) row_step(bufA[r], row0 + st * S + r, st * S + r);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < kSteps)
+        load(row0 + (st + 2) * S, bufA);
+      else if (bt + 1 < nbatch)
+        load(row0 + kWaves * kPassBatch, bufA);
+#pragma unroll
+      for (int r = 0; r < S; r++) row_step(bufB[r], row0 + (st + 1) * S + r, (st + 1) * S + r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ra_cur = ra_nxt;
+    a_cur = a_nxt;
+    if (ROW) {
+      // 8 rows done: 8 lanes per row add 8 lane partials each (transposed through LDS),
+      // then across the 8 lanes in a fixed order
+      __builtin_amdgcn_wave_barrier();
+      const double2* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
+      double N = 0.0, D = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const double2 v = src[k];
+        N += v.x;
+        D += v.y;
+      }
+      N = sum8_dpp(N);
+      D = sum8_dpp(D);
+      const int64_t i = row0 + (lane >> 3);
+      if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, D);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  if (COL) {  // the four waves' column sums, added in wave order
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; k++) smem[wave * kTileCols + lane * kEpl + k] = make_double2(P[k], Q[k]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < kTileCols; c += kBlock) {
+      double2 s = smem[c];
+#pragma unroll
+      for (int v = 1; v < kWaves; v++) {
+        s.x += smem[v * kTileCols + c].x;
+        s.y += smem[v * kTileCols + c].y;
+      }
+      const int64_t j = (int64_t)ct * kTileCols + c;
+      if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = s;
+    }
+  }
+  if (flags) atomicOr(p.status, flags);  // rare: only lanes that saw a problem
+}
+
+template <int FMT, int G, int MODE>
+static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
+  if (a.n % kTileCols != 0)
+    hipLaunchKernelGGL((k_pass<FMT, G, MODE, true, 2>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_pass<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int MODE>
+static hipError_t pass_group(const SweepArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.G) {
+    case 16: return pass_partial<FMT, 16, MODE>(a, grid, s);
+    case 32: return pass_partial<FMT, 32, MODE>(a, grid, s);
+    case 64: return pass_partial<FMT, 64, MODE>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int FMT>
+static hipError_t pass_mode(int mode, const SweepArgs& a, dim3 grid, hipStream_t s) {
+  switch (mode) {
+    case kModeRow: return pass_group<FMT, kModeRow>(a, grid, s);
+    case kModeCol: return pass_group<FMT, kModeCol>(a, grid, s);
+    case kModeRow | kModeEmit: return pass_group<FMT, kModeRow | kModeEmit>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nct * a.nrc));
+  switch (fmt) {
+    case kInt4Bf16: return pass_mode<kInt4Bf16>(mode, a, grid, s);
+    case kMxInt4: return pass_mode<kMxInt4>(mode, a, grid, s);
+    case kMxFp4: return pass_mode<kMxFp4>(mode, a, grid, s);
+    case kNvFp4: return pass_mode<kNvFp4>(mode, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dq

@@ -127,3 +127,37 @@ def test_group_quantizer_matches_oracle(H, oracle_lib, fmt, fid, group):
                      _p(q), _p(sc))
         assert np.array_equal(q.astype(np.float64), fb.unpack_codes(ref["codes"], fmt))
         assert np.array_equal(sc, ref["scales"].astype(np.uint32))
+
+
+def test_div7_is_the_correctly_rounded_quotient(H):
+    # the argument (a fractional part k/7 never near a rounding midpoint) does not depend on
+    # the exponent except where m / 7 is subnormal: every subnormal m, every m whose quotient
+    # is subnormal or at the boundary, and a few normal binades including the largest
+    H.h_div7_mismatches.restype = ctypes.c_int64
+    for e0, e1 in [(0, 3), (126, 128), (200, 200), (254, 254)]:
+        assert H.h_div7_mismatches(e0, e1) == 0, (e0, e1)
+
+
+def test_int4_quotient_rounding_at_ties_with_inexact_reciprocal(H):
+    # every bf16 significand at several exponents, plus subnormal bf16 divisors
+    sig = np.arange(128, 256, dtype=np.float64)
+    d = np.concatenate([sig * 2.0 ** e for e in (-140, -133, -127, -107, -20, -7, 0, 9, 60, 110)])
+    d = d[(d >= 2.0 ** -133) & (d < 2.0 ** 120)].astype(np.float32)
+    H.h_rne_quotient_mismatches.restype = ctypes.c_int64
+    assert H.h_rne_quotient_mismatches(_p(d), ctypes.c_int64(d.size)) == 0
+
+
+def test_double_quotient_codes_at_boundaries(H):
+    H.h_code64_mismatches.restype = ctypes.c_int64
+    sig = np.arange(128, 256, dtype=np.float64)
+    # INT4 divisors: bf16 values, normal and subnormal (down to the 2^-133 floor)
+    d = np.concatenate([sig * 2.0 ** e for e in (-140, -133, -127, -107, -20, -7, 0, 9, 60, 110)])
+    d = d[(d >= 2.0 ** -133) & (d < 2.0 ** 120)].astype(np.float32)
+    assert H.h_code64_mismatches(0, _p(d), ctypes.c_int64(d.size)) == 0
+    # NVFP4 divisors: fl32(s * g), s an E4M3 value, g an arbitrary fp32 tensor scale
+    rng = np.random.default_rng(5)
+    s = fb.E4M3_POS_VALS[fb.E4M3_POS_VALS > 0]
+    g = np.concatenate([np.exp(rng.uniform(-30, 30, 40)), [2.0 ** -126, 1.0, 1.0 / 3.0]])
+    d = (s[None, :].astype(np.float32) * g[:, None].astype(np.float32)).reshape(-1)
+    d = d[(d > 0) & np.isfinite(d)].astype(np.float32)
+    assert H.h_code64_mismatches(3, _p(d), ctypes.c_int64(d.size)) == 0
