@@ -123,7 +123,7 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.f_rpc = (m + f_want - 1) / f_want;
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
   p.f_nrc = (int)((m + p.f_rpc - 1) / p.f_rpc);
-  p.g_nct = p.nct;
+  p.g_nct = (int)((n + dq::pass_tile_cols() - 1) / dq::pass_tile_cols());
   int64_t g_want = (pass_target() + p.g_nct - 1) / p.g_nct;
   if (g_want < 1) g_want = 1;
   p.g_rpc = (m + g_want - 1) / g_want;

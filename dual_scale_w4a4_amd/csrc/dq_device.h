@@ -251,8 +251,8 @@ DQ_HD float code_of(float x, const GroupQ& gq) {
 // the code grid (a half-integer, or an E2M1 midpoint 1/4, 3/4, ..., 5) or at least 2^-29
 // away from every boundary: x - h d is a nonzero multiple of min(ulp(x), ulp(d)) / 4 and
 // x ~ h d bounds how small that is against d. A double quotient p = x * r with r within
-// 2^-48 of 1 / d (relative) is within 2^-44 of x / d, so snapping p onto the multiples of
-// 2^-32 keeps it on the same side of every boundary and makes it equal at a tie; the
+// 2^-48 of 1 / d (relative) is within 2^-44 of x / d, so snapping x * r onto the multiples
+// of 2^-32 keeps it on the same side of every boundary and makes it equal at a tie; the
 // hardware's round-to-nearest-even of the snapped value then gives the exact code.
 
 // 1 / v in double, relative error below 2^-48 (the hardware estimate and two Newton steps)
@@ -269,8 +269,9 @@ DQ_HD double recip64(float v) {
 #endif
 }
 
-// p (|p| < 2^19) rounded onto the multiples of 2^-32
-DQ_HD double snap_quotient(double p) { return (p + 0x1.8p20) - 0x1.8p20; }
+// x * r (|x r| < 2^19) rounded onto the multiples of 2^-32 with one rounding: the fused
+// multiply-add rounds the exact product plus C = 1.5 * 2^20, whose ulp is 2^-32
+DQ_HD double snap_quotient(double x, double r) { return fma(x, r, 0x1.8p20) - 0x1.8p20; }
 
 // E2M1 magnitude nearest to a snapped quotient v >= 0, ties to the even index, saturating:
 // adding C = 2^51 * max(1, 2^floor(log2 v)) puts the double ulp at the grid spacing of v's
@@ -287,9 +288,9 @@ DQ_HD double e2m1_grid64(double v) {
 // acts, because |x| <= mx and s >= (mx / 7)(1 - 2^-8) keep |x / s| below 7.03
 template <int FMT>
 DQ_HD double code64(float x, double r, const GroupQ& gq) {
-  if (FMT == kInt4Bf16) return rint(snap_quotient((double)x * r));
+  if (FMT == kInt4Bf16) return rint(snap_quotient((double)x, r));
   if (FMT == kNvFp4) {
-    const double m = e2m1_grid64(snap_quotient((double)fabsf(x) * r));
+    const double m = e2m1_grid64(snap_quotient((double)fabsf(x), r));
     return x < 0.0f ? -m : m;
   }
   return (double)code_of<FMT>(x, gq);  // MX: d is a power of two, the fp32 quotient is exact

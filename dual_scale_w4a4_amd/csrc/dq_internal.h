@@ -126,8 +126,10 @@ hipError_t launch_vec(const VecArgs& a, hipStream_t s);
 hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);
 hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStream_t s);
-// two-sweep pass for bf16 weights (dq_pass.hip): mode kModeRow, kModeCol or kModeRow | kModeEmit
+// two-sweep pass for bf16 weights (dq_pass.hip): mode kModeRow, kModeCol or kModeRow | kModeEmit;
+// SweepArgs::nct counts tiles of pass_tile_cols() columns
 hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s);
+int pass_tile_cols();
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,

@@ -447,33 +447,56 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
 }
 
 // ------------------------------------------------------------------------- row statistics
-// E_i = sum_j W_ij^2 (fp64, fixed order), a non-finite check on W, and optionally the row
-// max of |X| at the initial scales (NVFP4 tensor scale). One wave per row.
-template <bool BF>
+// E_i = sum_j W_ij^2 (fp64, fixed order), a non-finite check on W, and (AMAX) the row max of
+// |X| at the initial scales (NVFP4 tensor scale). One wave per row; each step has four
+// 512-column tiles in flight, summed into four accumulators that are added in a fixed order.
+constexpr int kStatTiles = 4;
+
+template <bool BF, bool AMAX>
 __global__ __launch_bounds__(kBlock) void k_rowstat(RowStatArgs p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t i = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   if (i >= p.m) return;
-  double e = 0.0;
-  float mx = 0.0f;
-  const float ra = p.ra[i];
-  for (int64_t c = (int64_t)lane * kEpl; c < p.n; c += kTileCols) {
-    float w[8];
-    load8<BF>(p.W, i * p.n + c, true, w);
+  double e[kStatTiles];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      e = fma((double)w[k], (double)w[k], e);
-      if (p.amax) mx = fmaxf(mx, fabsf((w[k] * p.rb[c + k]) * ra));
+  for (int u = 0; u < kStatTiles; u++) e[u] = 0.0;
+  float mx = 0.0f;
+  const float ra = AMAX ? p.ra[i] : 1.0f;
+  for (int64_t c0 = (int64_t)lane * kEpl; c0 < p.n; c0 += kStatTiles * kTileCols) {
+    float w[kStatTiles][8], rb[kStatTiles][8];
+#pragma unroll
+    for (int u = 0; u < kStatTiles; u++) {
+      const int64_t c = c0 + u * kTileCols;
+      const bool act = c < p.n;
+      load8<BF>(p.W, i * p.n + c, act, w[u]);
+      if (AMAX) {
+        float4 r0 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), r1 = r0;
+        if (act) {
+          r0 = reinterpret_cast<const float4*>(p.rb + c)[0];
+          r1 = reinterpret_cast<const float4*>(p.rb + c)[1];
+        }
+        rb[u][0] = r0.x; rb[u][1] = r0.y; rb[u][2] = r0.z; rb[u][3] = r0.w;
+        rb[u][4] = r1.x; rb[u][5] = r1.y; rb[u][6] = r1.z; rb[u][7] = r1.w;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kStatTiles; u++)
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        e[u] = fma((double)w[u][k], (double)w[u][k], e[u]);
+        if (AMAX) mx = fmaxf(mx, fabsf((w[u][k] * rb[u][k]) * ra));
+      }
   }
-  e = wave_sum(e);
-  if (p.amax) mx = wave_max(mx);
+  static_assert(kStatTiles == 4, "the fixed order below adds four accumulators");
+  double et = (e[0] + e[1]) + (e[2] + e[3]);
+  et = wave_sum(et);
+  if (AMAX) mx = wave_max(mx);
   if (lane == 0) {
-    p.E[i] = e;
-    if (p.amax) p.amax[i] = mx;
+    p.E[i] = et;
+    if (AMAX) p.amax[i] = mx;
     int f = 0;
-    if (!(e <= DBL_MAX)) f |= kStNonFinite;      // W^2 never overflows fp64: e is finite
-    if (p.amax && !(mx <= FLT_MAX)) f |= kStRange;  // iff W is
+    if (!(et <= DBL_MAX)) f |= kStNonFinite;     // W^2 never overflows fp64: E is finite
+    if (AMAX && !(mx <= FLT_MAX)) f |= kStRange;  // iff W is
     atomic_flag(p.status, f);
   }
 }
@@ -683,10 +706,17 @@ hipError_t launch_vec(const VecArgs& a, hipStream_t s) {
 
 hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.m + kWaves - 1) / kWaves));
-  if (bf16)
-    hipLaunchKernelGGL(k_rowstat<true>, grid, dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_rowstat<false>, grid, dim3(kBlock), 0, s, a);
+  if (bf16) {
+    if (a.amax)
+      hipLaunchKernelGGL((k_rowstat<true, true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_rowstat<true, false>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    if (a.amax)
+      hipLaunchKernelGGL((k_rowstat<false, true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_rowstat<false, false>), grid, dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -8,14 +8,16 @@
 // Q_j = sum_i S_ij^2 with S = D_a Qhat. The MX formats take this pass too when the
 // single-sweep identity is not used.
 //
-// Layout (as the single-sweep pass): a workgroup of four 64-lane waves owns a 512-column
-// tile of a chunk of rows; a lane owns 8 consecutive columns, loaded with one 128-bit load
-// per row, so a wave-row is one contiguous 1 KiB segment. A wave takes its rows in batches
-// of 8 consecutive rows, 32 rows apart across the workgroup, with the loads of the next
-// step issued before the current rows are computed.
+// Layout: a workgroup of four 64-lane waves owns a 1024-column tile of a chunk of rows; a
+// lane owns 16 consecutive columns (two 128-bit loads per row), so a group of G columns
+// spans G / 16 lanes and the per-group work (absmax, scale rule, reciprocal) is shared by
+// 16 elements per lane. A wave takes its rows in batches of 8 consecutive rows, 32 rows
+// apart across the workgroup, with the loads of the next step, and the row scales of the
+// next batch, issued before the current rows are computed.
 //
-// Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact product
-// in fp64 and is accumulated in fp64 in a fixed order; a row's 64 lane partials are
+// Codes come from the snapped double quotient (code64): exact, and already in fp64 for the
+// sums. Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact
+// product in fp64 and is accumulated in fp64 in a fixed order; a row's 64 lane partials are
 // transposed through LDS every 8 rows and added by 8 lanes per row, and the four waves'
 // column partials are added through LDS at the end. No floating-point atomics.
 #include <float.h>
@@ -25,51 +27,55 @@
 
 namespace dq {
 
-constexpr int kPassBatch = 8;  // rows per wave between row reductions
+constexpr int kPassBatch = 8;                // rows per wave between row reductions
+constexpr int kPassEpl = 16;                 // consecutive columns per lane
+constexpr int kPassCols = kWave * kPassEpl;  // 1024 columns per tile
 
-// One row of 8 elements of this lane: Q, and then (ROW) the lane's contribution to the
-// row sums, (COL) the column accumulators, (EMIT) the packed codes and the scale codes.
+// One row of this lane's 16 elements: Q, and then (ROW) the lane's contribution to the row
+// sums, (COL) the column accumulators, (EMIT) the packed codes and the scale codes.
 template <int FMT, int LPG, int MODE, bool PARTIAL>
-__device__ __forceinline__ void pass_row(uint4 v, const float (&rb)[8], const double (&bbd)[8],
-                                         float ra, float ai, float g, float sixg, uint32_t amask,
-                                         double& nacc, double& dacc, double (&P)[8],
-                                         double (&Q)[8], int& flags, uint32_t* code_word,
+__device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[kPassEpl],
+                                         const double (&bbd)[kPassEpl], float ra, float ai,
+                                         float g, float sixg, uint32_t amask, double& nacc,
+                                         double& dacc, double (&P)[kPassEpl],
+                                         double (&Q)[kPassEpl], int& flags, uint32_t* code_word,
                                          void* scale_ptr) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
   constexpr bool COL = (MODE & kModeCol) != 0;
   constexpr bool EMIT = (MODE & kModeEmit) != 0;
-  uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  constexpr int E = kPassEpl;
+  uint32_t u[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
   if (PARTIAL) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) u[k] &= amask;
+    for (int k = 0; k < 8; k++) u[k] &= amask;
   }
-  float w[8], x[8];
+  float w[E], x[E];
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
+  for (int k = 0; k < 8; k++) {
     w[2 * k] = u2f(u[k] << 16);
     w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
   }
   float mx = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; k++) {
+  for (int k = 0; k < E; k++) {
     x[k] = (w[k] * rb[k]) * ra;  // column scale first, then row scale; two fp32 roundings
     mx = fmaxf(mx, fabsf(x[k]));
   }
-  float gm = u2f(group_max_bits<LPG>(f2u(mx)));
+  float gm = LPG > 1 ? u2f(group_max_bits<LPG>(f2u(mx))) : mx;
   if (!(gm <= FLT_MAX)) {  // a scaled value overflowed
     flags |= kStRange;
     gm = 0.0f;
   }
   const GroupQ gq = group_scale<FMT>(gm, g, sixg);
   const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
-  double q[8];  // the codes as values, through the snapped double quotient
+  double q[E];  // the codes as values
 #pragma unroll
-  for (int k = 0; k < 8; k++) q[k] = code64<FMT>(x[k], r, gq);
+  for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);
 
   if (ROW) {
     double nl = 0.0, dl = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < E; k++) {
       const double t = q[k] * bbd[k];  // R / d, exact
       nl = fma((double)w[k], t, nl);
       dl = fma(t, t, dl);
@@ -81,17 +87,17 @@ __device__ __forceinline__ void pass_row(uint4 v, const float (&rb)[8], const do
   if (COL) {
     const double c = (double)ai * (double)gq.d;  // exact
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < E; k++) {
       const double s = c * q[k];  // S, exact
       P[k] = fma((double)w[k], s, P[k]);
       Q[k] = fma(s, s, Q[k]);
     }
   }
   if (EMIT && (!PARTIAL || amask != 0u)) {
-    uint32_t packed = 0;
+    uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 8; k++) packed |= nibble_of<FMT>((float)q[k]) << (4 * k);
-    *code_word = packed;
+    for (int k = 0; k < E; k++) packed[k / 8] |= nibble_of<FMT>((float)q[k]) << (4 * (k % 8));
+    *reinterpret_cast<uint2*>(code_word) = make_uint2(packed[0], packed[1]);
     if ((__lane_id() % LPG) == 0) {
       if (FMT == kInt4Bf16)
         *static_cast<uint16_t*>(scale_ptr) = (uint16_t)gq.scode;
@@ -102,15 +108,18 @@ __device__ __forceinline__ void pass_row(uint4 v, const float (&rb)[8], const do
 }
 
 // The pass. MODE: kModeRow, kModeCol or kModeRow | kModeEmit (the final Q with the row sums
-// of its error). S: rows per load step.
+// of its error). S: rows per load step. G >= 16; LPG = G / 16 lanes per group.
 template <int FMT, int G, int MODE, bool PARTIAL, int S>
 __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
   constexpr bool COL = (MODE & kModeCol) != 0;
   constexpr bool EMIT = (MODE & kModeEmit) != 0;
-  constexpr int LPG = G / kEpl;
-  static_assert(kWaves * kPassBatch * kWave == kWaves * kTileCols, "one LDS buffer serves both");
-  __shared__ double2 smem[kWaves * kTileCols];
+  constexpr int LPG = G / kPassEpl;
+  constexpr int E = kPassEpl;
+  // LDS: a wave's [8 rows][64 lanes] row partials, or the column combine of half a tile
+  constexpr int kLds = kWaves * kPassBatch * kWave;
+  static_assert(kLds == kWaves * (kPassCols / 2), "one LDS buffer serves both");
+  __shared__ double2 smem[kLds];
 
   const uint16_t* W = static_cast<const uint16_t*>(p.W);
   const int lane = threadIdx.x & (kWave - 1);
@@ -119,23 +128,23 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
   const int rc = blockIdx.x / p.nct;
   const int64_t r_begin = (int64_t)rc * p.rpc;
   const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
-  const int64_t col = (int64_t)ct * kTileCols + lane * kEpl;
-  const bool act = col < p.n;
+  const int64_t col = (int64_t)ct * kPassCols + lane * E;
+  const bool act = col < p.n;          // n is a multiple of 16: a lane is wholly in or out
   const int64_t lcol = act ? col : 0;  // in-bounds address
   const uint32_t amask = act ? 0xFFFFFFFFu : 0u;
 
-  float rb[8];
-  double bbd[8];
-  {
-    const float4* rbp = reinterpret_cast<const float4*>(p.rb + lcol);
-    const float4* bbp = reinterpret_cast<const float4*>(p.b + lcol);
-    const float4 r0 = rbp[0], r1 = rbp[1], b0 = bbp[0], b1 = bbp[1];
-    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  float rb[E];
+  double bbd[E];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      rb[k] = act ? rr[k] : 1.0f;
-      bbd[k] = act ? (double)bv[k] : 0.0;
+  for (int h = 0; h < E / 4; h++) {
+    const float4 rv = reinterpret_cast<const float4*>(p.rb + lcol)[h];
+    const float4 bv = reinterpret_cast<const float4*>(p.b + lcol)[h];
+    const float rr[4] = {rv.x, rv.y, rv.z, rv.w};
+    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      rb[4 * h + k] = act ? rr[k] : 1.0f;
+      bbd[4 * h + k] = act ? (double)bb[k] : 0.0;
     }
   }
   float g = 1.0f, sixg = 6.0f;
@@ -143,9 +152,9 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
     g = p.gs[0];
     sixg = p.gs[1];
   }
-  double P[8], Q[8];
+  double P[E], Q[E];
 #pragma unroll
-  for (int k = 0; k < 8; k++) P[k] = Q[k] = 0.0;
+  for (int k = 0; k < E; k++) P[k] = Q[k] = 0.0;
   int flags = 0;
 
   const int64_t first = r_begin + (int64_t)wave * kPassBatch;
@@ -153,15 +162,17 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
       first < r_end ? (r_end - first + kWaves * kPassBatch - 1) / (kWaves * kPassBatch) : 0;
   // loads of rows i .. i+S-1 from in-bounds addresses (rows past the chunk reload its first
   // row and are skipped below; columns past n are masked in pass_row)
-  auto load = [&](int64_t i, uint4 (&buf)[S]) {
+  auto load = [&](int64_t i, uint4 (&buf)[S][2]) {
 #pragma unroll
     for (int r = 0; r < S; r++) {
       const int64_t row = i + r < r_end ? i + r : r_begin;
-      buf[r] = *reinterpret_cast<const uint4*>(W + row * p.n + lcol);
+      const uint4* src = reinterpret_cast<const uint4*>(W + row * p.n + lcol);
+      buf[r][0] = src[0];
+      buf[r][1] = src[1];
     }
   };
   // the row scales of a batch: lane l holds those of row row0 + (l & 7) (clamped into the
-  // chunk), loaded one batch ahead, so that no row waits on a load of its own; a row takes
+  // chunk), loaded one batch ahead so that no row waits on a load of its own; a row takes
   // them with a readlane
   auto load_rows = [&](int64_t row0, float& ra_v, float& a_v) {
     int64_t i = row0 + (lane & 7);
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
   };
   double2* R = smem + wave * (kPassBatch * kWave);  // this wave's [8 rows][64 lanes] partials
   float ra_cur = 0.0f, a_cur = 0.0f, ra_nxt = 0.0f, a_nxt = 0.0f;
-  auto row_step = [&](uint4 v, int64_t i, int r) {
+  auto row_step = [&](const uint4 (&v)[2], int64_t i, int r) {
     double nacc = 0.0, dacc = 0.0;
     if (i < r_end) {  // uniform across the wave
       const float ra = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_cur), r));
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
 
   constexpr int kSteps = kPassBatch / S;
   static_assert(kSteps % 2 == 0, "an even number of steps per batch");
-  uint4 bufA[S], bufB[S];
+  uint4 bufA[S][2], bufB[S][2];
   if (nbatch > 0) {
     load_rows(first, ra_cur, a_cur);
     load(first, bufA);
@@ -236,20 +247,29 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
     }
   }
 
-  if (COL) {  // the four waves' column sums, added in wave order
-    __syncthreads();
+  if (COL) {
+    // the four waves' column sums, added in wave order, half a tile (lanes 0..31, then
+    // 32..63) at a time
+    constexpr int kHalf = kPassCols / 2;
 #pragma unroll
-    for (int k = 0; k < 8; k++) smem[wave * kTileCols + lane * kEpl + k] = make_double2(P[k], Q[k]);
-    __syncthreads();
-    for (int c = threadIdx.x; c < kTileCols; c += kBlock) {
-      double2 s = smem[c];
+    for (int h = 0; h < 2; h++) {
+      __syncthreads();
+      if ((lane >> 5) == h) {
 #pragma unroll
-      for (int v = 1; v < kWaves; v++) {
-        s.x += smem[v * kTileCols + c].x;
-        s.y += smem[v * kTileCols + c].y;
+        for (int k = 0; k < E; k++)
+          smem[wave * kHalf + (lane & 31) * E + k] = make_double2(P[k], Q[k]);
       }
-      const int64_t j = (int64_t)ct * kTileCols + c;
-      if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = s;
+      __syncthreads();
+      for (int c = threadIdx.x; c < kHalf; c += kBlock) {
+        double2 s = smem[c];
+#pragma unroll
+        for (int v = 1; v < kWaves; v++) {
+          s.x += smem[v * kHalf + c].x;
+          s.y += smem[v * kHalf + c].y;
+        }
+        const int64_t j = (int64_t)ct * kPassCols + h * kHalf + c;
+        if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = s;
+      }
     }
   }
   if (flags) atomicOr(p.status, flags);  // rare: only lanes that saw a problem
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
 
 template <int FMT, int G, int MODE>
 static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
-  if (a.n % kTileCols != 0)
+  if (a.n % kPassCols != 0)
     hipLaunchKernelGGL((k_pass<FMT, G, MODE, true, 2>), grid, dim3(kBlock), 0, s, a);
   else
     hipLaunchKernelGGL((k_pass<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, a);
@@ -283,6 +303,8 @@ static hipError_t pass_mode(int mode, const SweepArgs& a, dim3 grid, hipStream_t
     default: return hipErrorInvalidValue;
   }
 }
+
+int pass_tile_cols() { return kPassCols; }
 
 hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.nct * a.nrc));
