@@ -37,7 +37,7 @@ COUNTERS = {
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
     "fetch_kib": 57469.0, "fetch_scale": 2.0,
     "write_kib": 7584.0, "write_scale": 1.0,
-    "sources_sha256": "f165a313bdab1db07820477a5c3b86b5cc9d8cee2f151cdea10a755b58cbb0cd",
+    "sources_sha256": "ef105b59587d48db3eba7bfe167184021da26fbc2de6f24fdec08ef918f06600",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -137,10 +137,14 @@ def main() -> None:
 
         pool = ThreadPoolExecutor(max_workers=len(mats))
 
+    # read in full before each cold re-run of the dominant pass: twice the 256 MB
+    # Infinity Cache, so that W is evicted from every cache level
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+
     def solve_one(k, T, timing, stream):
         w = mats[k]
         return dq.solve(dev_w[k], w.fmt, w.group, w.T if T is None else T, workspace=wss[k],
-                        timing=timing, stream=stream)
+                        timing=timing, stream=stream, flush=flush if timing else None)
 
     def step(T=None, timing=False):
         # dq_solve returns when its stream is done; concurrent calls use separate streams
@@ -172,6 +176,7 @@ def main() -> None:
     bytes_per_elem = 2 if mats[0].dtype == "bf16" else 4
     ms_all, used_fused = {}, True
     iso = [0.0, 0, 0.0]  # ms, launches, bytes of the isolated back-to-back runs
+    cw = [0.0, 0.0, 0, 0.0]  # cold ms, warm ms, launches, bytes of the one-at-a-time re-runs
     for _ in range(args.steps):
         for w, o in zip(mats, step(timing=True)):
             used_fused = used_fused and o["used_fused"]
@@ -182,6 +187,11 @@ def main() -> None:
             iso[0] += o["isolated"][0]
             iso[1] += o["isolated"][1]
             iso[2] += o["isolated"][1] * w.rows * w.cols * bytes_per_elem
+            cold, warm, n1 = o["cold_warm"]
+            cw[0] += cold
+            cw[1] += warm
+            cw[2] += n1
+            cw[3] += n1 * w.rows * w.cols * bytes_per_elem
     ms_kind, n_kind = ms_all[kind]
     # dominant kernel: each launch reads every weight of its matrix once, T launches per solve
     bytes_total = args.steps * sum(w.rows * w.cols * bytes_per_elem * w.T for w in mats)
@@ -220,7 +230,7 @@ def main() -> None:
         "per_iteration": {"ms": t_iter * 1e3, "elems_per_s": elems / t_iter,
                           "GBps_one_read_of_W": iter_gbs, "frac_hbm_peak": iter_gbs / HBM_PEAK_GBS,
                           "ms_per_step_T0": t_step0 * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "k_fused_mx" if kind == "fused" else "k_sweep (row mode)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_fused_mx" if kind == "fused" else "k_pass (row mode)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counted_traffic(args.workload, kind == "fused" and used_fused),
                      "traffic_unit": "bytes per launch", "avg_launch_us": avg_launch_ms * 1e3,
@@ -229,6 +239,13 @@ def main() -> None:
                      "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}},
         "mse": {"first": mse_first, "final": mse_final,
                 "ratio_first_over_final": [a / b for a, b in zip(mse_first, mse_final)]},
+        "cache": None if cw[2] == 0 else {
+            "method": "dominant pass timed one launch at a time with HIP events, cold = after "
+                      "a full read of a 512 MiB buffer (evicts W from L2 and the 256 MB "
+                      "Infinity Cache), warm = back to back (W of 117 MB can stay in it)",
+            "cold_us": cw[0] / cw[2] * 1e3, "warm_us": cw[1] / cw[2] * 1e3,
+            "cold_GBps": cw[3] / (cw[0] * 1e-3) / 1e9, "warm_GBps": cw[3] / (cw[1] * 1e-3) / 1e9,
+            "warm_over_cold_speed": cw[0] / cw[1]},
         "single_sweep_path": used_fused if kind == "fused" else None,
         "concurrent_matrices": pool is not None,
     }

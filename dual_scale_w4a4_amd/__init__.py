@@ -35,7 +35,9 @@ class DQError(RuntimeError):
 class _Timing(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
                 ("used_fused", ctypes.c_int), ("isolated_ms", ctypes.c_double),
-                ("isolated_launches", ctypes.c_int)]
+                ("isolated_launches", ctypes.c_int), ("flush", ctypes.c_void_p),
+                ("flush_bytes", ctypes.c_size_t), ("cold_ms", ctypes.c_double),
+                ("warm_ms", ctypes.c_double), ("per_launch", ctypes.c_int)]
 
 
 class _Init(ctypes.Structure):
@@ -122,11 +124,12 @@ def _vec(v, n, device):
 
 def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
           two_sweep: bool = False, workspace=None, timing: bool = False,
-          stream=None) -> Dict[str, object]:
+          stream=None, flush=None) -> Dict[str, object]:
     """dq_solve on W (rows x cols, CUDA float32 / bfloat16). Returns a dict of device
     tensors codes (rows x cols/2 u8), scales (rows x cols/group; int16 holding bf16 bits for
     int4_bf16, else u8), a, b (float32), mse (T+1 float64), g (float32[1]) and, when
-    ``timing``, per-kernel-kind milliseconds and launch counts."""
+    ``timing``, per-kernel-kind milliseconds and launch counts (``flush``: a device buffer
+    read in full before each cold re-run of the single-sweep pass)."""
     torch = _torch()
     dt = _check_w(W)
     rows, cols = W.shape
@@ -139,6 +142,9 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
     a0 = _vec(a0, rows, dev)
     b0 = _vec(b0, cols, dev)
     tm = _Timing() if timing else None
+    if tm is not None and flush is not None:
+        tm.flush = flush.data_ptr()
+        tm.flush_bytes = flush.numel() * flush.element_size() // 16 * 16
     init = _Init(_ptr(a0), _ptr(b0), float(g0), SOLVE_TWO_SWEEP if two_sweep else 0,
                  ctypes.pointer(tm) if tm is not None else None)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
@@ -154,6 +160,7 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
         out["timing"] = {k: (tm.ms[i], tm.launches[i]) for i, k in enumerate(KERNEL_KINDS)}
         out["used_fused"] = bool(tm.used_fused)
         out["isolated"] = (tm.isolated_ms, tm.isolated_launches)
+        out["cold_warm"] = (tm.cold_ms, tm.warm_ms, tm.per_launch)
     return out
 
 

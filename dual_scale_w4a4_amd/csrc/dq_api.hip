@@ -463,10 +463,27 @@ dq_status time_isolated(const Plan& p, char* ws, const void* W, float* a, const 
   DQ_TRY(hipEventSynchronize(e1));
   float ms = 0.0f;
   DQ_TRY(hipEventElapsedTime(&ms, e0, e1));
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
   out->isolated_ms = ms;
   out->isolated_launches = kReps;
+  if (out->flush && out->flush_bytes >= 16) {
+    // one launch at a time, after a full read of the flush buffer (cold) and without (warm)
+    double cold = 0.0, warm = 0.0;
+    for (int pass = 0; pass < 2; pass++)
+      for (int r = 0; r < kReps; r++) {
+        if (pass == 0) DQ_TRY(launch_flush(out->flush, out->flush_bytes / 16, fu.status + 1, s));
+        DQ_TRY(hipEventRecord(e0, s));
+        DQ_TRY(launch_fused(p.fmt, false, fu, s));
+        DQ_TRY(hipEventRecord(e1, s));
+        DQ_TRY(hipEventSynchronize(e1));
+        DQ_TRY(hipEventElapsedTime(&ms, e0, e1));
+        (pass == 0 ? cold : warm) += ms;
+      }
+    out->cold_ms = cold;
+    out->warm_ms = warm;
+    out->per_launch = kReps;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   return DQ_OK;
 }
 
@@ -535,11 +552,16 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
   const bool mx = fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4;
   bool fused = mx && !(init && (init->flags & DQ_SOLVE_TWO_SWEEP));
   dq_timing* timing = init ? init->timing : nullptr;
-  if (timing) memset(timing, 0, sizeof *timing);
 
   int flags = 0;
+  const void* flush = timing ? timing->flush : nullptr;
+  const size_t flush_bytes = timing ? timing->flush_bytes : 0;
   for (int attempt = 0; attempt < 2; attempt++) {
-    if (timing) memset(timing, 0, sizeof *timing);
+    if (timing) {
+      memset(timing, 0, sizeof *timing);
+      timing->flush = flush;
+      timing->flush_bytes = flush_bytes;
+    }
     Timer tm{timing, stream};
     st = enqueue_solve(p, ws.ptr, io, fused, attempt > 0, tm, stream);
     if (st != DQ_OK) return st;

@@ -122,6 +122,9 @@ struct FinArgs {
 };
 
 hipError_t launch_clear(int* words, int count, hipStream_t s);
+// reads `vec16` 16-byte words of buf in full (to evict other data from the caches); `sink`
+// is written only if the data has an impossible checksum, so that the reads stay
+hipError_t launch_flush(const void* buf, size_t vec16, int* sink, hipStream_t s);
 hipError_t launch_vec(const VecArgs& a, hipStream_t s);
 hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s);
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s);

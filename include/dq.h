@@ -92,6 +92,15 @@ typedef struct {
      back to back between one pair of events (results unchanged); this is its time */
   double isolated_ms;
   int isolated_launches;
+  /* in (kept by the call): an optional device buffer of flush_bytes bytes (a multiple of 16).
+     When given, the re-runs are also timed one launch at a time, cold_ms after a full read
+     of this buffer before each launch (evicting W from the caches when it is larger than
+     them) and warm_ms without it; per_launch re-runs each */
+  const void* flush;
+  size_t flush_bytes;
+  double cold_ms;
+  double warm_ms;
+  int per_launch;
 } dq_timing;
 
 typedef struct {
