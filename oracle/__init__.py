@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         P, I, I64, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
         L.dq_ref_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P]
         L.dq_ref_quantize.restype = I
+        L.dq_ref_quantize_act.argtypes = [P, I, I64, I64, I, I, P, P, P, P]
+        L.dq_ref_quantize_act.restype = I
         L.dq_ref_solve.argtypes = [P, I, I64, I64, I, I, I, P, P, F, P, P, P, P, P, P]
         L.dq_ref_solve.restype = I
         L.dq_ref_solve_diag.argtypes = [P, I, I64, I64, I, I, I, P, P, F, P, P, P, P, P, P, P, P]
@@ -109,6 +111,23 @@ def quantize(W: np.ndarray, dtype: str, fmt: str, group: int, a=None, b=None,
     gbuf = np.array([g], np.float32)
     st = lib().dq_ref_quantize(_ptr(W), DTYPE[dtype], rows, cols, FMT[fmt], group, _ptr(a),
                                _ptr(b), _ptr(gbuf), _ptr(codes), _ptr(scales))
+    if st:
+        raise OracleError(st)
+    return {"codes": codes, "scales": scales, "g": float(gbuf[0])}
+
+
+def quantize_act(X: np.ndarray, dtype: str, fmt: str, group: int, b=None,
+                 g: float = 0.0) -> Dict[str, np.ndarray]:
+    """Activation quantization: Q of x = fl32(X * b) per row (tokens x cols), groups along
+    the channels. Returns codes (tokens x cols/2 u8), scales, g."""
+    X = _prep_w(X, dtype)
+    rows, cols = X.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // group), _scale_dtype(fmt))
+    b = None if b is None else np.ascontiguousarray(b, np.float32)
+    gbuf = np.array([g], np.float32)
+    st = lib().dq_ref_quantize_act(_ptr(X), DTYPE[dtype], rows, cols, FMT[fmt], group, _ptr(b),
+                                   _ptr(gbuf), _ptr(codes), _ptr(scales))
     if st:
         raise OracleError(st)
     return {"codes": codes, "scales": scales, "g": float(gbuf[0])}

@@ -489,6 +489,65 @@ done:
   return st;
 }
 
+/* ------------------------------------------------- public: activation quantization */
+
+/* The consumer side of the factorized product (daiwk notes, "核心公式" eq. 1: X W^T ~=
+ * (X D_beta^-1) Qhat^T D_alpha^-1 with D_beta^-1 = D_b; the flowchart's step that scales the
+ * real activations by the column inverse scales before quantizing them): every activation
+ * row is scaled channel by channel, x_tj = fl32(X_tj * b_j), and quantized by the same group
+ * quantizer Q as the weights, in groups of `group` consecutive channels (reading: one
+ * quantizer per format for weights and activations, as in the W+A rows of the pages'
+ * Table 1). NVFP4: g as for the weights, from max |x| of this tensor unless given. */
+int dq_ref_quantize_act(const void* X, int xt, int64_t tokens, int64_t cols, int fmt, int group,
+                        const float* b, float* g_inout, uint8_t* codes, void* scales) {
+  int st = check_common(X, xt, tokens, cols, fmt, group);
+  if (st) return st;
+  if (!codes || !scales || (fmt == DQR_FMT_NVFP4 && !g_inout)) return DQR_ERR_ARG;
+  if (b && !positive_finite(b, cols)) return DQR_ERR_ARG;
+  if (fmt == DQR_FMT_NVFP4 && (isnan(*g_inout) || isinf(*g_inout))) return DQR_ERR_ARG;
+  ctx_t c = {X, xt, tokens, cols, fmt, group, cols / group, 1.0f, 6.0f};
+  if (!w_finite(&c)) return DQR_ERR_NONFINITE;
+  const int64_t n = cols, ng = c.ng;
+  float* x = malloc(sizeof(float) * (size_t)(tokens * n));
+  int8_t* q2 = malloc((size_t)(tokens * n));
+  double* dv = malloc(sizeof(double) * (size_t)(tokens * ng));
+  uint16_t* sc = malloc(sizeof(uint16_t) * (size_t)(tokens * ng));
+  if (!x || !q2 || !dv || !sc) {
+    st = DQR_ERR_INTERNAL;
+    goto done;
+  }
+  float A = 0.0f;
+  for (int64_t t = 0; t < tokens; t++)
+    for (int64_t j = 0; j < n; j++) {
+      const float v = fl32_mul(w_at(&c, t, j), b ? b[j] : 1.0f);
+      if (!isfinite(v)) {
+        st = DQR_ERR_RANGE;
+        goto done;
+      }
+      x[t * n + j] = v;
+      A = fmaxf(A, fabsf(v));
+    }
+  if (fmt == DQR_FMT_NVFP4) {
+    if (!(*g_inout > 0.0f)) {
+      float g = A == 0.0f ? 1.0f : fl32_div(A, 2688.0f);
+      *g_inout = g < 0x1p-126f ? 0x1p-126f : g;
+    }
+    c.g = *g_inout;
+    c.sixg = fl32_mul(6.0f, c.g);
+  }
+  for (int64_t t = 0; t < tokens; t++)
+    for (int64_t gi = 0; gi < ng; gi++)
+      quant_group(&c, x + t * n + gi * group, q2 + t * n + gi * group, dv + t * ng + gi,
+                  sc + t * ng + gi);
+  emit(&c, q2, sc, codes, scales);
+done:
+  free(x);
+  free(q2);
+  free(dv);
+  free(sc);
+  return st;
+}
+
 /* ----------------------------------------------------------------- public: the solver */
 
 int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int group,

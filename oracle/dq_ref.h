@@ -56,6 +56,16 @@ int dq_ref_quantize(const void* W, int wt, int64_t rows, int64_t cols, int fmt, 
                     const float* a, const float* b, float* g_inout, uint8_t* codes,
                     void* scales);
 
+/* Activation quantization with the column inverse scales (the consumer side of the
+ * factorized product): x_tj = fl32(X_tj * b_j) for X of tokens x cols (xt: DQR_F32 or
+ * DQR_BF16), then Q per group of `group` consecutive channels, exactly as dq_ref_quantize
+ * quantizes a scaled weight tile. b: NULL means ones, else positive and finite values used
+ * as given. g_inout (NVFP4 only): if *g_inout > 0 it is used, else g = fl32(max|x| / 2688)
+ * (at least 2^-126; 1 if x == 0) is computed and written back. codes and scales are laid
+ * out as for dq_ref_quantize. */
+int dq_ref_quantize_act(const void* X, int xt, int64_t tokens, int64_t cols, int fmt, int group,
+                        const float* b, float* g_inout, uint8_t* codes, void* scales);
+
 /* T iterations of the block-coordinate descent. a0/b0: NULL means ones, else
  * projected onto the format's scale set first; g0 > 0 fixes the NVFP4 tensor
  * scale, g0 <= 0 computes it from the initial scaled tile. Outputs: final codes
