@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.dq_solve.restype = I
         L.dq_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, SZ, P]
         L.dq_quantize.restype = I
+        L.dq_act_workspace_bytes.argtypes = [I64, I64, I, I]
+        L.dq_act_workspace_bytes.restype = SZ
+        L.dq_quantize_act.argtypes = [P, I, I64, I64, I, I, P, ctypes.c_float, P, P, P, P, SZ, P]
+        L.dq_quantize_act.restype = I
         L.dq_status_str.argtypes = [I]
         L.dq_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -182,4 +186,30 @@ def quantize(W, fmt: str, group: int, a=None, b=None, g: float = 0.0, workspace=
                            ws_ptr, ws_bytes, _stream(stream))
     if st != 0:
         raise DQError(st, "dq_quantize")
+    return {"codes": codes, "scales": scales, "g": gbuf}
+
+
+def act_workspace_bytes(tokens: int, cols: int, fmt: str, group: int) -> int:
+    return int(lib().dq_act_workspace_bytes(int(tokens), int(cols), FMT[fmt], int(group)))
+
+
+def quantize_act(X, fmt: str, group: int, b=None, g: float = 0.0, workspace=None,
+                 stream=None) -> Dict[str, object]:
+    """dq_quantize_act: Q of x = fl32(X * b) per token row (X: tokens x cols, CUDA float32 /
+    bfloat16), groups of ``group`` channels. ``g`` > 0 fixes NVFP4's tensor scale, else it is
+    computed from X. Returns device tensors codes, scales and g (float32[1])."""
+    torch = _torch()
+    dt = _check_w(X)
+    tokens, cols = X.shape
+    dev = X.device
+    codes, scales = _outputs(X, fmt, group)
+    gbuf = torch.zeros(1, dtype=torch.float32, device=dev)
+    b = _vec(b, cols, dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = lib().dq_quantize_act(X.data_ptr(), DTYPE[dt], tokens, cols, FMT[fmt], group, _ptr(b),
+                               float(g), gbuf.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                               ws_ptr, ws_bytes, _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_quantize_act")
     return {"codes": codes, "scales": scales, "g": gbuf}

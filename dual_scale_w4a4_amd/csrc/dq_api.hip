@@ -487,6 +487,30 @@ dq_status time_isolated(const Plan& p, char* ws, const void* W, float* a, const 
   return DQ_OK;
 }
 
+// Launch shape and workspace of the activation quantizer: 1024-channel tiles, chunks of
+// tokens in multiples of 16 (four waves of four rows), about 1024 workgroups.
+struct ActPlan {
+  int nct = 0, nrc = 0;
+  int64_t rpc = 0;
+  size_t off_status = 0, off_part = 0, off_gs = 0, total = 0;
+};
+
+ActPlan act_plan(int64_t m, int64_t n) {
+  ActPlan p;
+  p.nct = (int)((n + dq::act_tile_cols() - 1) / dq::act_tile_cols());
+  int64_t want = (1024 + p.nct - 1) / p.nct;
+  if (want < 1) want = 1;
+  p.rpc = (m + want - 1) / want;
+  p.rpc = (p.rpc + 15) / 16 * 16;
+  p.nrc = (int)((m + p.rpc - 1) / p.rpc);
+  size_t o = 0;
+  p.off_status = o; o = align_up(o + 64);
+  p.off_part = o; o = align_up(o + sizeof(float) * (size_t)dq::act_amax_blocks());
+  p.off_gs = o; o = align_up(o + 16);
+  p.total = o;
+  return p;
+}
+
 dq_status read_flags(char* ws, const Plan& p, hipStream_t s, int* flags) {
   int host[2] = {0, 0};
   DQ_TRY(hipMemcpyAsync(host, ws + p.off_status, sizeof host, hipMemcpyDeviceToHost, s));
@@ -636,6 +660,70 @@ dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq
   int flags = 0;
   st = read_flags(base, p, stream, &flags);
   if (st != DQ_OK) return st;
+  return map_status(flags);
+}
+
+size_t dq_act_workspace_bytes(int64_t tokens, int64_t cols, dq_format fmt, int group) {
+  if (!fmt_ok(fmt) || !shape_ok(tokens, cols, group)) return 0;
+  return act_plan(tokens, cols).total;
+}
+
+dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t cols,
+                          dq_format fmt, int group, const float* b, float g, float* tensor_scale,
+                          uint8_t* codes, void* inner_scales, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  using namespace dq;
+  dq_status st = check_common(X, xt, tokens, cols, fmt, group, codes, inner_scales);
+  if (st != DQ_OK) return st;
+  if (((uintptr_t)codes & 7u) != 0 || ((uintptr_t)b & 15u) != 0) return DQ_ERR_ARG;
+  if (g != g || g > 3.4028234663852886e38f) return DQ_ERR_ARG;
+  const ActPlan p = act_plan(tokens, cols);
+  WsGuard ws;
+  {
+    void* w = workspace;
+    size_t wb = workspace_bytes;
+    if (w) {
+      if (wb < p.total) return DQ_ERR_WORKSPACE;
+      if (((uintptr_t)w & 255u) != 0) return DQ_ERR_ARG;
+      ws.ptr = static_cast<char*>(w);
+      ws.s = stream;
+    } else {
+      void* ptr = nullptr;
+      DQ_TRY(hipMallocAsync(&ptr, p.total, stream));
+      ws.ptr = static_cast<char*>(ptr);
+      ws.owned = true;
+      ws.s = stream;
+    }
+  }
+  int* status = at<int>(ws.ptr, p.off_status);
+  ActArgs aa{};
+  aa.X = X;
+  aa.m = tokens;
+  aa.n = cols;
+  aa.G = group;
+  aa.b = b;
+  aa.g = g;
+  aa.gs = nullptr;
+  aa.gs_out = at<float>(ws.ptr, p.off_gs);
+  aa.g_out = fmt == DQ_FMT_NVFP4 ? tensor_scale : nullptr;
+  aa.part = at<float>(ws.ptr, p.off_part);
+  aa.nct = p.nct;
+  aa.nrc = p.nrc;
+  aa.rpc = p.rpc;
+  aa.codes = codes;
+  aa.scales = inner_scales;
+  aa.status = status;
+  DQ_TRY(launch_clear(status, 16, stream));
+  if (fmt == DQ_FMT_NVFP4 && !(g > 0.0f)) {
+    DQ_TRY(launch_act_gscale(xt == DQ_BF16, aa, stream));
+    aa.gs = aa.gs_out;
+  }
+  DQ_TRY(launch_act(fmt, xt == DQ_BF16, aa, stream));
+  int flags = 0;
+  int host[2] = {0, 0};
+  DQ_TRY(hipMemcpyAsync(host, status, sizeof host, hipMemcpyDeviceToHost, stream));
+  DQ_TRY(hipStreamSynchronize(stream));
+  flags = host[0];
   return map_status(flags);
 }
 

@@ -284,8 +284,14 @@ DQ_HD double e2m1_grid64(double v) {
   return r < 6.0 ? r : 6.0;
 }
 
-// the signed code of x given r ~ 1 / d (see above); for INT4 the clamp to [-8, 7] never
-// acts, because |x| <= mx and s >= (mx / 7)(1 - 2^-8) keep |x / s| below 7.03
+// INT4 codes need their clamp to [-8, 7] only where s is a subnormal bf16 value (s < 2^-126):
+// a normal s lies within 2^-9 (relative) of mx / 7, so |x / s| <= 7.03, but the subnormal
+// grid is coarser (spacing 2^-133) and |x / s| can reach about 8.4 there
+DQ_HD double int4_clamp(double q) { return q < -8.0 ? -8.0 : (q > 7.0 ? 7.0 : q); }
+DQ_HD bool int4_needs_clamp(float d) { return d < 0x1p-126f; }
+
+// the signed code of x given r ~ 1 / d (see above), before INT4's clamp (int4_clamp, needed
+// only where int4_needs_clamp(d))
 template <int FMT>
 DQ_HD double code64(float x, double r, const GroupQ& gq) {
   if (FMT == kInt4Bf16) return rint(snap_quotient((double)x, r));

@@ -121,6 +121,24 @@ struct FinArgs {
   int* status;
 };
 
+// Activation quantization x = fl32(X * b), then Q (dq_act.hip).
+struct ActArgs {
+  const void* X;
+  int64_t m, n;      // tokens, channels
+  int G;
+  const float* b;    // channels, or null for ones
+  float g;           // NVFP4: the tensor scale when gs is null
+  const float* gs;   // NVFP4: device tensor scale (from the amax pass), or null
+  float* gs_out;     // the amax pass's result
+  float* g_out;      // NVFP4: the tensor scale used, for the caller (may be null)
+  float* part;       // amax pass: per-block maxima
+  int nct, nrc;      // tiles of act_tile_cols() channels, chunks of rpc tokens
+  int64_t rpc;
+  uint8_t* codes;
+  void* scales;
+  int* status;
+};
+
 hipError_t launch_clear(int* words, int count, hipStream_t s);
 // reads `vec16` 16-byte words of buf in full (to evict other data from the caches); `sink`
 // is written only if the data has an impossible checksum, so that the reads stay
@@ -133,6 +151,10 @@ hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStr
 // SweepArgs::nct counts tiles of pass_tile_cols() columns
 hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s);
 int pass_tile_cols();
+hipError_t launch_act(int fmt, bool bf16, const ActArgs& a, hipStream_t s);
+hipError_t launch_act_gscale(bool bf16, const ActArgs& a, hipStream_t s);  // amax pass + g
+int act_tile_cols();
+int act_amax_blocks();
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,

@@ -69,8 +69,13 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
   const GroupQ gq = group_scale<FMT>(gm, g, sixg);
   const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
   double q[E];  // the codes as values
+  if (FMT == kInt4Bf16 && __any(int4_needs_clamp(gq.d))) {  // rare: a subnormal scale
 #pragma unroll
-  for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);
+    for (int k = 0; k < E; k++) q[k] = int4_clamp(code64<FMT>(x[k], r, gq));
+  } else {
+#pragma unroll
+    for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);
+  }
 
   if (ROW) {
     double nl = 0.0, dl = 0.0;

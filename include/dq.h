@@ -147,6 +147,32 @@ dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq
                       uint8_t* codes, void* inner_scales, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace dq_quantize_act needs (0 on invalid arguments); scratch only. */
+size_t dq_act_workspace_bytes(int64_t tokens, int64_t cols, dq_format fmt, int group);
+
+/* Activation quantization with the column inverse scales: the consumer side of the
+ * factorized product (daiwk notes, "核心公式" eq. 1: X W^T ~= (X D_beta^-1) Qhat^T D_alpha^-1,
+ * with D_beta^-1 = D_b; the flowchart scales the real activations by the column inverse
+ * scales, then quantizes them; trove summary, "How to use it": beta is applied inside the
+ * activation quantizer). Every row (token) of X is scaled channel by channel,
+ * x_tj = fl32(X_tj * b_j), and quantized by the weights' group quantizer Q in groups of
+ * `group` consecutive channels; the scaled values never go to memory.
+ *  X:            tokens x cols, fp32 or bf16 (xt), device, 16-byte aligned, row-major.
+ *  b:            device, cols floats > 0 (the solver's column inverse scales, used as given),
+ *                16-byte aligned, or NULL for ones.
+ *  g:            NVFP4 only: > 0 fixes the tensor scale; <= 0 computes it from this X as
+ *                fl32(max|x| / 2688), at least 2^-126 (1 if x == 0), with one extra read of X.
+ *  tensor_scale: out (device, 1 float): NVFP4's g as used; ignored (may be NULL) otherwise.
+ *  codes:        out, tokens*cols/2 bytes, 8-byte aligned, packed as for dq_solve.
+ *  inner_scales: out, tokens*(cols/group) entries (u16 bf16 bits, or u8), as for dq_solve.
+ *  workspace:    device scratch of at least dq_act_workspace_bytes(...) bytes, or NULL.
+ * Returns DQ_ERR_NONFINITE for a NaN / Inf in X, DQ_ERR_RANGE when X * b overflows; like the
+ * other calls it synchronizes `stream` before returning. */
+dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t cols,
+                          dq_format fmt, int group, const float* b, float g, float* tensor_scale,
+                          uint8_t* codes, void* inner_scales, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Static string for a status code. */
 const char* dq_status_str(dq_status status);
 

@@ -163,3 +163,30 @@ extern "C" int64_t h_code64_mismatches(int fmt, const float* d, int64_t nd) {
   }
   return bad;
 }
+
+// Q of one group through the double-quotient codes (code64), as the two-sweep pass and the
+// activation quantizer form them: values q (one per element) and the scale code.
+extern "C" void h_group_code64(int fmt, const float* x, int G, float g, double* q, uint32_t* scode) {
+  float mx = 0.0f;
+  for (int k = 0; k < G; k++) mx = fmaxf(mx, fabsf(x[k]));
+  const float sixg = 6.0f * g;
+  switch (fmt) {
+    case 0: {
+      const dq::GroupQ gq = dq::group_scale<0>(mx, g, sixg);
+      const double r = dq::recip64(gq.d);
+      for (int k = 0; k < G; k++) {
+        q[k] = dq::code64<0>(x[k], r, gq);
+        if (dq::int4_needs_clamp(gq.d)) q[k] = dq::int4_clamp(q[k]);
+      }
+      *scode = gq.scode;
+      break;
+    }
+    default: {
+      const dq::GroupQ gq = dq::group_scale<3>(mx, g, sixg);
+      const double r = dq::recip64(gq.d);
+      for (int k = 0; k < G; k++) q[k] = dq::code64<3>(x[k], r, gq);
+      *scode = gq.scode;
+      break;
+    }
+  }
+}

@@ -161,3 +161,26 @@ def test_double_quotient_codes_at_boundaries(H):
     d = (s[None, :].astype(np.float32) * g[:, None].astype(np.float32)).reshape(-1)
     d = d[(d > 0) & np.isfinite(d)].astype(np.float32)
     assert H.h_code64_mismatches(3, _p(d), ctypes.c_int64(d.size)) == 0
+
+
+@pytest.mark.parametrize("fmt,fid", [("int4_bf16", 0), ("nvfp4", 3)])
+@pytest.mark.parametrize("group", [16, 32, 64])
+def test_double_quotient_group_quantizer_matches_oracle(H, oracle_lib, fmt, fid, group):
+    # the codes as the two-sweep pass and the activation quantizer form them (code64, with
+    # INT4's clamp where the scale is a subnormal bf16 value), on rows with planted ties,
+    # zero groups, subnormal groups (subnormal INT4 scales) and outliers
+    W = adversarial_w(fmt, group, 60, seed=group + 7)
+    W[7, :group] = (np.linspace(-1, 1, group) * 2.2e-39).astype(np.float32)  # subnormal scale
+    ref = oracle_lib.quantize(W, "f32", fmt, group, None, None)
+    qr = fb.unpack_codes(ref["codes"], fmt)
+    H.h_group_code64.restype = None
+    rows, cols = W.shape
+    for i in range(rows):
+        for k in range(cols // group):
+            x = np.ascontiguousarray(W[i, k * group:(k + 1) * group])
+            q = np.zeros(group)
+            sc = np.zeros(1, np.uint32)
+            H.h_group_code64(ctypes.c_int(fid), _p(x), ctypes.c_int(group),
+                             ctypes.c_float(ref["g"] if fmt == "nvfp4" else 1.0), _p(q), _p(sc))
+            assert sc[0] == int(ref["scales"][i, k]), (i, k)
+            assert np.array_equal(q, qr[i, k * group:(k + 1) * group]), (i, k, q, qr[i, k * group:(k + 1) * group])

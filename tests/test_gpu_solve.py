@@ -176,3 +176,16 @@ def test_error_statuses(dq):
     x = dq.solve(to_device(W, "f32"), "mxfp4", 32, 3, workspace=ws)
     y = dq.solve(to_device(W, "f32"), "mxfp4", 32, 3)
     assert np.array_equal(host(x["codes"]), host(y["codes"]))
+
+
+@pytest.mark.parametrize("fmt", ["int4_bf16", "nvfp4"])
+def test_subnormal_groups_on_the_two_sweep_pass(dq, oracle_lib, fmt):
+    # bf16 weights with groups of subnormal values: their INT4 scale is a subnormal bf16
+    # value, where the codes need the clamp to [-8, 7]
+    group = 16 if fmt == "nvfp4" else 32
+    W32 = rand_w(48, 1088, seed=17)
+    W32[5, :32] = (np.linspace(-1, 1, 32) * 2.2e-39).astype(np.float32)
+    W32[11, 64:96] = (np.linspace(-1, 1, 32) * 5e-40).astype(np.float32)
+    Wb = workloads.fp32_to_bf16_bits(W32)
+    w = workloads.Workload("subnormal", Wb, "bf16", fmt, group, 4)
+    _run_pair(dq, oracle_lib, w)

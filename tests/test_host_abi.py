@@ -30,7 +30,8 @@ def dqlib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["dq_quantize", "dq_solve", "dq_status_str", "dq_workspace_bytes"]
+    assert names == ["dq_act_workspace_bytes", "dq_quantize", "dq_quantize_act", "dq_solve",
+                     "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(dqlib):
@@ -87,3 +88,27 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert st == 5
     st = L.dq_quantize(fake, 1, 128, 256, 3, 32, None, None, None, fake, fake, None, 0, None)
     assert st == 1  # NVFP4 needs the tensor-scale pointer
+
+
+def test_act_arguments_are_rejected_on_the_host(dqlib):
+    L = dqlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
+    args = dict(X=fake, xt=1, tokens=64, cols=256, fmt=2, group=32, b=None, g=0.0, codes=fake)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dq_quantize_act(a["X"], a["xt"], a["tokens"], a["cols"], a["fmt"], a["group"],
+                                 a["b"], a["g"], fake, a["codes"], fake, None, 0, None)
+
+    assert call(X=None) == 1
+    assert call(tokens=0) == 1
+    assert call(cols=250) == 1
+    assert call(group=8) == 1
+    assert call(fmt=9) == 2
+    assert call(xt=5) == 2
+    assert call(X=ctypes.c_void_p(0x1008)) == 1      # X not 16-byte aligned
+    assert call(codes=ctypes.c_void_p(0x1004)) == 1  # codes not 8-byte aligned
+    assert call(b=ctypes.c_void_p(0x1004)) == 1      # b not 16-byte aligned
+    assert call(g=float("nan")) == 1
+    assert dqlib.act_workspace_bytes(64, 256, "nvfp4", 16) > 0
+    assert dqlib.act_workspace_bytes(64, 250, "nvfp4", 16) == 0

@@ -210,3 +210,33 @@ def full(cfg: int) -> List[Workload]:
     if cfg == 4:
         return [config4()]
     raise ValueError("config 5 is a stream of 224 matrices: use config5()")
+
+
+# ------------------------------------------------------------------- activations (next row)
+ACT_CFG = 6  # seed-stream id of the activation inputs
+
+
+def activations(tokens: int, cols: int, seed: int = 0, dtype: str = "bf16") -> np.ndarray:
+    """Activation-like rows for the activation quantizer: N(0, 1) per entry times a
+    per-channel lognormal(0, 0.5) level, and 1% of the channels a further x U(10, 50) (the
+    outlier channels that the DualQuant pages tie to large-norm weight columns)."""
+    rng = rng_for(ACT_CFG, 0, seed)
+    level = np.exp(rng.normal(0.0, 0.5, size=cols))
+    level *= outlier_multipliers(rng, cols, max(1, cols // 100), 10.0, 50.0)
+    return _gaussian_matrix(rng, tokens, cols, 1.0, level, dtype)
+
+
+def act_column_scales(cols: int, seed: int = 0) -> np.ndarray:
+    """Column inverse scales for the activation inputs: powers of two 2^k, k uniform in
+    [-3, 3], which are exact values of every outer scale set (BF16, E8M0 and E4M3)."""
+    rng = rng_for(ACT_CFG, 1, seed)
+    return np.ldexp(np.ones(cols, np.float32), rng.integers(-3, 4, size=cols)).astype(np.float32)
+
+
+def act_inputs(name: str) -> Tuple[np.ndarray, np.ndarray]:
+    """The activation quantizer's measured inputs: the Llama-3.1-8B MLP inputs of a batch of
+    8192 tokens, 'up' (8192 x 4096, the input of the up / gate projections) or 'down'
+    (8192 x 14336), bf16, with their column inverse scales."""
+    cols = {"up": 4096, "down": 14336}[name]
+    seed = {"up": 1, "down": 2}[name]
+    return activations(8192, cols, seed), act_column_scales(cols, seed)
