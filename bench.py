@@ -58,11 +58,23 @@ def _load(workload: int):
     raise SystemExit(f"unknown workload {workload}")
 
 
-def sources_sha256() -> str:
+ACT_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_act.hip", "dual_scale_w4a4_amd/csrc/dq_device.h",
+               "dual_scale_w4a4_amd/csrc/dq_internal.h")
+# HBM bytes of one activation-quantizer step (both 8192-token inputs, MXFP4 G32) from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the two dispatches of
+# a step), scaled as above; valid only for the sources they were taken on.
+ACT_COUNTERS = {
+    "fetch_kib": 32903.9 + 114924.9, "fetch_scale": 2.0,
+    "write_kib": 17408.0 + 60928.0, "write_scale": 1.0,
+    "sources_sha256": "b4b152bba5ca431c7099231792fb5626403c6487c087cfe4d070213693d7199a",
+}
+
+
+def sources_sha256(files=KERNEL_SOURCES) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -100,6 +112,9 @@ def main() -> None:
     ap.add_argument("--sequential", action="store_true",
                     help="solve the matrices of a step one after another on one stream "
                          "(default: each on its own stream, concurrently)")
+    ap.add_argument("--act", action="store_true",
+                    help="measure the activation quantizer instead (x = X b, then Q) on the "
+                         "Llama-3.1-8B MLP inputs of 8192 tokens; prints its own JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 512 MiB device-to-device copies (the reference that "
                          "scales HBM byte counters)")
@@ -124,6 +139,10 @@ def main() -> None:
         return
 
     import dual_scale_w4a4_amd as dq
+
+    if args.act:
+        bench_act(args, dq)
+        return
 
     mats, desc = _load(args.workload)
     dev_w = [to_device(w.W, w.dtype) for w in mats]
@@ -255,6 +274,89 @@ def main() -> None:
     print(json.dumps(line), flush=True)
 
 
+def act_traffic():
+    c = ACT_COUNTERS
+    if sources_sha256(ACT_SOURCES) != c["sources_sha256"]:
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+
+
+def bench_act(args, dq) -> None:
+    """The activation quantizer on the Llama-3.1-8B MLP inputs of a batch of 8192 tokens
+    (8192 x 4096 into up / gate, 8192 x 14336 into down), bf16, MXFP4 G32 and NVFP4 G16 (g
+    given), each a step of both inputs. Kernel time: back-to-back asynchronous calls between
+    one pair of HIP events on the calling stream. Algorithmic bytes per element: read X (2 B),
+    write the code (0.5 B) and 1/G of an inner-scale byte."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    stream = torch.cuda.current_stream()
+    inputs = []
+    for name in ("up", "down"):
+        X, b = workloads.act_inputs(name)
+        inputs.append((name, to_device(X, "bf16"), to_device(b, "f32")))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    results = {}
+    for fmt, group, g in (("mxfp4", 32, 0.0), ("nvfp4", 16, 0.01)):
+        outs = []
+        for name, Xd, bd in inputs:
+            o = dq.quantize_act(Xd, fmt, group, bd, g=g)
+            outs.append((name, Xd, bd, o["codes"], o["scales"]))
+        def step():
+            for name, Xd, bd, codes, scales in outs:
+                dq.quantize_act_async(Xd, fmt, group, codes, scales, status, b=bd, g=g,
+                                      stream=stream)
+        for _ in range(args.warmup):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        elems = sum(Xd.numel() for _, Xd, _, _, _ in outs)
+        algo = elems * (2.0 + 0.5 + 1.0 / group)
+        results[fmt] = {"group": group, "ms_per_step": ms, "elems_per_s": elems / (ms * 1e-3),
+                        "achieved_GBps": algo / (ms * 1e-3) / 1e9,
+                        "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "bytes_per_step": algo}
+    assert int(status.item()) == 0
+    m = results["mxfp4"]
+    # the CPU oracle on a bounded sample: the whole 8192-token up input
+    import oracle
+
+    Xs, bs = workloads.act_inputs("up")
+    Xs = np.ascontiguousarray(Xs)
+    t0 = time.perf_counter()
+    ref = oracle.quantize_act(Xs, "bf16", "mxfp4", 32, bs)
+    dt = time.perf_counter() - t0
+    got = dq.quantize_act(to_device(Xs, "bf16"), "mxfp4", 32, to_device(bs, "f32"))
+    same = bool(np.array_equal(got["codes"].cpu().numpy(), ref["codes"]) and
+                np.array_equal(got["scales"].cpu().numpy(), ref["scales"]))
+    line = {
+        "metric": "activation quantization (x = X b, then Q) elements/s, % HBM peak",
+        "value": m["elems_per_s"], "unit": "activation elements / s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded generators in workloads/)",
+        "config": {"workload": "llama3.1-8b MLP inputs of 8192 tokens: 8192x4096 + 8192x14336, "
+                               "bf16, MXFP4 G32 (NVFP4 G16 with a given g alongside)"},
+        "roofline": {"bound": "hbm", "kernel": "k_act", "achieved": m["achieved_GBps"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["frac"],
+                     "traffic": act_traffic(), "traffic_unit": "bytes per step",
+                     "timing": "back-to-back asynchronous calls between one pair of events"},
+        "formats": results,
+        "cpu_baseline": {"value": Xs.size / dt, "unit": "activation elements / s", "cores": 1,
+                         "kind": "oracle", "sample": "the whole 8192x4096 input, MXFP4 G32",
+                         "seconds": dt, "gpu_identical_on_sample": same},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(w, dq, to_device):
     """The oracle on a bounded row sample of the first matrix (same T), all host cores up to
     16, and the GPU on the same sample checked against it."""
@@ -262,7 +364,7 @@ def cpu_baseline(w, dq, to_device):
 
     import oracle
 
-    rows = min(w.rows, max(64, (2048 * 4096) // w.cols))
+    rows = min(w.rows, max(64, (8192 * 4096) // w.cols))
     sample = np.ascontiguousarray(w.W[:rows])
     threads = oracle.set_threads(min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()

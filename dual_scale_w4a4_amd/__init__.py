@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.dq_act_workspace_bytes.restype = SZ
         L.dq_quantize_act.argtypes = [P, I, I64, I64, I, I, P, ctypes.c_float, P, P, P, P, SZ, P]
         L.dq_quantize_act.restype = I
+        L.dq_quantize_act_async.argtypes = [P, I, I64, I64, I, I, P, ctypes.c_float, P, P, P, P,
+                                            P, SZ, P]
+        L.dq_quantize_act_async.restype = I
         L.dq_status_str.argtypes = [I]
         L.dq_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -213,3 +216,19 @@ def quantize_act(X, fmt: str, group: int, b=None, g: float = 0.0, workspace=None
     if st != 0:
         raise DQError(st, "dq_quantize_act")
     return {"codes": codes, "scales": scales, "g": gbuf}
+
+
+def quantize_act_async(X, fmt: str, group: int, codes, scales, status, b=None, g: float = 0.0,
+                       gout=None, workspace=None, stream=None) -> None:
+    """dq_quantize_act_async into caller-allocated outputs (codes, scales as quantize_act
+    returns them, ``status`` an int32 device tensor that collects error bits); no wait."""
+    dt = _check_w(X)
+    tokens, cols = X.shape
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = lib().dq_quantize_act_async(X.data_ptr(), DTYPE[dt], tokens, cols, FMT[fmt], group,
+                                     _ptr(b), float(g), _ptr(gout), codes.data_ptr(),
+                                     scales.data_ptr(), status.data_ptr(), ws_ptr, ws_bytes,
+                                     _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_quantize_act_async")

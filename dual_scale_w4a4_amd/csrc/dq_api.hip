@@ -668,6 +668,59 @@ size_t dq_act_workspace_bytes(int64_t tokens, int64_t cols, dq_format fmt, int g
   return act_plan(tokens, cols).total;
 }
 
+dq_status dq_quantize_act_async(const void* X, dq_dtype xt, int64_t tokens, int64_t cols,
+                                dq_format fmt, int group, const float* b, float g,
+                                float* tensor_scale, uint8_t* codes, void* inner_scales,
+                                int* status, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  using namespace dq;
+  dq_status st = check_common(X, xt, tokens, cols, fmt, group, codes, inner_scales);
+  if (st != DQ_OK) return st;
+  if (!status || ((uintptr_t)status & 3u) != 0) return DQ_ERR_ARG;
+  if (((uintptr_t)codes & 7u) != 0 || ((uintptr_t)b & 15u) != 0) return DQ_ERR_ARG;
+  if (g != g || g > 3.4028234663852886e38f) return DQ_ERR_ARG;
+  const ActPlan p = act_plan(tokens, cols);
+  const bool amax = fmt == DQ_FMT_NVFP4 && !(g > 0.0f);
+  WsGuard ws;
+  if (amax) {  // only the amax pass uses the workspace
+    if (workspace) {
+      if (workspace_bytes < p.total) return DQ_ERR_WORKSPACE;
+      if (((uintptr_t)workspace & 255u) != 0) return DQ_ERR_ARG;
+      ws.ptr = static_cast<char*>(workspace);
+      ws.s = stream;
+    } else {
+      void* ptr = nullptr;
+      DQ_TRY(hipMallocAsync(&ptr, p.total, stream));
+      ws.ptr = static_cast<char*>(ptr);
+      ws.owned = true;
+      ws.s = stream;
+    }
+  }
+  ActArgs aa{};
+  aa.X = X;
+  aa.m = tokens;
+  aa.n = cols;
+  aa.G = group;
+  aa.b = b;
+  aa.g = g;
+  aa.gs = nullptr;
+  aa.gs_out = amax ? at<float>(ws.ptr, p.off_gs) : nullptr;
+  aa.g_out = fmt == DQ_FMT_NVFP4 ? tensor_scale : nullptr;
+  aa.part = amax ? at<float>(ws.ptr, p.off_part) : nullptr;
+  aa.nct = p.nct;
+  aa.nrc = p.nrc;
+  aa.rpc = p.rpc;
+  aa.codes = codes;
+  aa.scales = inner_scales;
+  aa.status = status;
+  if (amax) {
+    DQ_TRY(launch_act_gscale(xt == DQ_BF16, aa, stream));
+    aa.gs = aa.gs_out;
+  }
+  DQ_TRY(launch_act(fmt, xt == DQ_BF16, aa, stream));
+  return DQ_OK;
+}
+
 dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t cols,
                           dq_format fmt, int group, const float* b, float g, float* tensor_scale,
                           uint8_t* codes, void* inner_scales, void* workspace,
@@ -679,52 +732,27 @@ dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t co
   if (g != g || g > 3.4028234663852886e38f) return DQ_ERR_ARG;
   const ActPlan p = act_plan(tokens, cols);
   WsGuard ws;
-  {
-    void* w = workspace;
-    size_t wb = workspace_bytes;
-    if (w) {
-      if (wb < p.total) return DQ_ERR_WORKSPACE;
-      if (((uintptr_t)w & 255u) != 0) return DQ_ERR_ARG;
-      ws.ptr = static_cast<char*>(w);
-      ws.s = stream;
-    } else {
-      void* ptr = nullptr;
-      DQ_TRY(hipMallocAsync(&ptr, p.total, stream));
-      ws.ptr = static_cast<char*>(ptr);
-      ws.owned = true;
-      ws.s = stream;
-    }
+  if (workspace) {
+    if (workspace_bytes < p.total) return DQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return DQ_ERR_ARG;
+    ws.ptr = static_cast<char*>(workspace);
+    ws.s = stream;
+  } else {
+    void* ptr = nullptr;
+    DQ_TRY(hipMallocAsync(&ptr, p.total, stream));
+    ws.ptr = static_cast<char*>(ptr);
+    ws.owned = true;
+    ws.s = stream;
   }
   int* status = at<int>(ws.ptr, p.off_status);
-  ActArgs aa{};
-  aa.X = X;
-  aa.m = tokens;
-  aa.n = cols;
-  aa.G = group;
-  aa.b = b;
-  aa.g = g;
-  aa.gs = nullptr;
-  aa.gs_out = at<float>(ws.ptr, p.off_gs);
-  aa.g_out = fmt == DQ_FMT_NVFP4 ? tensor_scale : nullptr;
-  aa.part = at<float>(ws.ptr, p.off_part);
-  aa.nct = p.nct;
-  aa.nrc = p.nrc;
-  aa.rpc = p.rpc;
-  aa.codes = codes;
-  aa.scales = inner_scales;
-  aa.status = status;
   DQ_TRY(launch_clear(status, 16, stream));
-  if (fmt == DQ_FMT_NVFP4 && !(g > 0.0f)) {
-    DQ_TRY(launch_act_gscale(xt == DQ_BF16, aa, stream));
-    aa.gs = aa.gs_out;
-  }
-  DQ_TRY(launch_act(fmt, xt == DQ_BF16, aa, stream));
-  int flags = 0;
+  st = dq_quantize_act_async(X, xt, tokens, cols, fmt, group, b, g, tensor_scale, codes,
+                             inner_scales, status, ws.ptr, p.total, stream);
+  if (st != DQ_OK) return st;
   int host[2] = {0, 0};
   DQ_TRY(hipMemcpyAsync(host, status, sizeof host, hipMemcpyDeviceToHost, stream));
   DQ_TRY(hipStreamSynchronize(stream));
-  flags = host[0];
-  return map_status(flags);
+  return map_status(host[0]);
 }
 
 }  // extern "C"

@@ -173,6 +173,19 @@ dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t co
                           uint8_t* codes, void* inner_scales, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* dq_quantize_act without the wait, for callers that cannot synchronize per call (a serving
+ * loop): the same arguments and results, only enqueued on `stream`. Errors found on the
+ * device are OR-ed into *status (device, caller-owned, 4-byte aligned): bit 1 a NaN / Inf
+ * in X, bit 2 an overflow of X * b. The caller clears it (0) before the calls it wants to
+ * check and reads it afterwards; it accumulates across calls. Only NVFP4 with g <= 0 uses the
+ * workspace (which may then be NULL: allocated and freed stream-ordered). Host-side argument
+ * checks return errors as dq_quantize_act does, before anything is enqueued. */
+dq_status dq_quantize_act_async(const void* X, dq_dtype xt, int64_t tokens, int64_t cols,
+                                dq_format fmt, int group, const float* b, float g,
+                                float* tensor_scale, uint8_t* codes, void* inner_scales,
+                                int* status, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* Static string for a status code. */
 const char* dq_status_str(dq_status status);
 

@@ -117,3 +117,32 @@ def test_act_error_statuses(dq):
     x = dq.quantize_act(to_device(X, "f32"), "mxfp4", 32, workspace=ws)
     y = dq.quantize_act(to_device(X, "f32"), "mxfp4", 32)
     assert np.array_equal(host(x["codes"]), host(y["codes"]))
+
+
+def test_act_async_matches_blocking_and_collects_status(dq):
+    import torch
+
+    X, b = workloads.act_inputs("up")
+    X = X[:300]
+    Xd = to_device(X, "bf16")
+    bd = _bvec(b)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for fmt, group in (("mxfp4", 32), ("nvfp4", 16), ("int4_bf16", 64)):
+        want = dq.quantize_act(Xd, fmt, group, bd)
+        codes = torch.empty_like(want["codes"])
+        scales = torch.empty_like(want["scales"])
+        gout = torch.zeros(1, dtype=torch.float32, device="cuda")
+        dq.quantize_act_async(Xd, fmt, group, codes, scales, status, b=bd, gout=gout)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(codes), host(want["codes"])), fmt
+        assert np.array_equal(host(scales), host(want["scales"])), fmt
+        if fmt == "nvfp4":
+            assert host(gout)[0] == host(want["g"])[0]
+    assert int(host(status)[0]) == 0
+    bad = X[:32].copy()
+    bad[3, 5] = 0x7FC0  # a bf16 NaN
+    Bd = to_device(bad, "bf16")
+    out = dq.quantize_act(to_device(X[:32], "bf16"), "mxfp4", 32, bd)
+    dq.quantize_act_async(Bd, "mxfp4", 32, out["codes"], out["scales"], status, b=bd)
+    torch.cuda.synchronize()
+    assert int(host(status)[0]) & 1

@@ -30,8 +30,8 @@ def dqlib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["dq_act_workspace_bytes", "dq_quantize", "dq_quantize_act", "dq_solve",
-                     "dq_status_str", "dq_workspace_bytes"]
+    assert names == ["dq_act_workspace_bytes", "dq_quantize", "dq_quantize_act",
+                     "dq_quantize_act_async", "dq_solve", "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(dqlib):
@@ -112,3 +112,16 @@ def test_act_arguments_are_rejected_on_the_host(dqlib):
     assert call(g=float("nan")) == 1
     assert dqlib.act_workspace_bytes(64, 256, "nvfp4", 16) > 0
     assert dqlib.act_workspace_bytes(64, 250, "nvfp4", 16) == 0
+
+    # the asynchronous variant checks the same, and its status pointer
+    def call_async(status=fake, **kw):
+        a = dict(args, **kw)
+        return L.dq_quantize_act_async(a["X"], a["xt"], a["tokens"], a["cols"], a["fmt"],
+                                       a["group"], a["b"], a["g"], fake, a["codes"], fake, status,
+                                       None, 0, None)
+
+    assert call_async(X=None) == 1
+    assert call_async(cols=250) == 1
+    assert call_async(status=None) == 1
+    assert call_async(status=ctypes.c_void_p(0x1002)) == 1
+    assert call_async(codes=ctypes.c_void_p(0x1004)) == 1
