@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.dq_ref_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P]
         L.dq_ref_quantize.restype = I
         L.dq_ref_quantize_act.argtypes = [P, I, I64, I64, I, I, P, P, P, P]
+        L.dq_ref_solve_pass_g.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, P, P]
+        L.dq_ref_solve_pass_g.restype = I
         L.dq_ref_quantize_act.restype = I
         L.dq_ref_solve.argtypes = [P, I, I64, I64, I, I, I, P, P, F, P, P, P, P, P, P]
         L.dq_ref_solve.restype = I
@@ -131,6 +133,27 @@ def quantize_act(X: np.ndarray, dtype: str, fmt: str, group: int, b=None,
     if st:
         raise OracleError(st)
     return {"codes": codes, "scales": scales, "g": float(gbuf[0])}
+
+
+def solve_pass_g(W: np.ndarray, dtype: str, group: int, T: int, a0=None,
+                 b0=None) -> Dict[str, np.ndarray]:
+    """NVFP4 solve with the tensor scale recomputed before every Q pass."""
+    W = _prep_w(W, dtype)
+    rows, cols = W.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // group), np.uint8)
+    a = np.zeros(rows, np.float32)
+    b = np.zeros(cols, np.float32)
+    mse = np.zeros(T + 1, np.float64)
+    g = np.zeros(1, np.float32)
+    a0 = None if a0 is None else np.ascontiguousarray(a0, np.float32)
+    b0 = None if b0 is None else np.ascontiguousarray(b0, np.float32)
+    st = lib().dq_ref_solve_pass_g(_ptr(W), DTYPE[dtype], rows, cols, group, T, _ptr(a0),
+                                   _ptr(b0), _ptr(codes), _ptr(scales), _ptr(g), _ptr(a), _ptr(b),
+                                   _ptr(mse))
+    if st:
+        raise OracleError(st)
+    return {"codes": codes, "scales": scales, "g": float(g[0]), "a": a, "b": b, "mse": mse}
 
 
 def solve(W: np.ndarray, dtype: str, fmt: str, group: int, T: int, a0=None, b0=None,

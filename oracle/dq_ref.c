@@ -550,10 +550,18 @@ done:
 
 /* ----------------------------------------------------------------- public: the solver */
 
-int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int group,
-                      int T, const float* a0, const float* b0, float g0, uint8_t* codes,
-                      void* scales, float* g_out, float* a, float* b, double* mse,
-                      int64_t* changes, double* margin) {
+/* NVFP4 with a per-pass tensor scale: g from the scaled tile about to be quantized */
+static int set_pass_g(ctx_t* c, const float* ra, const float* rb) {
+  c->g = tensor_scale(c, ra, rb);
+  if (!isfinite(c->g)) return DQR_ERR_RANGE;
+  c->sixg = fl32_mul(6.0f, c->g);
+  return DQR_OK;
+}
+
+static int solve_core(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int group,
+                      int T, const float* a0, const float* b0, float g0, int per_pass,
+                      uint8_t* codes, void* scales, float* g_out, float* a, float* b,
+                      double* mse, int64_t* changes, double* margin) {
   int st = check_common(W, wt, rows, cols, fmt, group);
   if (st) return st;
   if (T < 0 || !codes || !scales || !a || !b || !mse || (fmt == DQR_FMT_NVFP4 && !g_out))
@@ -601,6 +609,7 @@ int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt
 
   for (int t = 0; t < T; t++) {
     /* 1-2: quantize the synced state, record its error */
+    if (per_pass && (st = set_pass_g(&c, ra, rb))) goto done;
     if ((st = q_pass(&c, ra, rb, qA, dA, sA))) goto done;
     mse[t] = mse_of(&c, a, b, qA, dA, row_err);
     if (changes && t > 0) {
@@ -639,6 +648,7 @@ int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt
     fill_reciprocals(a, ra, m);
 
     /* 4: re-quantize with the synced inner copy of the new a */
+    if (per_pass && (st = set_pass_g(&c, ra, rb))) goto done;
     if ((st = q_pass(&c, ra, rb, qB, dB, sB))) goto done;
     if (changes) {
       changes[4 * t + 0] = count_diff_i8(qA, qB, m * n);
@@ -678,6 +688,10 @@ int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt
   }
 
   /* final synced state: codes, inner scales and its error */
+  if (per_pass) {
+    if ((st = set_pass_g(&c, ra, rb))) goto done;
+    *g_out = c.g;
+  }
   if ((st = q_pass(&c, ra, rb, qA, dA, sA))) goto done;
   mse[T] = mse_of(&c, a, b, qA, dA, row_err);
   if (changes && T > 0) {
@@ -700,6 +714,25 @@ done:
   free(Dc);
   free(mrow);
   return st;
+}
+
+int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int group,
+                      int T, const float* a0, const float* b0, float g0, uint8_t* codes,
+                      void* scales, float* g_out, float* a, float* b, double* mse,
+                      int64_t* changes, double* margin) {
+  return solve_core(W, wt, rows, cols, fmt, group, T, a0, b0, g0, 0, codes, scales, g_out, a,
+                    b, mse, changes, margin);
+}
+
+/* NVFP4 with the tensor scale recomputed before every Q pass (reading of the pages'
+ * black-box quantizer applied to each scaled tile as it stands; the per-tensor scale is not
+ * on the pages): g = fl32(max|X| / 2688) of the tile about to be quantized, for the synced
+ * state, the re-quantization after the row update and the final pass alike. */
+int dq_ref_solve_pass_g(const void* W, int wt, int64_t rows, int64_t cols, int group, int T,
+                        const float* a0, const float* b0, uint8_t* codes, void* scales,
+                        float* g_out, float* a, float* b, double* mse) {
+  return solve_core(W, wt, rows, cols, DQR_FMT_NVFP4, group, T, a0, b0, 0.0f, 1, codes, scales,
+                    g_out, a, b, mse, NULL, NULL);
 }
 
 int dq_ref_solve(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int group, int T,

@@ -76,6 +76,14 @@ int dq_ref_solve(const void* W, int wt, int64_t rows, int64_t cols, int fmt, int
                  const float* a0, const float* b0, float g0, uint8_t* codes, void* scales,
                  float* g_out, float* a, float* b, double* mse);
 
+/* NVFP4 (group 16) with the tensor scale recomputed before every Q pass: g =
+ * fl32(max|X| / 2688) (at least 2^-126; 1 if X == 0) of the scaled tile about to be
+ * quantized, for each synced state, each re-quantization after a row update and the final
+ * pass. g_out receives the final pass's g. Other arguments as dq_ref_solve. */
+int dq_ref_solve_pass_g(const void* W, int wt, int64_t rows, int64_t cols, int group, int T,
+                        const float* a0, const float* b0, uint8_t* codes, void* scales,
+                        float* g_out, float* a, float* b, double* mse);
+
 /* dq_ref_solve plus diagnostics (either pointer may be NULL):
  * changes[4*t + 0/1]: codes / inner scales that differ between the synced state
  *                     before iteration t and the re-quantization after its row update;
