@@ -23,6 +23,7 @@ DTYPE = {"f32": 0, "bf16": 1}
 STATUS = {0: "DQ_OK", 1: "DQ_ERR_ARG", 2: "DQ_ERR_UNSUPPORTED", 3: "DQ_ERR_NONFINITE",
           4: "DQ_ERR_RANGE", 5: "DQ_ERR_WORKSPACE", 6: "DQ_ERR_HIP", 7: "DQ_ERR_INTERNAL"}
 SOLVE_TWO_SWEEP = 1
+SOLVE_PER_PASS_G = 2
 KERNEL_KINDS = ("setup", "fused", "row", "col", "final", "emit")
 
 
@@ -131,7 +132,7 @@ def _vec(v, n, device):
 
 def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
           two_sweep: bool = False, workspace=None, timing: bool = False,
-          stream=None, flush=None) -> Dict[str, object]:
+          stream=None, flush=None, per_pass_g: bool = False) -> Dict[str, object]:
     """dq_solve on W (rows x cols, CUDA float32 / bfloat16). Returns a dict of device
     tensors codes (rows x cols/2 u8), scales (rows x cols/group; int16 holding bf16 bits for
     int4_bf16, else u8), a, b (float32), mse (T+1 float64), g (float32[1]) and, when
@@ -152,7 +153,8 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
     if tm is not None and flush is not None:
         tm.flush = flush.data_ptr()
         tm.flush_bytes = flush.numel() * flush.element_size() // 16 * 16
-    init = _Init(_ptr(a0), _ptr(b0), float(g0), SOLVE_TWO_SWEEP if two_sweep else 0,
+    flags = (SOLVE_TWO_SWEEP if two_sweep else 0) | (SOLVE_PER_PASS_G if per_pass_g else 0)
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags,
                  ctypes.pointer(tm) if tm is not None else None)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())

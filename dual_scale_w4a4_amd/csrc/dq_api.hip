@@ -269,6 +269,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   const float* a_src = again ? a0s : (io.init ? io.init->a0 : nullptr);
   const float* b_src = again ? b0s : (io.init ? io.init->b0 : nullptr);
   const bool fast = fused && io.bf16;  // the single-sweep kernel for bf16 weights
+  const bool pass_g = nv && io.init && (io.init->flags & DQ_SOLVE_PER_PASS_G);
   VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(va, s));
   VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, fast ? 1 : 0, status};
@@ -280,6 +281,17 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
     DQ_TRY(launch_tensor_scale(sa, s));
   }
   tm.after();
+
+  // NVFP4 with a per-pass tensor scale: g from the scaled tile about to be quantized
+  auto pass_scale = [&]() -> dq_status {
+    tm.before(DQ_K_SETUP);
+    RowStatArgs r2{io.W, p.m, p.n, ra, rb, E, amax, status};
+    DQ_TRY(launch_rowstat(io.bf16, r2, s));
+    ScaleArgs s2{amax, p.m, nullptr, 0.0f, gs, io.tensor_scale, status};
+    DQ_TRY(launch_tensor_scale(s2, s));
+    tm.after();
+    return DQ_OK;
+  };
 
   SweepArgs sw{};
   sw.W = io.W;
@@ -382,29 +394,34 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       fa.gauge_check = 1;
       if ((st = finalize(true, true, true)) != DQ_OK) return st;
     } else if (io.bf16) {
+      if (pass_g && t > 0 && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_ROW);
       DQ_TRY(launch_pass(p.fmt, kModeRow, sp, s));
       tm.after();
       fa.nct = p.g_nct;
       fa.nrc = p.g_nrc;
       if ((st = finalize(true, false, true)) != DQ_OK) return st;
+      if (pass_g && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_COL);
       DQ_TRY(launch_pass(p.fmt, kModeCol, sp, s));
       tm.after();
       if ((st = finalize(false, true, false)) != DQ_OK) return st;
     } else {
+      if (pass_g && t > 0 && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_ROW);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow, sw, s));
       tm.after();
       fa.nct = p.nct;
       fa.nrc = p.nrc;
       if ((st = finalize(true, false, true)) != DQ_OK) return st;
+      if (pass_g && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_COL);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeCol, sw, s));
       tm.after();
       if ((st = finalize(false, true, false)) != DQ_OK) return st;
     }
   }
+  if (pass_g && io.T > 0 && (st = pass_scale()) != DQ_OK) return st;
   tm.before(DQ_K_EMIT);
   if (fast) {
     DQ_TRY(launch_fused(p.fmt, true, fu, s));
@@ -566,6 +583,8 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
   if (st != DQ_OK) return st;
   if (T < 0 || !a || !b || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale)) return DQ_ERR_ARG;
   if (init && (init->g0 != init->g0 || (init->g0 > 0.0f && init->g0 > 3.4028234663852886e38f)))
+    return DQ_ERR_ARG;
+  if (init && fmt == DQ_FMT_NVFP4 && (init->flags & DQ_SOLVE_PER_PASS_G) && init->g0 > 0.0f)
     return DQ_ERR_ARG;
   const Plan p = make_plan(rows, cols, fmt, group);
   WsGuard ws;

@@ -71,6 +71,11 @@ typedef enum { DQ_F32 = 0, DQ_BF16 = 1 } dq_dtype;
 /* Solver options (dq_init.flags). */
 #define DQ_SOLVE_TWO_SWEEP 1u /* MX formats: always re-read W for the column pass instead of
                                  reusing the row pass's codes (the general path) */
+/* NVFP4 only (ignored for the other formats): recompute the tensor scale g before every Q
+ * pass, g = fl32(max|X| / 2688) of the scaled tile about to be quantized (at least 2^-126;
+ * 1 if X == 0), instead of fixing it from the initial tile; tensor_scale receives the final
+ * pass's g, and init->g0 must then be <= 0. Costs one read of W per Q pass. */
+#define DQ_SOLVE_PER_PASS_G 2u
 
 /* Per-kernel timing, filled by dq_solve when dq_init.timing is not NULL (HIP events recorded
  * on `stream` around each launch; adds a little overhead). Index by dq_kernel_kind. */

@@ -410,6 +410,7 @@ static int w_finite(const ctx_t* c) {
  * below 2^-126. Computed once from the initial state and then held fixed. */
 static float tensor_scale(const ctx_t* c, const float* ra, const float* rb) {
   float A = 0.0f;
+#pragma omp parallel for num_threads(g_threads) schedule(static) reduction(max : A)
   for (int64_t i = 0; i < c->m; i++)
     for (int64_t j = 0; j < c->n; j++)
       A = fmaxf(A, fabsf(fl32_mul(fl32_mul(w_at(c, i, j), rb[j]), ra[i])));

@@ -189,3 +189,26 @@ def test_subnormal_groups_on_the_two_sweep_pass(dq, oracle_lib, fmt):
     Wb = workloads.fp32_to_bf16_bits(W32)
     w = workloads.Workload("subnormal", Wb, "bf16", fmt, group, 4)
     _run_pair(dq, oracle_lib, w)
+
+
+@pytest.mark.parametrize("shape,T,dtype", [((520, 1104), 20, "bf16"), ((96, 512), 6, "f32"),
+                                           ((4096, 8192), 8, "bf16")])
+def test_nvfp4_per_pass_tensor_scale(dq, par_oracle, shape, T, dtype):
+    # the tensor scale recomputed from each scaled tile before every Q pass
+    rows, cols = shape
+    w = workloads.config4(rows, cols)
+    W = w.W if dtype == "bf16" else workloads.bf16_bits_to_fp32(w.W)
+    print(f"[solve] per-pass g {shape} {dtype} T={T}", flush=True)
+    ref = par_oracle.solve_pass_g(W, dtype, 16, T)
+    gpu = dq.solve(to_device(W, dtype), "nvfp4", 16, T, per_pass_g=True)
+    res = compare_solve(gpu, ref, "nvfp4", rows, cols)
+    assert_parity(res, exact=False, name=f"per-pass g {shape}")
+    assert res["code_diffs"] == 0 and res["a_flips"] == 0 and res["b_flips"] == 0, res
+    assert host(gpu["g"])[0] == np.float32(ref["g"])
+
+
+def test_per_pass_tensor_scale_rejects_a_fixed_one(dq):
+    W = to_device(rand_w(64, 512, seed=2), "f32")
+    with pytest.raises(dq.DQError) as e:
+        dq.solve(W, "nvfp4", 16, 2, g0=0.01, per_pass_g=True)
+    assert e.value.status == 1
