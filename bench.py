@@ -112,6 +112,8 @@ def main() -> None:
     ap.add_argument("--sequential", action="store_true",
                     help="solve the matrices of a step one after another on one stream "
                          "(default: each on its own stream, concurrently)")
+    ap.add_argument("--per-pass-g", action="store_true",
+                    help="NVFP4 workloads: recompute the tensor scale before every Q pass")
     ap.add_argument("--act", action="store_true",
                     help="measure the activation quantizer instead (x = X b, then Q) on the "
                          "Llama-3.1-8B MLP inputs of 8192 tokens; prints its own JSON line")
@@ -163,7 +165,8 @@ def main() -> None:
     def solve_one(k, T, timing, stream):
         w = mats[k]
         return dq.solve(dev_w[k], w.fmt, w.group, w.T if T is None else T, workspace=wss[k],
-                        timing=timing, stream=stream, flush=flush if timing else None)
+                        timing=timing, stream=stream, flush=flush if timing else None,
+                        per_pass_g=args.per_pass_g and w.fmt == "nvfp4")
 
     def step(T=None, timing=False):
         # dq_solve returns when its stream is done; concurrent calls use separate streams
@@ -243,7 +246,8 @@ def main() -> None:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators in workloads/, no checkpoint)",
-        "config": {"workload": desc, "matrices": [w.name for w in mats],
+        "config": {"workload": desc + (", tensor scale per Q pass" if args.per_pass_g else ""),
+                   "matrices": [w.name for w in mats],
                    "format": mats[0].fmt, "group": mats[0].group, "T": mats[0].T,
                    "weights": mats[0].dtype, "sums": "f64"},
         "per_iteration": {"ms": t_iter * 1e3, "elems_per_s": elems / t_iter,
@@ -270,7 +274,7 @@ def main() -> None:
     }
 
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(mats[0], dq, to_device)
+        line["cpu_baseline"] = cpu_baseline(mats[0], dq, to_device, args.per_pass_g)
     print(json.dumps(line), flush=True)
 
 
@@ -357,7 +361,7 @@ def bench_act(args, dq) -> None:
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, dq, to_device):
+def cpu_baseline(w, dq, to_device, per_pass_g=False):
     """The oracle on a bounded row sample of the first matrix (same T), all host cores up to
     16, and the GPU on the same sample checked against it."""
     import numpy as np
@@ -368,10 +372,14 @@ def cpu_baseline(w, dq, to_device):
     sample = np.ascontiguousarray(w.W[:rows])
     threads = oracle.set_threads(min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    ref = oracle.solve(sample, w.dtype, w.fmt, w.group, w.T)
+    pp = per_pass_g and w.fmt == "nvfp4"
+    if pp:
+        ref = oracle.solve_pass_g(sample, w.dtype, w.group, w.T)
+    else:
+        ref = oracle.solve(sample, w.dtype, w.fmt, w.group, w.T)
     dt = time.perf_counter() - t0
     oracle.set_threads(1)
-    gpu = dq.solve(to_device(sample, w.dtype), w.fmt, w.group, w.T)
+    gpu = dq.solve(to_device(sample, w.dtype), w.fmt, w.group, w.T, per_pass_g=pp)
     mse_g = gpu["mse"].cpu().numpy()
     a_eq = bool(np.array_equal(gpu["a"].cpu().numpy(), ref["a"]))
     b_eq = bool(np.array_equal(gpu["b"].cpu().numpy(), ref["b"]))

@@ -89,7 +89,7 @@ struct Plan {
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
-  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, total = 0;
+  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, off_ymax = 0, total = 0;
 };
 
 bool shape_ok(int64_t rows, int64_t cols, int group) {
@@ -146,6 +146,10 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
   p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
   p.off_msepart = o; o = align_up(o + 2 * sizeof(double) * p.nblk_rows);
+  if (fmt == DQ_FMT_NVFP4) {  // per-pass tensor scale: the row pass's row maxima of |y|
+    p.off_ymax = o;
+    o = align_up(o + sizeof(float) * (size_t)p.g_nct * m);
+  }
   p.total = o;
   return p;
 }
@@ -313,6 +317,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   sw.status = status;
 
   SweepArgs sp = sw;  // the two-sweep pass for bf16 weights
+  sp.ymax = p.off_ymax ? at<float>(ws, p.off_ymax) : nullptr;
   sp.nct = p.g_nct;
   sp.nrc = p.g_nrc;
   sp.rpc = p.g_rpc;
@@ -396,12 +401,23 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
     } else if (io.bf16) {
       if (pass_g && t > 0 && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_ROW);
-      DQ_TRY(launch_pass(p.fmt, kModeRow, sp, s));
+      // per-pass tensor scale: the row pass also records each row's max |fl32(W rb)|, from
+      // which the finalize forms the column pass's row maxima of |X| without a read of W
+      DQ_TRY(launch_pass(p.fmt, pass_g ? (kModeRow | kModeYmax) : kModeRow, sp, s));
       tm.after();
       fa.nct = p.g_nct;
       fa.nrc = p.g_nrc;
+      fa.ymax = pass_g ? sp.ymax : nullptr;
+      fa.amax_out = pass_g ? amax : nullptr;
       if ((st = finalize(true, false, true)) != DQ_OK) return st;
-      if (pass_g && (st = pass_scale()) != DQ_OK) return st;
+      fa.ymax = nullptr;
+      fa.amax_out = nullptr;
+      if (pass_g) {
+        tm.before(DQ_K_SETUP);
+        ScaleArgs s2{amax, p.m, nullptr, 0.0f, gs, io.tensor_scale, status};
+        DQ_TRY(launch_tensor_scale(s2, s));
+        tm.after();
+      }
       tm.before(DQ_K_COL);
       DQ_TRY(launch_pass(p.fmt, kModeCol, sp, s));
       tm.after();

@@ -18,7 +18,7 @@ enum : int {
 };
 
 // sweep modes (bit set)
-enum : int { kModeRow = 1, kModeCol = 2, kModeEmit = 4, kModeGauge = 8 };
+enum : int { kModeRow = 1, kModeCol = 2, kModeEmit = 4, kModeGauge = 8, kModeYmax = 16 };
 
 struct SweepArgs {
   const void* W;
@@ -37,6 +37,7 @@ struct SweepArgs {
   uint8_t* codes;
   void* scales;
   int* status;
+  float* ymax;       // kModeYmax: [nct][m] row maxima of |fl32(W rb)| per column tile
 };
 
 // Single-sweep MX pass on bf16 weights (see k_fused_mx).
@@ -119,6 +120,10 @@ struct FinArgs {
   float* b;
   float* rb;
   int* status;
+  // rows, NVFP4 with a per-pass tensor scale: the row pass's [nct][m] maxima of |y| in, and
+  // the next pass's row maxima of |x| out
+  const float* ymax;
+  float* amax_out;
 };
 
 // Activation quantization x = fl32(X * b), then Q (dq_act.hip).

@@ -528,13 +528,25 @@ __global__ void k_vec(VecArgs p) {
 }
 
 // NVFP4 tensor scale g = fl32(A / 2688) (2688 = 6 * 448), at least 2^-126; 1 if A = 0.
-__global__ __launch_bounds__(256) void k_tensor_scale(ScaleArgs p) {
-  __shared__ float red[256];
+constexpr int kScaleThreads = 1024;
+
+__global__ __launch_bounds__(kScaleThreads) void k_tensor_scale(ScaleArgs p) {
+  __shared__ float red[kScaleThreads];
   float mx = 0.0f;
-  for (int64_t i = threadIdx.x; i < p.m; i += 256) mx = fmaxf(mx, p.amax[i]);
+  constexpr int kU = 8;  // loads in flight per thread
+  for (int64_t i0 = threadIdx.x; i0 < p.m; i0 += (int64_t)kU * kScaleThreads) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int64_t i = i0 + (int64_t)u * kScaleThreads;
+      v[u] = i < p.m ? p.amax[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; u++) mx = fmaxf(mx, v[u]);
+  }
   red[threadIdx.x] = mx;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = kScaleThreads / 2; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
     __syncthreads();
   }
@@ -645,6 +657,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
       } else {
         err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
       }
+      float Y = 0.0f;  // max over this row of |y| = |fl32(W rb)|, from the row pass's tiles
+      if (p.ymax)
+        for (int k = 0; k < p.nct; k++) Y = fmaxf(Y, p.ymax[(int64_t)k * p.m + i]);
       if (p.update_a) {
         float an = 1.0f;  // an all-zero code slice keeps scale 1
         if (D > 0.0) {
@@ -659,6 +674,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
         if (p.envelope && !(an >= 0x1p-24f && an <= 0x1p24f)) flags |= kStGauge;
         p.a[i] = an;
         p.ra[i] = recip32(an);
+        // the next pass's row max of |x| = |fl32(y ra')|: fl32 is monotone, so it is
+        // fl32(max |y| * ra') exactly
+        if (p.ymax) p.amax_out[i] = Y * p.ra[i];
       }
     }
     red[tid] = err;
@@ -735,7 +753,7 @@ hipError_t launch_rowstat(bool bf16, const RowStatArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(kScaleThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
                                          float g, float sixg, uint32_t amask, double& nacc,
                                          double& dacc, double (&P)[kPassEpl],
                                          double (&Q)[kPassEpl], int& flags, uint32_t* code_word,
-                                         void* scale_ptr) {
+                                         void* scale_ptr, float& ymax) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
   constexpr bool COL = (MODE & kModeCol) != 0;
   constexpr bool EMIT = (MODE & kModeEmit) != 0;
@@ -55,12 +55,15 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
     w[2 * k] = u2f(u[k] << 16);
     w[2 * k + 1] = u2f(u[k] & 0xFFFF0000u);
   }
-  float mx = 0.0f;
+  float mx = 0.0f, ym = 0.0f;
 #pragma unroll
   for (int k = 0; k < E; k++) {
-    x[k] = (w[k] * rb[k]) * ra;  // column scale first, then row scale; two fp32 roundings
+    const float y = w[k] * rb[k];  // column scale first, then row scale; two fp32 roundings
+    x[k] = y * ra;
     mx = fmaxf(mx, fabsf(x[k]));
+    if (MODE & kModeYmax) ym = fmaxf(ym, fabsf(y));
   }
+  ymax = ym;
   float gm = LPG > 1 ? u2f(group_max_bits<LPG>(f2u(mx))) : mx;
   if (!(gm <= FLT_MAX)) {  // a scaled value overflowed
     flags |= kStRange;
@@ -185,10 +188,14 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
     ra_v = p.ra[i];
     if (COL) a_v = p.a[i];
   };
+  constexpr bool YMAX = (MODE & kModeYmax) != 0;
+  __shared__ float ysmem[YMAX ? kWaves * kPassBatch * kWave : 1];
+  float* Ry = ysmem + (YMAX ? wave * (kPassBatch * kWave) : 0);  // [8 rows][64 lanes] max |y|
   double2* R = smem + wave * (kPassBatch * kWave);  // this wave's [8 rows][64 lanes] partials
   float ra_cur = 0.0f, a_cur = 0.0f, ra_nxt = 0.0f, a_nxt = 0.0f;
   auto row_step = [&](const uint4 (&v)[2], int64_t i, int r) {
     double nacc = 0.0, dacc = 0.0;
+    float ym = 0.0f;
     if (i < r_end) {  // uniform across the wave
       const float ra = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_cur), r));
       const float ai = COL ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a_cur), r)) : 0.0f;
@@ -201,9 +208,10 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
                                      : (void*)(static_cast<uint8_t*>(p.scales) + si);
       }
       pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, amask, nacc, dacc, P, Q,
-                                        flags, code_word, scale_ptr);
+                                        flags, code_word, scale_ptr, ym);
     }
     if (ROW) R[r * kWave + lane] = make_double2(nacc, dacc);
+    if (YMAX) Ry[r * kWave + lane] = ym;
   };
 
   constexpr int kSteps = kPassBatch / S;
@@ -248,6 +256,14 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
       D = sum8_dpp(D);
       const int64_t i = row0 + (lane >> 3);
       if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, D);
+      if (YMAX) {  // the same for the row max of |y| (bit patterns of non-negative floats)
+        const float* ysrc = Ry + (lane >> 3) * kWave + (lane & 7) * 8;
+        uint32_t yb = 0u;
+#pragma unroll
+        for (int k = 0; k < 8; k++) yb = max(yb, f2u(ysrc[k]));
+        yb = group_max_bits<8>(yb);
+        if ((lane & 7) == 0 && i < r_end) p.ymax[(int64_t)ct * p.m + i] = u2f(yb);
+      }
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -305,6 +321,9 @@ static hipError_t pass_mode(int mode, const SweepArgs& a, dim3 grid, hipStream_t
     case kModeRow: return pass_group<FMT, kModeRow>(a, grid, s);
     case kModeCol: return pass_group<FMT, kModeCol>(a, grid, s);
     case kModeRow | kModeEmit: return pass_group<FMT, kModeRow | kModeEmit>(a, grid, s);
+    case kModeRow | kModeYmax:
+      if constexpr (FMT == kNvFp4) return pass_group<FMT, kModeRow | kModeYmax>(a, grid, s);
+      return hipErrorInvalidValue;  // only NVFP4 has a tensor scale
     default: return hipErrorInvalidValue;
   }
 }
