@@ -112,6 +112,14 @@ def main() -> None:
     ap.add_argument("--sequential", action="store_true",
                     help="solve the matrices of a step one after another on one stream "
                          "(default: each on its own stream, concurrently)")
+    ap.add_argument("--only", default="",
+                    help="workload 5: solve only these of the layer's matrices (comma list of "
+                         "q,k,v,o,gate,up,down), e.g. the small k,v")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="workload 5: decoder layers per step (layer-by-layer inputs 0..N-1)")
+    ap.add_argument("--batch", action="store_true",
+                    help="solve the step's matrices with one batch solve (shared launches) "
+                         "instead of one solve per matrix")
     ap.add_argument("--per-pass-g", action="store_true",
                     help="NVFP4 workloads: recompute the tensor scale before every Q pass")
     ap.add_argument("--act", action="store_true",
@@ -147,6 +155,14 @@ def main() -> None:
         return
 
     mats, desc = _load(args.workload)
+    if args.workload == 5:
+        import workloads
+
+        only = tuple(args.only.split(",")) if args.only else None
+        mats = [w for L in range(args.layers) for w in workloads.config5_layer(L, only=only)]
+        desc = desc.replace("layer 0", f"layers 0..{args.layers - 1}" if args.layers > 1 else "layer 0")
+        if args.only:
+            desc += f", only {args.only}"
     dev_w = [to_device(w.W, w.dtype) for w in mats]
     work = [dq.workspace_bytes(w.rows, w.cols, w.fmt, w.group) for w in mats]
     wss = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in work]
@@ -168,7 +184,18 @@ def main() -> None:
                         timing=timing, stream=stream, flush=flush if timing else None,
                         per_pass_g=args.per_pass_g and w.fmt == "nvfp4")
 
+    batch_ws = None
+    if args.batch:
+        batch_ws = torch.empty(dq.batch_workspace_bytes([(w.rows, w.cols) for w in mats],
+                                                        mats[0].fmt, mats[0].group),
+                               dtype=torch.uint8, device="cuda")
+
     def step(T=None, timing=False):
+        if args.batch and not timing:
+            w = mats[0]
+            return dq.solve_batch(dev_w, w.fmt, w.group, w.T if T is None else T,
+                                  per_pass_g=args.per_pass_g and w.fmt == "nvfp4",
+                                  workspace=batch_ws)
         # dq_solve returns when its stream is done; concurrent calls use separate streams
         # and workspaces (the library keeps no global state)
         if pool is None or timing:
@@ -246,7 +273,8 @@ def main() -> None:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators in workloads/, no checkpoint)",
-        "config": {"workload": desc + (", tensor scale per Q pass" if args.per_pass_g else ""),
+        "config": {"workload": desc + (", tensor scale per Q pass" if args.per_pass_g else "")
+                   + (", one batch solve" if args.batch else ""),
                    "matrices": [w.name for w in mats],
                    "format": mats[0].fmt, "group": mats[0].group, "T": mats[0].T,
                    "weights": mats[0].dtype, "sums": "f64"},
@@ -270,7 +298,8 @@ def main() -> None:
             "cold_GBps": cw[3] / (cw[0] * 1e-3) / 1e9, "warm_GBps": cw[3] / (cw[1] * 1e-3) / 1e9,
             "warm_over_cold_speed": cw[0] / cw[1]},
         "single_sweep_path": used_fused if kind == "fused" else None,
-        "concurrent_matrices": pool is not None,
+        "concurrent_matrices": pool is not None and not args.batch,
+        "batch_solve": args.batch,
     }
 
     if not args.no_cpu:

@@ -234,3 +234,69 @@ def quantize_act_async(X, fmt: str, group: int, codes, scales, status, b=None, g
                                      _stream(stream))
     if st != 0:
         raise DQError(st, "dq_quantize_act_async")
+
+
+class _BatchItem(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("a0", ctypes.c_void_p), ("b0", ctypes.c_void_p), ("g0", ctypes.c_float),
+                ("codes", ctypes.c_void_p), ("inner_scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("mse", ctypes.c_void_p)]
+
+
+def _batch_lib():
+    L = lib()
+    if not getattr(L, "_batch_ready", False):
+        P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.dq_batch_workspace_bytes.argtypes = [I, ctypes.POINTER(_BatchItem), I, I]
+        L.dq_batch_workspace_bytes.restype = SZ
+        L.dq_solve_batch.argtypes = [I, ctypes.POINTER(_BatchItem), I, I, I, I, ctypes.c_uint, P,
+                                     P, SZ, P]
+        L.dq_solve_batch.restype = I
+        L._batch_ready = True
+    return L
+
+
+def solve_batch(Ws, fmt: str, group: int, T: int, per_pass_g: bool = False, workspace=None,
+                stream=None):
+    """dq_solve_batch on a list of bf16 CUDA matrices (one format and group): every matrix
+    solved as dq.solve would solve it, with the per-iteration passes of up to 16 matrices
+    sharing each launch. Returns one dict per matrix, as solve() does, with its status."""
+    torch = _torch()
+    n = len(Ws)
+    items = (_BatchItem * n)()
+    outs = []
+    for k, W in enumerate(Ws):
+        if _check_w(W) != "bf16":
+            raise ValueError("solve_batch takes bf16 weights")
+        rows, cols = W.shape
+        codes, scales = _outputs(W, fmt, group)
+        o = {"codes": codes, "scales": scales,
+             "a": torch.empty(rows, dtype=torch.float32, device=W.device),
+             "b": torch.empty(cols, dtype=torch.float32, device=W.device),
+             "mse": torch.empty(T + 1, dtype=torch.float64, device=W.device),
+             "g": torch.zeros(1, dtype=torch.float32, device=W.device)}
+        items[k] = _BatchItem(W.data_ptr(), rows, cols, None, None, 0.0, codes.data_ptr(),
+                              scales.data_ptr(), o["g"].data_ptr(), o["a"].data_ptr(),
+                              o["b"].data_ptr(), o["mse"].data_ptr())
+        outs.append(o)
+    L = _batch_lib()
+    status = (ctypes.c_int * n)()
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = L.dq_solve_batch(n, items, DTYPE["bf16"], FMT[fmt], group, T,
+                          SOLVE_PER_PASS_G if per_pass_g else 0, ctypes.cast(status, ctypes.c_void_p),
+                          ws_ptr, ws_bytes, _stream(stream))
+    for k in range(n):
+        outs[k]["status"] = int(status[k])
+    if st != 0:
+        raise DQError(st, "dq_solve_batch")
+    return outs
+
+
+def batch_workspace_bytes(shapes, fmt: str, group: int) -> int:
+    n = len(shapes)
+    items = (_BatchItem * n)()
+    for k, (rows, cols) in enumerate(shapes):
+        items[k] = _BatchItem(None, rows, cols, None, None, 0.0, None, None, None, None, None, None)
+    return int(_batch_lib().dq_batch_workspace_bytes(n, items, FMT[fmt], group))

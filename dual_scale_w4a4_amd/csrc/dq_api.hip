@@ -463,6 +463,166 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   return DQ_OK;
 }
 
+// ------------------------------------------------------------------------- batch solves
+// One matrix of a batch solve on the two-sweep path for bf16 weights: the same state, kernels
+// and order of operations as enqueue_solve's two-sweep branch, stepped phase by phase so that
+// the per-iteration passes and finalizes of all matrices share launches.
+struct BatchMat {
+  Plan p;
+  char* ws = nullptr;
+  SolveIo io{};
+  bool pass_g = false;
+  int* status = nullptr;
+  float *ra = nullptr, *rb = nullptr, *amax = nullptr, *gs = nullptr;
+  double* E = nullptr;
+  double* msepart = nullptr;
+  dq::SweepArgs sp{};
+  dq::FinArgs fa{};
+  int produced = 0, pend_idx = -1;
+
+  dq_status setup(const dq_init* init, hipStream_t s) {
+    using namespace dq;
+    status = at<int>(ws, p.off_status);
+    ra = at<float>(ws, p.off_ra);
+    rb = at<float>(ws, p.off_rb);
+    E = at<double>(ws, p.off_E);
+    amax = at<float>(ws, p.off_amax);
+    gs = at<float>(ws, p.off_gs);
+    msepart = at<double>(ws, p.off_msepart);
+    const bool nv = p.fmt == kNvFp4;
+    DQ_TRY(launch_clear(status, 16, s));
+    VecArgs va{init->a0, io.a, ra, nullptr, p.m, p.fmt, 1, 0, status};
+    DQ_TRY(launch_vec(va, s));
+    VecArgs vb{init->b0, io.b, rb, nullptr, p.n, p.fmt, 1, 0, status};
+    DQ_TRY(launch_vec(vb, s));
+    RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
+    DQ_TRY(launch_rowstat(true, rs, s));
+    if (nv) {
+      ScaleArgs sa{amax, p.m, nullptr, init->g0, gs, io.tensor_scale, status};
+      DQ_TRY(launch_tensor_scale(sa, s));
+    }
+    sp = SweepArgs{};
+    sp.W = io.W;
+    sp.m = p.m;
+    sp.n = p.n;
+    sp.G = p.G;
+    sp.ra = ra;
+    sp.rb = rb;
+    sp.a = io.a;
+    sp.b = io.b;
+    sp.gs = gs;
+    sp.nct = p.g_nct;
+    sp.nrc = p.g_nrc;
+    sp.rpc = p.g_rpc;
+    sp.rowpart = at<double2>(ws, p.off_rowpart);
+    sp.colpart = at<double2>(ws, p.off_colpart);
+    sp.codes = io.codes;
+    sp.scales = io.scales;
+    sp.status = status;
+    sp.ymax = p.off_ymax ? at<float>(ws, p.off_ymax) : nullptr;
+    fa = FinArgs{};
+    fa.m = p.m;
+    fa.n = p.n;
+    fa.fmt = p.fmt;
+    fa.rowpart = sp.rowpart;
+    fa.E = E;
+    fa.a = io.a;
+    fa.ra = ra;
+    fa.inv_mn = 1.0 / ((double)p.m * (double)p.n);
+    fa.colpart = sp.colpart;
+    fa.b = io.b;
+    fa.rb = rb;
+    fa.status = status;
+    fa.prev_count = p.nblk_rows;
+    fa.nct = p.g_nct;
+    fa.nrc = p.g_nrc;
+    return DQ_OK;
+  }
+
+  // per-pass tensor scale of the tile about to be quantized (a read of W)
+  dq_status pass_scale(hipStream_t s) {
+    using namespace dq;
+    RowStatArgs r2{io.W, p.m, p.n, ra, rb, E, amax, status};
+    DQ_TRY(launch_rowstat(true, r2, s));
+    ScaleArgs s2{amax, p.m, nullptr, 0.0f, gs, io.tensor_scale, status};
+    DQ_TRY(launch_tensor_scale(s2, s));
+    return DQ_OK;
+  }
+
+  // the arguments of one finalize launch, with the double-buffered mse bookkeeping
+  dq::FinArgs fin(bool rows, bool cols, bool update) {
+    fa.nblk_rows = rows ? p.nblk_rows : 0;
+    fa.nblk_cols = cols ? p.nblk_cols : 0;
+    fa.update_a = update ? 1 : 0;
+    fa.prev_part = pend_idx >= 0 ? msepart + (size_t)(pend_idx % 2) * p.nblk_rows : nullptr;
+    fa.prev_out = pend_idx >= 0 ? io.mse + pend_idx : nullptr;
+    pend_idx = -1;
+    fa.part_out = nullptr;
+    if (rows) {
+      fa.part_out = msepart + (size_t)(produced % 2) * p.nblk_rows;
+      pend_idx = produced++;
+    }
+    return fa;
+  }
+
+  dq_status emit(hipStream_t s) {
+    using namespace dq;
+    if (pass_g && io.T > 0) DQ_TRY(pass_scale(s));
+    DQ_TRY(launch_pass(p.fmt, kModeEmit | kModeRow, sp, s));
+    fa.ymax = nullptr;
+    fa.amax_out = nullptr;
+    DQ_TRY(launch_finalize(fin(true, false, false), s));
+    DQ_TRY(launch_mse_collect(msepart + (size_t)(pend_idx % 2) * p.nblk_rows, p.nblk_rows,
+                              io.mse + pend_idx, fa.inv_mn, s));
+    return DQ_OK;
+  }
+};
+
+// One iteration of every matrix of a batch: grouped row passes, row finalizes, column passes
+// and column finalizes, up to kMaxMulti matrices per launch.
+dq_status batch_iteration(BatchMat* mats, int n, int t, hipStream_t s) {
+  using namespace dq;
+  const int fmt = mats[0].p.fmt;
+  const bool pass_g = mats[0].pass_g;
+  for (int k0 = 0; k0 < n; k0 += kMaxMulti) {
+    const int cnt = n - k0 < kMaxMulti ? n - k0 : kMaxMulti;
+    BatchMat* b = mats + k0;
+    if (pass_g && t > 0)
+      for (int k = 0; k < cnt; k++) DQ_TRY(b[k].pass_scale(s));
+    PassMulti pm{};
+    pm.n = cnt;
+    for (int k = 0; k < cnt; k++) {
+      pm.a[k] = b[k].sp;
+      pm.start[k + 1] = pm.start[k] + b[k].p.g_nct * b[k].p.g_nrc;
+    }
+    DQ_TRY(launch_pass_multi(fmt, pass_g ? (kModeRow | kModeYmax) : kModeRow, pm, s));
+    FinMulti fm{};
+    fm.n = cnt;
+    for (int k = 0; k < cnt; k++) {
+      b[k].fa.ymax = pass_g ? b[k].sp.ymax : nullptr;
+      b[k].fa.amax_out = pass_g ? b[k].amax : nullptr;
+      fm.a[k] = b[k].fin(true, false, true);
+      fm.start[k + 1] = fm.start[k] + b[k].p.nblk_rows;
+      b[k].fa.ymax = nullptr;
+      b[k].fa.amax_out = nullptr;
+    }
+    DQ_TRY(launch_finalize_multi(fm, s));
+    if (pass_g)
+      for (int k = 0; k < cnt; k++) {
+        ScaleArgs s2{b[k].amax, b[k].p.m, nullptr, 0.0f, b[k].gs, b[k].io.tensor_scale, b[k].status};
+        DQ_TRY(launch_tensor_scale(s2, s));
+      }
+    for (int k = 0; k < cnt; k++) pm.a[k] = b[k].sp;
+    DQ_TRY(launch_pass_multi(fmt, kModeCol, pm, s));
+    for (int k = 0; k < cnt; k++) {
+      fm.a[k] = b[k].fin(false, true, false);
+      fm.start[k + 1] = fm.start[k] + b[k].p.nblk_cols;
+    }
+    DQ_TRY(launch_finalize_multi(fm, s));
+  }
+  return DQ_OK;
+}
+
 // Re-run the single-sweep pass back to back between one pair of events (after the solve, on
 // its final b; only the workspace's partial sums change) to time the kernel without the
 // per-launch event overhead.
@@ -788,6 +948,83 @@ dq_status dq_quantize_act(const void* X, dq_dtype xt, int64_t tokens, int64_t co
   DQ_TRY(hipMemcpyAsync(host, status, sizeof host, hipMemcpyDeviceToHost, stream));
   DQ_TRY(hipStreamSynchronize(stream));
   return map_status(host[0]);
+}
+
+size_t dq_batch_workspace_bytes(int n, const dq_batch_item* items, dq_format fmt, int group) {
+  if (n < 1 || n > DQ_BATCH_MAX || !items || !fmt_ok(fmt)) return 0;
+  size_t total = 0;
+  for (int k = 0; k < n; k++) {
+    if (!shape_ok(items[k].rows, items[k].cols, group)) return 0;
+    total += align_up(make_plan(items[k].rows, items[k].cols, fmt, group).total);
+  }
+  return total;
+}
+
+dq_status dq_solve_batch(int n, const dq_batch_item* items, dq_dtype wt, dq_format fmt, int group,
+                         int T, unsigned flags, dq_status* item_status, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  using namespace dq;
+  if (n < 1 || n > DQ_BATCH_MAX || !items || T < 0) return DQ_ERR_ARG;
+  if (!fmt_ok(fmt) || wt != DQ_BF16) return DQ_ERR_UNSUPPORTED;
+  const bool pass_g = fmt == DQ_FMT_NVFP4 && (flags & DQ_SOLVE_PER_PASS_G);
+  for (int k = 0; k < n; k++) {
+    const dq_batch_item& it = items[k];
+    dq_status st = check_common(it.W, wt, it.rows, it.cols, fmt, group, it.codes, it.inner_scales);
+    if (st != DQ_OK) return st;
+    if (!it.a || !it.b || !it.mse || (fmt == DQ_FMT_NVFP4 && !it.tensor_scale)) return DQ_ERR_ARG;
+    if (it.g0 != it.g0 || it.g0 > 3.4028234663852886e38f || (pass_g && it.g0 > 0.0f))
+      return DQ_ERR_ARG;
+  }
+  const size_t need = dq_batch_workspace_bytes(n, items, fmt, group);
+  WsGuard ws;
+  if (workspace) {
+    if (workspace_bytes < need) return DQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return DQ_ERR_ARG;
+    ws.ptr = static_cast<char*>(workspace);
+    ws.s = stream;
+  } else {
+    void* ptr = nullptr;
+    DQ_TRY(hipMallocAsync(&ptr, need, stream));
+    ws.ptr = static_cast<char*>(ptr);
+    ws.owned = true;
+    ws.s = stream;
+  }
+  std::vector<BatchMat> mats(n);
+  size_t off = 0;
+  for (int k = 0; k < n; k++) {
+    const dq_batch_item& it = items[k];
+    BatchMat& m = mats[k];
+    m.p = make_plan(it.rows, it.cols, fmt, group);
+    m.ws = ws.ptr + off;
+    off += align_up(m.p.total);
+    m.io = SolveIo{it.W, true, nullptr, it.codes, it.inner_scales, it.tensor_scale, it.a, it.b,
+                   it.mse, T};
+    m.pass_g = pass_g;
+    dq_init init{it.a0, it.b0, it.g0, flags, nullptr};
+    dq_status st = m.setup(&init, stream);
+    if (st != DQ_OK) return st;
+  }
+  for (int t = 0; t < T; t++) {
+    dq_status st = batch_iteration(mats.data(), n, t, stream);
+    if (st != DQ_OK) return st;
+  }
+  for (int k = 0; k < n; k++) {
+    dq_status st = mats[k].emit(stream);
+    if (st != DQ_OK) return st;
+  }
+  // every matrix's status word
+  std::vector<int> host(2 * (size_t)n, 0);
+  for (int k = 0; k < n; k++)
+    DQ_TRY(hipMemcpyAsync(&host[2 * k], mats[k].status, 2 * sizeof(int), hipMemcpyDeviceToHost,
+                          stream));
+  DQ_TRY(hipStreamSynchronize(stream));
+  dq_status first = DQ_OK;
+  for (int k = 0; k < n; k++) {
+    const dq_status st = map_status(host[2 * k]);
+    if (item_status) item_status[k] = st;
+    if (first == DQ_OK) first = st;
+  }
+  return first;
 }
 
 }  // extern "C"

@@ -126,6 +126,21 @@ struct FinArgs {
   float* amax_out;
 };
 
+// Several matrices per launch (a batch solve): workgroups [start[k], start[k+1]) belong to
+// matrix k; the argument blocks travel in the kernel arguments.
+constexpr int kMaxMulti = 16;  // keeps FinMulti (the larger block) under 4 KiB of arguments
+struct PassMulti {
+  int n;
+  int start[kMaxMulti + 1];
+  SweepArgs a[kMaxMulti];
+};
+struct FinMulti {
+  int n;
+  int start[kMaxMulti + 1];
+  FinArgs a[kMaxMulti];
+};
+static_assert(sizeof(FinMulti) <= 4096 && sizeof(PassMulti) <= 4096, "kernel argument size");
+
 // Activation quantization x = fl32(X * b), then Q (dq_act.hip).
 struct ActArgs {
   const void* X;
@@ -156,6 +171,8 @@ hipError_t launch_sweep(int fmt, bool bf16, int mode, const SweepArgs& a, hipStr
 // SweepArgs::nct counts tiles of pass_tile_cols() columns
 hipError_t launch_pass(int fmt, int mode, const SweepArgs& a, hipStream_t s);
 int pass_tile_cols();
+hipError_t launch_pass_multi(int fmt, int mode, const PassMulti& m, hipStream_t s);
+hipError_t launch_finalize_multi(const FinMulti& m, hipStream_t s);
 hipError_t launch_act(int fmt, bool bf16, const ActArgs& a, hipStream_t s);
 hipError_t launch_act_gscale(bool bf16, const ActArgs& a, hipStream_t s);  // amax pass + g
 int act_tile_cols();

@@ -628,16 +628,16 @@ __global__ __launch_bounds__(256) void k_mse_collect(const double* part, int cou
 // taken at, e_i = E_i - 2 a_i N_i + a_i^2 D_i (or the directly summed row error). Per block
 // the row errors are added in a fixed tree order into part_out; the next finalize (or a
 // final collect kernel) adds the block sums in a fixed order.
-__global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
+__device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
   __shared__ double red[256];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && p.prev_out) {
+  if (bid == 0 && p.prev_out) {
     // the previous finalize's per-block error sums (visible across the kernel boundary)
     mse_collect(p.prev_part, p.prev_count, p.prev_out, p.inv_mn, red);
     __syncthreads();
   }
-  if ((int)blockIdx.x < p.nblk_rows) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+  if (bid < p.nblk_rows) {
+    const int64_t i = (int64_t)bid * 256 + tid;
     double err = 0.0;
     int flags = 0;
     if (i < p.m) {
@@ -686,10 +686,10 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
       __syncthreads();
     }
     if (flags) atomicOr(p.status, flags);
-    if (tid == 0 && p.part_out) p.part_out[blockIdx.x] = red[0];
+    if (tid == 0 && p.part_out) p.part_out[bid] = red[0];
   } else {
     // 8 lanes per column: lane s adds partials s, s + 8, ... in order, then a fixed tree
-    const int64_t j = (int64_t)(blockIdx.x - p.nblk_rows) * 32 + tid / 8;
+    const int64_t j = (int64_t)(bid - p.nblk_rows) * 32 + tid / 8;
     const int sub = tid & 7;
     double2 nd = make_double2(0.0, 0.0);
     if (j < p.n) nd = sum_parts(p.colpart + j, p.n, sub, 8, p.nrc);
@@ -707,6 +707,14 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs p) {
     p.b[j] = bn;
     p.rb[j] = recip32(bn);
   }
+}
+
+__global__ __launch_bounds__(256) void k_finalize(FinArgs p) { finalize_block(p, blockIdx.x); }
+
+__global__ __launch_bounds__(256) void k_finalize_multi(FinMulti m) {
+  int k = 0;
+  while (k + 1 < m.n && (int)blockIdx.x >= m.start[k + 1]) k++;
+  finalize_block(m.a[k], (int)blockIdx.x - m.start[k]);
 }
 
 // ------------------------------------------------------------------------------- launchers
@@ -760,6 +768,12 @@ hipError_t launch_tensor_scale(const ScaleArgs& a, hipStream_t s) {
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,
                               hipStream_t s) {
   hipLaunchKernelGGL(k_mse_collect, dim3(1), dim3(256), 0, s, part, count, out, inv_mn);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_multi(const FinMulti& m, hipStream_t s) {
+  if (m.n < 1 || m.n > kMaxMulti) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_finalize_multi, dim3((unsigned)m.start[m.n]), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

@@ -115,10 +115,11 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
   }
 }
 
-// The pass. MODE: kModeRow, kModeCol or kModeRow | kModeEmit (the final Q with the row sums
-// of its error). S: rows per load step. G >= 16; LPG = G / 16 lanes per group.
+// The pass on one workgroup's tile (block `bid` of the matrix's grid). MODE: kModeRow,
+// kModeCol or kModeRow | kModeEmit (the final Q with the row sums of its error), optionally
+// | kModeYmax. S: rows per load step. G >= 16; LPG = G / 16 lanes per group.
 template <int FMT, int G, int MODE, bool PARTIAL, int S>
-__global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
+__device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
   constexpr bool COL = (MODE & kModeCol) != 0;
   constexpr bool EMIT = (MODE & kModeEmit) != 0;
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
   const uint16_t* W = static_cast<const uint16_t*>(p.W);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int ct = blockIdx.x % p.nct;
-  const int rc = blockIdx.x / p.nct;
+  const int ct = bid % p.nct;
+  const int rc = bid / p.nct;
   const int64_t r_begin = (int64_t)rc * p.rpc;
   const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
   const int64_t col = (int64_t)ct * kPassCols + lane * E;
@@ -296,6 +297,19 @@ __global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
   if (flags) atomicOr(p.status, flags);  // rare: only lanes that saw a problem
 }
 
+template <int FMT, int G, int MODE, bool PARTIAL, int S>
+__global__ __launch_bounds__(kBlock) void k_pass(SweepArgs p) {
+  pass_block<FMT, G, MODE, PARTIAL, S>(p, blockIdx.x);
+}
+
+// Several matrices in one launch: workgroups [start[k], start[k+1]) run matrix k's grid.
+template <int FMT, int G, int MODE, bool PARTIAL, int S>
+__global__ __launch_bounds__(kBlock) void k_pass_multi(PassMulti m) {
+  int k = 0;
+  while (k + 1 < m.n && (int)blockIdx.x >= m.start[k + 1]) k++;
+  pass_block<FMT, G, MODE, PARTIAL, S>(m.a[k], (int)blockIdx.x - m.start[k]);
+}
+
 template <int FMT, int G, int MODE>
 static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
   if (a.n % kPassCols != 0)
@@ -303,6 +317,51 @@ static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
   else
     hipLaunchKernelGGL((k_pass<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+
+template <int FMT, int G, int MODE>
+static hipError_t pass_multi_partial(const PassMulti& m, hipStream_t s) {
+  bool partial = false;
+  for (int k = 0; k < m.n; k++) partial |= m.a[k].n % kPassCols != 0;
+  const dim3 grid((unsigned)m.start[m.n]);
+  if (partial)
+    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, true, 2>), grid, dim3(kBlock), 0, s, m);
+  else
+    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, m);
+  return hipGetLastError();
+}
+
+template <int FMT, int MODE>
+static hipError_t pass_multi_group(const PassMulti& m, hipStream_t s) {
+  switch (m.a[0].G) {
+    case 16: return pass_multi_partial<FMT, 16, MODE>(m, s);
+    case 32: return pass_multi_partial<FMT, 32, MODE>(m, s);
+    case 64: return pass_multi_partial<FMT, 64, MODE>(m, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int FMT>
+static hipError_t pass_multi_mode(int mode, const PassMulti& m, hipStream_t s) {
+  switch (mode) {
+    case kModeRow: return pass_multi_group<FMT, kModeRow>(m, s);
+    case kModeCol: return pass_multi_group<FMT, kModeCol>(m, s);
+    case kModeRow | kModeYmax:
+      if constexpr (FMT == kNvFp4) return pass_multi_group<FMT, kModeRow | kModeYmax>(m, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pass_multi(int fmt, int mode, const PassMulti& m, hipStream_t s) {
+  if (m.n < 1 || m.n > kMaxMulti) return hipErrorInvalidValue;
+  switch (fmt) {
+    case kInt4Bf16: return pass_multi_mode<kInt4Bf16>(mode, m, s);
+    case kMxInt4: return pass_multi_mode<kMxInt4>(mode, m, s);
+    case kMxFp4: return pass_multi_mode<kMxFp4>(mode, m, s);
+    case kNvFp4: return pass_multi_mode<kNvFp4>(mode, m, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int FMT, int MODE>

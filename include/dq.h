@@ -191,6 +191,41 @@ dq_status dq_quantize_act_async(const void* X, dq_dtype xt, int64_t tokens, int6
                                 int* status, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------ batch solves
+ * Several matrices of one format solved together, each exactly as dq_solve would solve it
+ * (bit-identical results), with the per-iteration passes and updates of several matrices
+ * sharing each kernel launch (up to 16 per launch): for a decoder layer's q, k, v, o, gate, up and down weights,
+ * whose small matrices alone would leave the GPU idle between launches. bf16 weights only;
+ * every matrix takes the two-sweep path (for MX formats its result equals the single-sweep
+ * path's). */
+#define DQ_BATCH_MAX 64
+
+typedef struct {
+  const void* W;         /* device, rows x cols bf16, 16-byte aligned */
+  int64_t rows, cols;
+  const float* a0;       /* device or NULL, as dq_init.a0 */
+  const float* b0;       /* device or NULL, as dq_init.b0 */
+  float g0;              /* NVFP4, as dq_init.g0 */
+  uint8_t* codes;        /* out, as for dq_solve */
+  void* inner_scales;    /* out */
+  float* tensor_scale;   /* out, NVFP4 */
+  float* a;              /* out, rows */
+  float* b;              /* out, cols */
+  double* mse;           /* out, T+1 */
+} dq_batch_item;
+
+/* Bytes of device workspace for dq_solve_batch (0 on invalid arguments). */
+size_t dq_batch_workspace_bytes(int n, const dq_batch_item* items, dq_format fmt, int group);
+
+/* Solve n (1..DQ_BATCH_MAX) matrices. flags: DQ_SOLVE_PER_PASS_G (NVFP4) as for dq_solve.
+ * item_status (host, n entries, may be NULL) receives each matrix's status; the return value
+ * is the first non-OK one. workspace: as for dq_solve, of dq_batch_workspace_bytes bytes.
+ * Arguments are checked on the host before anything is enqueued; the call synchronizes
+ * `stream` before returning. */
+dq_status dq_solve_batch(int n, const dq_batch_item* items, dq_dtype wt, dq_format fmt, int group,
+                         int T, unsigned flags, dq_status* item_status, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Static string for a status code. */
 const char* dq_status_str(dq_status status);
 

@@ -30,8 +30,9 @@ def dqlib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["dq_act_workspace_bytes", "dq_quantize", "dq_quantize_act",
-                     "dq_quantize_act_async", "dq_solve", "dq_status_str", "dq_workspace_bytes"]
+    assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_quantize",
+                     "dq_quantize_act", "dq_quantize_act_async", "dq_solve", "dq_solve_batch",
+                     "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(dqlib):
@@ -125,3 +126,19 @@ def test_act_arguments_are_rejected_on_the_host(dqlib):
     assert call_async(status=None) == 1
     assert call_async(status=ctypes.c_void_p(0x1002)) == 1
     assert call_async(codes=ctypes.c_void_p(0x1004)) == 1
+
+
+def test_batch_arguments_are_rejected_on_the_host(dqlib):
+    L = dqlib._batch_lib()
+    fake = 0x1000
+    item = dqlib._BatchItem(fake, 128, 256, None, None, 0.0, fake, fake, fake, fake, fake, fake)
+    items = (dqlib._BatchItem * 1)(item)
+    assert L.dq_solve_batch(0, items, 1, 2, 32, 4, 0, None, None, 0, None) == 1  # n
+    assert L.dq_solve_batch(1, items, 0, 2, 32, 4, 0, None, None, 0, None) == 2  # fp32 W
+    assert L.dq_solve_batch(1, items, 1, 2, 48, 4, 0, None, None, 0, None) == 1  # group
+    assert L.dq_solve_batch(1, items, 1, 2, 32, -1, 0, None, None, 0, None) == 1  # T
+    bad = (dqlib._BatchItem * 1)(dqlib._BatchItem(fake, 128, 250, None, None, 0.0, fake, fake,
+                                                  fake, fake, fake, fake))
+    assert L.dq_solve_batch(1, bad, 1, 2, 32, 4, 0, None, None, 0, None) == 1  # cols % group
+    assert dqlib.batch_workspace_bytes([(128, 256), (64, 512)], "mxfp4", 32) > 0
+    assert dqlib.batch_workspace_bytes([(128, 250)], "mxfp4", 32) == 0

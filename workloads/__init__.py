@@ -160,9 +160,11 @@ CONFIG5_MATRICES: Tuple[Tuple[str, int, int, str], ...] = (
 )
 
 
-def config5_layer(layer: int, scale_down: int = 1) -> List[Workload]:
-    """The seven matrices of decoder layer ``layer``. ``scale_down`` > 1 divides
-    every dimension (for oracle-sized test cases); outlier counts stay 0.5%."""
+def config5_layer(layer: int, scale_down: int = 1,
+                  only: Optional[Tuple[str, ...]] = None) -> List[Workload]:
+    """The seven matrices of decoder layer ``layer`` (or those named in ``only``; each
+    matrix has its own stream, so a subset draws the same values). ``scale_down`` > 1
+    divides every dimension (for oracle-sized test cases); outlier counts stay 0.5%."""
     orng = rng_for(5, layer, 99)
     spaces = {}
     for space, width in (("hidden", 4096), ("attn_out", 4096), ("mlp_inner", 14336)):
@@ -171,6 +173,8 @@ def config5_layer(layer: int, scale_down: int = 1) -> List[Workload]:
         spaces[space] = outlier_multipliers(orng, w, count, 20.0, None)
     out = []
     for mi, (name, r, c, space) in enumerate(CONFIG5_MATRICES):
+        if only is not None and name not in only:
+            continue
         r //= scale_down
         c //= scale_down
         rng = rng_for(5, layer, mi)
