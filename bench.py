@@ -37,7 +37,7 @@ COUNTERS = {
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
     "fetch_kib": 57469.0, "fetch_scale": 2.0,
     "write_kib": 7584.0, "write_scale": 1.0,
-    "sources_sha256": "bb88646c6695f6f20f957dea8a194dab1dea64764e11810ddee49c07939306f9",
+    "sources_sha256": "a8f1e6bb6c539da504b8ed5675bf3d50cd3b70736bd1ed0c8eba02793db5ddde",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
