@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.dq_ref_quantize_act.argtypes = [P, I, I64, I64, I, I, P, P, P, P]
         L.dq_ref_solve_pass_g.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, P, P]
         L.dq_ref_solve_pass_g.restype = I
+        L.dq_ref_gemm_mx.argtypes = [P, P, I64, I64, P, P, I64, P, P]
+        L.dq_ref_gemm_mx.restype = I
         L.dq_ref_quantize_act.restype = I
         L.dq_ref_solve.argtypes = [P, I, I64, I64, I, I, I, P, P, F, P, P, P, P, P, P]
         L.dq_ref_solve.restype = I
@@ -133,6 +135,24 @@ def quantize_act(X: np.ndarray, dtype: str, fmt: str, group: int, b=None,
     if st:
         raise OracleError(st)
     return {"codes": codes, "scales": scales, "g": float(gbuf[0])}
+
+
+def gemm_mx(act_codes, act_scales, w_codes, w_scales, a=None) -> np.ndarray:
+    """W4A4 product of MXFP4 activations and weights (codes and E8M0 scales as the quantizers
+    return them) with the weights' row scales a: tokens x out float64."""
+    act_codes = np.ascontiguousarray(act_codes, np.uint8)
+    act_scales = np.ascontiguousarray(act_scales, np.uint8)
+    w_codes = np.ascontiguousarray(w_codes, np.uint8)
+    w_scales = np.ascontiguousarray(w_scales, np.uint8)
+    tokens, K = act_codes.shape[0], act_codes.shape[1] * 2
+    out = w_codes.shape[0]
+    a = None if a is None else np.ascontiguousarray(a, np.float32)
+    Y = np.zeros((tokens, out), np.float64)
+    st = lib().dq_ref_gemm_mx(_ptr(act_codes), _ptr(act_scales), tokens, K, _ptr(w_codes),
+                              _ptr(w_scales), out, _ptr(a), _ptr(Y))
+    if st:
+        raise OracleError(st)
+    return Y
 
 
 def solve_pass_g(W: np.ndarray, dtype: str, group: int, T: int, a0=None,

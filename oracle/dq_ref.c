@@ -549,6 +549,40 @@ done:
   return st;
 }
 
+/* --------------------------------------------------------- public: the W4A4 product */
+
+/* The product the quantized weights serve (daiwk notes, "核心公式" eq. 1: X W^T ~=
+ * (X D_beta^-1) Qhat^T D_alpha^-1 = (X D_b) Qhat^T D_a; the flowchart's last step: the matmul
+ * of the quantized activations with the weight codes, then the row output scale): with
+ * MXFP4 activations x^ = Q(X D_b) (tokens x K) and weights Qhat = codes * 2^(e) (out x K),
+ * Y[t][i] = a_i * sum_k x^[t][k] Qhat[i][k], summed in double in ascending k. An E8M0 byte
+ * 0xFF is the format's NaN (OCP MX v1.0, E8M0) and makes its block's terms NaN. */
+static double e8m0_value(uint8_t s) { return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127); }
+
+int dq_ref_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                   int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int64_t out,
+                   const float* a, double* Y) {
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return DQR_ERR_ARG;
+  if (tokens <= 0 || out <= 0 || K <= 0 || K % 32 != 0) return DQR_ERR_ARG;
+  if (a && !positive_finite(a, out)) return DQR_ERR_ARG;
+  const int64_t kb = K / 32;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int64_t t = 0; t < tokens; t++) {
+    for (int64_t i = 0; i < out; i++) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        const uint8_t cx = act_codes[(t * K + k) / 2], cw = w_codes[(i * K + k) / 2];
+        const int nx = (k & 1) ? (cx >> 4) : (cx & 0xF), nw = (k & 1) ? (cw >> 4) : (cw & 0xF);
+        const double vx = (nx & 8 ? -1.0 : 1.0) * E2M1_GRID[nx & 7];
+        const double vw = (nw & 8 ? -1.0 : 1.0) * E2M1_GRID[nw & 7];
+        acc += vx * e8m0_value(act_scales[t * kb + k / 32]) * vw * e8m0_value(w_scales[i * kb + k / 32]);
+      }
+      Y[t * out + i] = acc * (a ? (double)a[i] : 1.0);
+    }
+  }
+  return DQR_OK;
+}
+
 /* ----------------------------------------------------------------- public: the solver */
 
 /* NVFP4 with a per-pass tensor scale: g from the scaled tile about to be quantized */

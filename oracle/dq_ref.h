@@ -66,6 +66,14 @@ int dq_ref_quantize(const void* W, int wt, int64_t rows, int64_t cols, int fmt, 
 int dq_ref_quantize_act(const void* X, int xt, int64_t tokens, int64_t cols, int fmt, int group,
                         const float* b, float* g_inout, uint8_t* codes, void* scales);
 
+/* The W4A4 product of MXFP4 activations (codes tokens x K/2 bytes, E8M0 scales tokens x K/32)
+ * and MXFP4 weights (codes out x K/2, scales out x K/32) with the weights' row scales a (out
+ * floats > 0, or NULL for ones): Y[t][i] = a_i * sum_k xhat[t][k] Qhat[i][k] (tokens x out
+ * doubles), the sum in double in ascending k. K % 32 == 0. */
+int dq_ref_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                   int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int64_t out,
+                   const float* a, double* Y);
+
 /* T iterations of the block-coordinate descent. a0/b0: NULL means ones, else
  * projected onto the format's scale set first; g0 > 0 fixes the NVFP4 tensor
  * scale, g0 <= 0 computes it from the initial scaled tile. Outputs: final codes
