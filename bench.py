@@ -122,6 +122,9 @@ def main() -> None:
                          "instead of one solve per matrix")
     ap.add_argument("--per-pass-g", action="store_true",
                     help="NVFP4 workloads: recompute the tensor scale before every Q pass")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the W4A4 MXFP4 product (dq_gemm_mx) on the Llama-3.1-8B MLP "
+                         "up / down shapes at 8192 tokens instead of the solver")
     ap.add_argument("--act", action="store_true",
                     help="measure the activation quantizer instead (x = X b, then Q) on the "
                          "Llama-3.1-8B MLP inputs of 8192 tokens; prints its own JSON line")
@@ -150,6 +153,9 @@ def main() -> None:
 
     import dual_scale_w4a4_amd as dq
 
+    if args.gemm:
+        bench_gemm(args, dq)
+        return
     if args.act:
         bench_act(args, dq)
         return
@@ -386,6 +392,97 @@ def bench_act(args, dq) -> None:
         "cpu_baseline": {"value": Xs.size / dt, "unit": "activation elements / s", "cores": 1,
                          "kind": "oracle", "sample": "the whole 8192x4096 input, MXFP4 G32",
                          "seconds": dt, "gpu_identical_on_sample": same},
+    }
+    print(json.dumps(line), flush=True)
+
+
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
+
+
+def bench_gemm(args, dq) -> None:
+    """The W4A4 product on the chain it serves: the Llama-3.1-8B MLP up (14336x4096) and down
+    (4096x14336) weights solved on the GPU (MXFP4 G32, T = 20), the MLP inputs of 8192 tokens
+    quantized with the solver's b, and a step = both products Y = (xhat Qhat^T) D_a, bf16 out.
+    Kernel time: back-to-back calls between one pair of HIP events on the calling stream, and
+    each product alone the same way. Algorithmic flops: 2 * tokens * out * K per product."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    stream = torch.cuda.current_stream()
+    mats = []
+    for w, name in zip(workloads.full(3), ("up", "down")):
+        sol = dq.solve(to_device(w.W, w.dtype), "mxfp4", 32, w.T)
+        X, b = workloads.act_inputs(name)
+        act = dq.quantize_act(to_device(X, "bf16"), "mxfp4", 32, sol["b"])
+        del X
+        tokens, K = act["codes"].shape[0], act["codes"].shape[1] * 2
+        out = sol["codes"].shape[0]
+        y = torch.empty((tokens, out), dtype=torch.bfloat16, device="cuda")
+        mats.append(dict(name=name, xc=act["codes"], xs=act["scales"], wc=sol["codes"],
+                         ws=sol["scales"], a=sol["a"], y=y, flops=2.0 * tokens * out * K,
+                         shape=(tokens, out, K)))
+
+    def run(ms_list):
+        for m in ms_list:
+            dq.gemm_mx(m["xc"], m["xs"], m["wc"], m["ws"], m["a"], out_dtype="bf16", y=m["y"],
+                       stream=stream)
+
+    def timed(ms_list, steps):
+        for _ in range(args.warmup):
+            run(ms_list)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            run(ms_list)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(mats, args.steps)
+    flops = sum(m["flops"] for m in mats)
+    per = {}
+    for m in mats:
+        t = timed([m], args.steps)
+        per[m["name"]] = {"shape_tokens_out_k": m["shape"], "ms": t,
+                          "tflops": m["flops"] / (t * 1e-3) / 1e12,
+                          "frac": m["flops"] / (t * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
+    tf = flops / (ms * 1e-3) / 1e12
+    # the CPU oracle on a bounded sample: 256 tokens of the up product, every output channel
+    import oracle
+
+    m = mats[0]
+    ts = np.arange(256)
+    xc, xs = m["xc"][ts].cpu().numpy(), m["xs"][ts].cpu().numpy()
+    wc, ws, a = m["wc"].cpu().numpy(), m["ws"].cpu().numpy(), m["a"].cpu().numpy()
+    threads = oracle.set_threads(min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ref = oracle.gemm_mx(xc, xs, wc, ws, a)
+    dt = time.perf_counter() - t0
+    oracle.set_threads(1)
+    got = m["y"][ts].float().cpu().numpy().astype(np.float64)
+    rel = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)))
+    sample_flops = 2.0 * len(ts) * wc.shape[0] * xc.shape[1] * 2
+    line = {
+        "metric": "W4A4 MXFP4 product TFLOP/s (dense-equivalent), % FP4 matrix-core peak",
+        "value": tf, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp4 (E2M1 x E2M1, E8M0 block scales, fp32 accumulate)",
+        "data": "synthetic (seeded generators in workloads/), weights and activations "
+                "quantized on the GPU by the solver and the activation quantizer",
+        "config": {"workload": "llama3.1-8b MLP at 8192 tokens: up 8192x4096 x (14336x4096)^T "
+                               "+ down 8192x14336 x (4096x14336)^T, MXFP4 G32, bf16 out"},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_mx", "achieved": tf,
+                     "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP4_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "timing": "back-to-back asynchronous calls between one pair of events"},
+        "products": per,
+        "cpu_baseline": {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                         "kind": "oracle",
+                         "sample": "256 tokens x 14336 channels x K=4096 of the up product",
+                         "seconds": dt, "gpu_max_rel_err_on_sample_bf16": rel},
     }
     print(json.dumps(line), flush=True)
 

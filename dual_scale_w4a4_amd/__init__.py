@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.dq_quantize_act_async.argtypes = [P, I, I64, I64, I, I, P, ctypes.c_float, P, P, P, P,
                                             P, SZ, P]
         L.dq_quantize_act_async.restype = I
+        L.dq_gemm_mx.argtypes = [P, P, I64, I64, P, P, P, I64, I, P, P]
+        L.dq_gemm_mx.restype = I
         L.dq_status_str.argtypes = [I]
         L.dq_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -234,6 +236,34 @@ def quantize_act_async(X, fmt: str, group: int, codes, scales, status, b=None, g
                                      _stream(stream))
     if st != 0:
         raise DQError(st, "dq_quantize_act_async")
+
+
+def gemm_mx(act_codes, act_scales, w_codes, w_scales, a=None, out_dtype: str = "bf16", y=None,
+            stream=None):
+    """dq_gemm_mx: Y = (xhat Qhat^T) D_a from MXFP4 activation codes / E8M0 scales (tokens x
+    K/2, tokens x K/32 uint8, as quantize_act returns them) and weight codes / scales (out x
+    K/2, out x K/32, as solve returns them) on the MX-scaled FP4 matrix cores. Returns Y
+    (tokens x out, bfloat16 or float32), into ``y`` when given."""
+    torch = _torch()
+    tokens, out = act_codes.shape[0], w_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    for t, shape in ((act_codes, (tokens, K // 2)), (act_scales, (tokens, K // 32)),
+                     (w_codes, (out, K // 2)), (w_scales, (out, K // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"expected a contiguous CUDA uint8 tensor of shape {shape}")
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
+    if y is None:
+        y = torch.empty((tokens, out), dtype=dt, device=act_codes.device)
+    elif y.dtype != dt or tuple(y.shape) != (tokens, out) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tokens x out tensor of the output dtype")
+    if a is not None and (a.dtype != torch.float32 or a.numel() != out or not a.is_contiguous()):
+        raise ValueError("a must be a contiguous float32 vector of the output channels")
+    st = lib().dq_gemm_mx(act_codes.data_ptr(), act_scales.data_ptr(), tokens, K,
+                          w_codes.data_ptr(), w_scales.data_ptr(), _ptr(a), out,
+                          DTYPE[out_dtype], y.data_ptr(), _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_gemm_mx")
+    return y
 
 
 class _BatchItem(ctypes.Structure):

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libdq.so")
-SOURCES = ["dq_kernels.hip", "dq_pass.hip", "dq_act.hip", "dq_api.hip"]
+SOURCES = ["dq_kernels.hip", "dq_pass.hip", "dq_act.hip", "dq_gemm.hip", "dq_api.hip"]
 ARCH = os.environ.get("DQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,405 @@
+// dq_gemm.hip -- the W4A4 product that the dual-scale weights are for, on gfx950's MX-scaled
+// FP4 matrix cores.
+//
+// What it computes (daiwk notes, "核心公式" eq. 1: X W^T ~= (X D_b) Qhat^T D_a; the flowchart
+// ends in the matmul of the quantized activations with the weight codes, then the row output
+// scale): with MXFP4 activations x^ = Q(X D_b) (tokens x K codes and E8M0 block scales, as the
+// activation quantizer writes them) and MXFP4 weights Qhat (out x K codes and E8M0 block
+// scales, as the solver writes them),
+//     Y[t][i] = a_i * sum_k x^[t][k] * Qhat[i][k],
+// with every product exact (E2M1 x E2M1 times two powers of two), the sum in the matrix
+// cores' fp32 accumulators, and a_i applied in the epilogue. Neither operand is ever
+// expanded: both stay 4-bit from HBM to the matrix cores, and their E8M0 bytes are the
+// instructions' block scales as they are.
+//
+// Tiling: a workgroup of four waves owns a 256 (weight rows) x 256 (tokens) tile of Y; each
+// wave a 128 x 128 quarter as 4 x 4 V_MFMA_SCALE_F32_32X32X64_F8F6F4 blocks (256 fp32
+// accumulators per lane). The weights are the instruction's A operand and the tokens its B
+// operand, so that a lane's 16 results of one block hold 4 runs of 4 consecutive output
+// channels of one token: the epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes at a time.
+// K runs in stages of 256 (128 code bytes per row): both operands' stages go through LDS,
+// double-buffered, loaded one stage ahead into registers with buffer loads (rows past the end
+// read as zero); in LDS a row's eight 16-byte chunks are XOR-swizzled so that neither the
+// stores nor the operand reads (a lane reads one 16-byte chunk of its row) conflict. Block
+// scales go from global memory straight to registers, one stage ahead.
+//
+// Operand layouts of the scaled MFMA (checked exactly on gfx950): lane l holds row l % 32 of
+// A (column l % 32 of B) for the 32 k values (l / 32) * 32 .. + 31 of the 64-k step, as four
+// dwords with value e in nibble e % 8 of dword e / 8 (low nibble first: the packed code
+// layout), and its scale byte applies to those 32 values; result v of lane l is
+// D[(v / 4) * 8 + (l / 32) * 4 + v % 4][l % 32].
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/dq.h"
+
+namespace dqg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 256;                   // weight rows (output channels) per workgroup
+constexpr int kBN = 256;                   // tokens per workgroup
+constexpr int kBK = 256;                   // k per stage
+constexpr int kRowB = kBK / 2;             // code bytes of one row in a stage (8 chunks)
+constexpr int kTileB = kBM * kRowB;        // 32 KiB: one operand's stage
+constexpr int kThreads = 256;
+constexpr int kGroupM = 4;                 // weight tiles per tile group (L2 reuse)
+constexpr uint32_t kBufRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+struct GemmArgs {
+  const uint8_t* xc;  // tokens x K/2
+  const uint8_t* xs;  // tokens x K/32
+  const uint8_t* wc;  // out x K/2
+  const uint8_t* ws;  // out x K/32
+  const float* a;     // out, or null
+  void* y;            // tokens x ldy
+  int tokens, out, K;
+  int64_t ldy;
+  int nti, ntt;
+};
+
+// Chunk position of chunk c (0..7) of LDS row r: conflict-free for eight lanes on eight
+// consecutive rows (one 128-byte bank sweep) and for sixteen (a 256-byte one).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           (int)kBufRsrcWord3);
+}
+
+// One operand's stage: 256 rows x 128 bytes, thread tid loads chunk tid % 8 of rows
+// tid / 8 + 32 j. The per-thread part of the offset is one register; the row step 32 j and
+// the stage go in the wave-uniform offset. Rows past the operand's end (and, on a partial last
+// stage, chunks past K) take an offset beyond any buffer and read zero.
+constexpr uint32_t kOob = 0x80000000u;
+
+template <bool FULLK>
+__device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, int row0, int rows,
+                                           int ldb, int kb0, int tid, u32x4 (&v)[8]) {
+  const int c = tid & 7, r0 = tid >> 3;
+  const uint32_t vbase = (uint32_t)(row0 + r0) * (uint32_t)ldb + (uint32_t)(c * 16);
+  const bool kin = FULLK || kb0 + c * 16 < ldb;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const bool in = kin && row0 + r0 + 32 * j < rows;
+    v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? vbase : kOob,
+                                                 (uint32_t)(32 * j * ldb + kb0), 0);
+  }
+}
+
+__device__ __forceinline__ void store_stage(uint8_t* lds, int tid, const u32x4 (&v)[8]) {
+  const int c = tid & 7;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int r = (tid >> 3) + 32 * j;
+    *reinterpret_cast<u32x4*>(lds + r * kRowB + swz(r, c) * 16) = v[j];
+  }
+}
+
+// Block scales of one row for one stage. FULLK (K % 256 == 0): the stage's 8 bytes of the
+// row, loaded raw in one aligned load and unpacked only when the stage is stored, so that the
+// load stays in flight during the previous stage's products. `voff` is the row's offset (or
+// kOob past the end), `soff` the uniform rest.
+__device__ __forceinline__ u32x2 load_scales_raw(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                 uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+}
+
+// The four scale bytes lane `lane` uses in a stage: byte ks is the scale of k block
+// 8 s + 2 ks + lane / 32 (the lane's half of k step ks). Rows past the end give 127 (2^0;
+// their codes are zero).
+__device__ __forceinline__ uint32_t unpack_scales(u32x2 w, bool in_rows, int lane) {
+  const uint64_t v = (((uint64_t)w[1] << 32) | w[0]) >> (8 * (lane >> 5));
+  const uint32_t out = (uint32_t)(v & 0xFFu) | (uint32_t)((v >> 8) & 0xFF00u) |
+                       (uint32_t)((v >> 16) & 0xFF0000u) | (uint32_t)((v >> 24) & 0xFF000000u);
+  return in_rows ? out : 0x7F7F7F7Fu;
+}
+
+// The same for any K % 32 == 0, byte by byte (blocks past K also give 127).
+__device__ __forceinline__ uint32_t load_scales_bytes(const uint8_t* sp, int row, int rows,
+                                                      int nkb, int s, int lane) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    const int kb = 8 * s + 2 * ks + (lane >> 5);
+    const uint32_t b = (row < rows && kb < nkb) ? sp[(int64_t)row * nkb + kb] : 127u;
+    out |= b << (8 * ks);
+  }
+  return out;
+}
+
+// 16 scaled MFMAs of one k step: fa / fb the lane's chunks of the four weight-row and four
+// token blocks, sw / sx the packed scale bytes.
+__device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const u32x4 (&fa)[4],
+                                          const u32x4 (&fb)[4], const uint32_t (&sw)[4],
+                                          const uint32_t (&sx)[4], int ks) {
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const v8i A = {(int)fa[m][0], (int)fa[m][1], (int)fa[m][2], (int)fa[m][3], 0, 0, 0, 0};
+    const int sa = (int)((sw[m] >> (8 * ks)) & 0xFFu);
+#pragma unroll
+    for (int n = 0; n < 4; n++) {
+      const v8i B = {(int)fb[n][0], (int)fb[n][1], (int)fb[n][2], (int)fb[n][3], 0, 0, 0, 0};
+      const int sb = (int)((sx[n] >> (8 * ks)) & 0xFFu);
+      acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[m][n], 4, 4, 0, sa,
+                                                                  0, sb);
+    }
+  }
+}
+
+__device__ __forceinline__ void read_frags(const uint8_t* lw, const uint8_t* lx, int co,
+                                           u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    fa[m] = *reinterpret_cast<const u32x4*>(lw + m * 32 * kRowB + co);
+    fb[m] = *reinterpret_cast<const u32x4*>(lx + m * 32 * kRowB + co);
+  }
+}
+
+// The stage's 64 products of one wave: four k steps of 16, the next step's operand reads
+// issued before this step's products. The scheduling barriers keep that order.
+__device__ __forceinline__ void stage_products(v16f (&acc)[4][4], const uint8_t* lw,
+                                               const uint8_t* lx, int sterm,
+                                               const uint32_t (&sw)[4], const uint32_t (&sx)[4]) {
+  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  read_frags(lw, lx, (0 ^ sterm) * 16, fa0, fb0);
+  read_frags(lw, lx, (2 ^ sterm) * 16, fa1, fb1);
+  mfma_step(acc, fa0, fb0, sw, sx, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(lw, lx, (4 ^ sterm) * 16, fa0, fb0);
+  mfma_step(acc, fa1, fb1, sw, sx, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(lw, lx, (6 ^ sterm) * 16, fa1, fb1);
+  mfma_step(acc, fa0, fb0, sw, sx, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(acc, fa1, fb1, sw, sx, 3);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One 256 x 256 tile. EDGE: the tile reaches past the last weight row or token (row checks on
+// loads and stores); otherwise every row is inside and no check is made.
+template <bool BF16, bool FULLK, bool VECY, bool EDGE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, int i0, int t0,
+                                          uint8_t (&lds)[2][2][kTileB]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
+  const int ldb = p.K / 2, nkb = p.K / 32;
+  const int nst = (p.K + kBK - 1) / kBK;
+  const int rows_w = EDGE ? p.out : INT32_MAX, rows_x = EDGE ? p.tokens : INT32_MAX;
+
+  const __amdgpu_buffer_rsrc_t rwc = rsrc(p.wc, (uint32_t)p.out * (uint32_t)ldb);
+  const __amdgpu_buffer_rsrc_t rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
+  const __amdgpu_buffer_rsrc_t rws = rsrc(p.ws, (uint32_t)p.out * (uint32_t)nkb);
+  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[m][n] = v16f{};
+
+  const int rl = lane & 31;
+  const uint32_t sbw = (uint32_t)(i0 + wi + rl) * (uint32_t)nkb;  // scale row offsets
+  const uint32_t sbx = (uint32_t)(t0 + wt + rl) * (uint32_t)nkb;
+  u32x4 vw[8], vx[8];
+  uint32_t sw[4], sx[4];
+  u32x2 rsw[4], rsx[4];
+
+  // stage s's loads: codes into vw / vx, scales raw into rsw / rsx (FULLK) or packed into
+  // sw / sx directly (byte path)
+  auto issue = [&](int s) {
+    load_stage<FULLK>(rwc, i0, rows_w, ldb, s * kRowB, tid, vw);
+    load_stage<FULLK>(rxc, t0, rows_x, ldb, s * kRowB, tid, vx);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int iw = i0 + wi + m * 32 + rl, it = t0 + wt + m * 32 + rl;
+      if (FULLK) {
+        rsw[m] = load_scales_raw(rws, iw < rows_w ? sbw : kOob, m * 32 * nkb + s * 8);
+        rsx[m] = load_scales_raw(rxs, it < rows_x ? sbx : kOob, m * 32 * nkb + s * 8);
+      }
+    }
+  };
+  auto commit = [&](int s, int buf) {
+    store_stage(lds[buf][0], tid, vw);
+    store_stage(lds[buf][1], tid, vx);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int iw = i0 + wi + m * 32 + rl, it = t0 + wt + m * 32 + rl;
+      if (FULLK) {
+        sw[m] = unpack_scales(rsw[m], iw < rows_w, lane);
+        sx[m] = unpack_scales(rsx[m], it < rows_x, lane);
+      } else {
+        sw[m] = load_scales_bytes(p.ws, iw, p.out, nkb, s, lane);
+        sx[m] = load_scales_bytes(p.xs, it, p.tokens, nkb, s, lane);
+      }
+    }
+  };
+
+  issue(0);
+  commit(0, 0);
+  __syncthreads();
+
+  // per-lane LDS read offsets: row wi + m * 32 + lane % 32 (its swizzle term depends on the
+  // lane only), chunk 2 ks + lane / 32
+  const int sterm = (rl & 7) ^ ((rl >> 3) & 1) ^ (lane >> 5);
+  const uint8_t* lw0 = &lds[0][0][(wi + rl) * kRowB];
+  const uint8_t* lx0 = &lds[0][1][(wt + rl) * kRowB];
+  constexpr int kBufB = 2 * kTileB;
+
+  // stages 0 .. nst - 2: the next stage's loads go out first and stay in flight during this
+  // stage's products, then go to the other buffer; the last stage has no successor
+  for (int s = 0; s + 1 < nst; s++) {
+    const int buf = s & 1;
+    issue(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_products(acc, lw0 + buf * kBufB, lx0 + buf * kBufB, sterm, sw, sx);
+    commit(s + 1, buf ^ 1);
+    __syncthreads();
+  }
+  stage_products(acc, lw0 + ((nst - 1) & 1) * kBufB, lx0 + ((nst - 1) & 1) * kBufB, sterm, sw,
+                 sx);
+
+  // epilogue: result v of block (m, n) is output channel i0 + wi + 32 m + 8 (v / 4) +
+  // 4 (lane / 32) + v % 4 of token t0 + wt + 32 n + lane % 32
+  const int ib = i0 + wi + (lane >> 5) * 4;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const int i = ib + m * 32 + g * 8;
+      const bool vec = VECY && (!EDGE || i < p.out);
+      f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (p.a) {
+        if (vec) {
+          av = *reinterpret_cast<const f32x4*>(p.a + i);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) av[e] = i + e < p.out ? p.a[i + e] : 1.0f;
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        const int t = t0 + wt + n * 32 + rl;
+        if (EDGE && t >= p.tokens) continue;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; e++) y[e] = acc[m][n][g * 4 + e] * av[e];
+        if (BF16) {
+          __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + i;
+          if (vec) {
+            const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+            *reinterpret_cast<bf16x4*>(yp) = hv;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (i + e < p.out) yp[e] = (__bf16)y[e];
+          }
+        } else {
+          float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + i;
+          if (vec) {
+            *reinterpret_cast<f32x4*>(yp) = y;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (i + e < p.out) yp[e] = y[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool BF16, bool FULLK, bool VECY>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileB];  // [buffer][W, X]
+
+  // Tile order: workgroups are dealt round-robin to the eight XCDs, so consecutive ids are
+  // spread; give each XCD a contiguous range of tiles, and order tiles in groups of kGroupM
+  // weight tiles by every token tile, so that the workgroups running together on one XCD
+  // share weight and token stages in its L2.
+  const int ntiles = p.nti * p.ntt;
+  const int bid = blockIdx.x;
+  const int full = (ntiles / 8) * 8;
+  const int L = bid < full ? (bid % 8) * (ntiles / 8) + bid / 8 : bid;
+  const int gsz = kGroupM * p.ntt;
+  const int first = (L / gsz) * kGroupM;
+  const int gm = min(p.nti - first, kGroupM);
+  const int ti = first + (L % gsz) % gm;
+  const int tt = (L % gsz) / gm;
+  const int i0 = ti * kBM, t0 = tt * kBN;
+  if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
+    gemm_tile<BF16, FULLK, VECY, false>(p, i0, t0, lds);
+  else
+    gemm_tile<BF16, FULLK, VECY, true>(p, i0, t0, lds);
+}
+
+template <bool BF16, bool FULLK, bool VECY>
+hipError_t launch_t(const GemmArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_mx<BF16, FULLK, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch(const GemmArgs& p, bool bf16, bool fullk, bool vecy, hipStream_t s) {
+  if (bf16) {
+    if (fullk) return vecy ? launch_t<true, true, true>(p, s) : launch_t<true, true, false>(p, s);
+    return vecy ? launch_t<true, false, true>(p, s) : launch_t<true, false, false>(p, s);
+  }
+  if (fullk) return vecy ? launch_t<false, true, true>(p, s) : launch_t<false, true, false>(p, s);
+  return vecy ? launch_t<false, false, true>(p, s) : launch_t<false, false, false>(p, s);
+}
+
+}  // namespace dqg
+
+extern "C" {
+
+dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                     int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, const float* a,
+                     int64_t out, dq_dtype yt, void* Y, hipStream_t stream) {
+  using namespace dqg;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return DQ_ERR_ARG;
+  if (tokens < 1 || out < 1 || K < 32 || K % 32 != 0) return DQ_ERR_ARG;
+  if (yt != DQ_F32 && yt != DQ_BF16) return DQ_ERR_UNSUPPORTED;
+  if (((uintptr_t)act_codes & 15u) || ((uintptr_t)w_codes & 15u) || ((uintptr_t)a & 15u))
+    return DQ_ERR_ARG;
+  // per launch, every buffer offset stays below 2^31: tokens (and output channels) are
+  // split into chunks of whole tiles that keep it so
+  const int64_t ldb = K / 2, nkb = K / 32;
+  if (ldb * (kBM + 1) > (int64_t(1) << 30)) return DQ_ERR_ARG;  // K <= 2^22
+  const int64_t lim = (int64_t(1) << 31) - ldb * (kBM + 1);
+  const int64_t tchunk = std::max<int64_t>(kBN, (lim / ldb) / kBN * kBN);
+  const int64_t ochunk = std::max<int64_t>(kBM, (lim / ldb) / kBM * kBM);
+  const bool bf16 = yt == DQ_BF16;
+  const size_t esz = bf16 ? 2 : 4;
+  const bool fullk = K % kBK == 0 && ((uintptr_t)act_scales & 7u) == 0 &&
+                     ((uintptr_t)w_scales & 7u) == 0;
+  const bool vecy = out % 4 == 0 && ((uintptr_t)Y & (4 * esz - 1)) == 0;
+  for (int64_t tb = 0; tb < tokens; tb += tchunk) {
+    for (int64_t ob = 0; ob < out; ob += ochunk) {
+      GemmArgs p{};
+      p.xc = act_codes + tb * ldb;
+      p.xs = act_scales + tb * nkb;
+      p.wc = w_codes + ob * ldb;
+      p.ws = w_scales + ob * nkb;
+      p.a = a ? a + ob : nullptr;
+      p.y = static_cast<char*>(Y) + (size_t)(tb * out + ob) * esz;
+      p.tokens = (int)std::min(tchunk, tokens - tb);
+      p.out = (int)std::min(ochunk, out - ob);
+      p.K = (int)K;
+      p.ldy = out;
+      p.nti = (p.out + kBM - 1) / kBM;
+      p.ntt = (p.tokens + kBN - 1) / kBN;
+      if (launch(p, bf16, fullk, vecy, stream) != hipSuccess) return DQ_ERR_HIP;
+    }
+  }
+  return DQ_OK;
+}
+
+}  // extern "C"

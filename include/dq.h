@@ -226,6 +226,29 @@ dq_status dq_solve_batch(int n, const dq_batch_item* items, dq_dtype wt, dq_form
                          int T, unsigned flags, dq_status* item_status, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ the W4A4 product
+ * The matmul the quantized weights are for (daiwk notes, "核心公式" eq. 1: X W^T ~=
+ * (X D_b) Qhat^T D_a; the flowchart's last step multiplies the quantized activations by the
+ * weight codes and applies the row output scale): MXFP4 activations as dq_quantize_act writes
+ * them (codes and E8M0 scales of x = X * b, group 32) times MXFP4 weights as dq_solve writes
+ * them (codes and E8M0 scales of Qhat), with the weights' row scales a on the output:
+ *     Y[t][i] = a_i * sum_k xhat[t][k] * Qhat[i][k]
+ * on gfx950's MX-scaled FP4 matrix cores: both operands stay 4-bit, every product is exact and
+ * the sum is accumulated in fp32.
+ *  act_codes:  tokens x K/2 bytes, packed as above, 16-byte aligned.
+ *  act_scales: tokens x K/32 E8M0 bytes.
+ *  w_codes:    out x K/2 bytes, 16-byte aligned.  w_scales: out x K/32 E8M0 bytes.
+ *  a:          out floats, 16-byte aligned, or NULL for ones.
+ *  Y:          out, tokens x out, row-major, fp32 or bf16 (yt; bf16 rounds to nearest even).
+ * K % 32 == 0 and K <= 2^22; any tokens, out >= 1. The fast path wants K % 256 == 0,
+ * out % 4 == 0, 8-byte aligned scales and Y aligned to 4 elements; other shapes take a
+ * slower path with the same results. An E8M0 byte 0xFF (the format's NaN) makes the outputs
+ * it reaches NaN. Arguments are checked on the host; the call only enqueues on `stream`
+ * (there is no device-side error to report) and returns. */
+dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                     int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, const float* a,
+                     int64_t out, dq_dtype yt, void* Y, hipStream_t stream);
+
 /* Static string for a status code. */
 const char* dq_status_str(dq_status status);
 

@@ -30,9 +30,9 @@ def dqlib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_quantize",
-                     "dq_quantize_act", "dq_quantize_act_async", "dq_solve", "dq_solve_batch",
-                     "dq_status_str", "dq_workspace_bytes"]
+    assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_gemm_mx",
+                     "dq_quantize", "dq_quantize_act", "dq_quantize_act_async", "dq_solve",
+                     "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(dqlib):
@@ -126,6 +126,31 @@ def test_act_arguments_are_rejected_on_the_host(dqlib):
     assert call_async(status=None) == 1
     assert call_async(status=ctypes.c_void_p(0x1002)) == 1
     assert call_async(codes=ctypes.c_void_p(0x1004)) == 1
+
+
+def test_gemm_arguments_are_rejected_on_the_host(dqlib):
+    L = dqlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
+    args = dict(xc=fake, xs=fake, tokens=64, K=256, wc=fake, ws=fake, a=None, out=128, yt=1,
+                Y=fake)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dq_gemm_mx(a["xc"], a["xs"], a["tokens"], a["K"], a["wc"], a["ws"], a["a"],
+                            a["out"], a["yt"], a["Y"], None)
+
+    assert call(xc=None) == 1
+    assert call(ws=None) == 1
+    assert call(Y=None) == 1
+    assert call(tokens=0) == 1
+    assert call(out=0) == 1
+    assert call(K=48) == 1                           # not a whole number of 32-blocks
+    assert call(K=0) == 1
+    assert call(K=2 ** 23) == 1                      # beyond the 32-bit offset budget
+    assert call(yt=5) == 2
+    assert call(xc=ctypes.c_void_p(0x1008)) == 1     # codes not 16-byte aligned
+    assert call(wc=ctypes.c_void_p(0x1004)) == 1
+    assert call(a=ctypes.c_void_p(0x1004)) == 1      # a not 16-byte aligned
 
 
 def test_batch_arguments_are_rejected_on_the_host(dqlib):

@@ -244,3 +244,17 @@ def act_inputs(name: str) -> Tuple[np.ndarray, np.ndarray]:
     cols = {"up": 4096, "down": 14336}[name]
     seed = {"up": 1, "down": 2}[name]
     return activations(8192, cols, seed), act_column_scales(cols, seed)
+
+
+MX_CFG = 7  # seed-stream id of the packed MXFP4 operands
+
+
+def mx_operands(rows: int, K: int, seed: int = 0, lo: int = 120, hi: int = 135,
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """Packed MXFP4 operands for the W4A4 product: rows x K/2 code bytes with every nibble
+    uniform over the 16 E2M1 codes (both zeros included), and rows x K/32 E8M0 block-scale
+    bytes uniform in [lo, hi) (the band a unit-scale tensor's blocks fall in)."""
+    rng = rng_for(MX_CFG, rows, seed)
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(lo, hi, size=(rows, K // 32), dtype=np.uint8)
+    return codes, scales
