@@ -164,6 +164,62 @@ __device__ __forceinline__ void read_frags(const uint8_t* lw, const uint8_t* lx,
   }
 }
 
+// The epilogue: result v of block (m, n) of the wave is output channel i0 + wi + 32 m +
+// 8 (v / 4) + 4 (lane / 32) + v % 4 of token t0 + wt + 32 n + lane % 32; a lane stores its four
+// consecutive channels at once, times their a.
+template <bool BF16, bool VECY, bool EDGE>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f (&acc)[4][4], int i0,
+                                           int t0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rl = lane & 31;
+  const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
+  const int ib = i0 + wi + (lane >> 5) * 4;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const int i = ib + m * 32 + g * 8;
+      const bool vec = VECY && (!EDGE || i < p.out);
+      f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (p.a) {
+        if (vec) {
+          av = *reinterpret_cast<const f32x4*>(p.a + i);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) av[e] = i + e < p.out ? p.a[i + e] : 1.0f;
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        const int t = t0 + wt + n * 32 + rl;
+        if (EDGE && t >= p.tokens) continue;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; e++) y[e] = acc[m][n][g * 4 + e] * av[e];
+        if (BF16) {
+          __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + i;
+          if (vec) {
+            const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+            *reinterpret_cast<bf16x4*>(yp) = hv;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (i + e < p.out) yp[e] = (__bf16)y[e];
+          }
+        } else {
+          float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + i;
+          if (vec) {
+            *reinterpret_cast<f32x4*>(yp) = y;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (i + e < p.out) yp[e] = y[e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // The stage's 64 products of one wave: four k steps of 16, the next step's operand reads
 // issued before this step's products. The scheduling barriers keep that order.
 __device__ __forceinline__ void stage_products(v16f (&acc)[4][4], const uint8_t* lw,
@@ -267,64 +323,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int i0, int t0,
   stage_products(acc, lw0 + ((nst - 1) & 1) * kBufB, lx0 + ((nst - 1) & 1) * kBufB, sterm, sw,
                  sx);
 
-  // epilogue: result v of block (m, n) is output channel i0 + wi + 32 m + 8 (v / 4) +
-  // 4 (lane / 32) + v % 4 of token t0 + wt + 32 n + lane % 32
-  const int ib = i0 + wi + (lane >> 5) * 4;
-#pragma unroll
-  for (int m = 0; m < 4; m++) {
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const int i = ib + m * 32 + g * 8;
-      const bool vec = VECY && (!EDGE || i < p.out);
-      f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (p.a) {
-        if (vec) {
-          av = *reinterpret_cast<const f32x4*>(p.a + i);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; e++) av[e] = i + e < p.out ? p.a[i + e] : 1.0f;
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const int t = t0 + wt + n * 32 + rl;
-        if (EDGE && t >= p.tokens) continue;
-        f32x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; e++) y[e] = acc[m][n][g * 4 + e] * av[e];
-        if (BF16) {
-          __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + i;
-          if (vec) {
-            const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-            *reinterpret_cast<bf16x4*>(yp) = hv;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              if (i + e < p.out) yp[e] = (__bf16)y[e];
-          }
-        } else {
-          float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + i;
-          if (vec) {
-            *reinterpret_cast<f32x4*>(yp) = y;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              if (i + e < p.out) yp[e] = y[e];
-          }
-        }
-      }
-    }
-  }
+  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0);
 }
 
-template <bool BF16, bool FULLK, bool VECY>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileB];  // [buffer][W, X]
-
-  // Tile order: workgroups are dealt round-robin to the eight XCDs, so consecutive ids are
-  // spread; give each XCD a contiguous range of tiles, and order tiles in groups of kGroupM
-  // weight tiles by every token tile, so that the workgroups running together on one XCD
-  // share weight and token stages in its L2.
+// Tile order: workgroups are dealt round-robin to the eight XCDs, so consecutive ids are
+// spread; give each XCD a contiguous range of tiles, and order tiles in groups of kGroupM
+// weight tiles by every token tile, so that the workgroups running together on one XCD share
+// weight and token stages in its L2.
+__device__ __forceinline__ void tile_origin(const GemmArgs& p, int& i0, int& t0) {
   const int ntiles = p.nti * p.ntt;
   const int bid = blockIdx.x;
   const int full = (ntiles / 8) * 8;
@@ -332,13 +338,189 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(GemmArgs p) {
   const int gsz = kGroupM * p.ntt;
   const int first = (L / gsz) * kGroupM;
   const int gm = min(p.nti - first, kGroupM);
-  const int ti = first + (L % gsz) % gm;
-  const int tt = (L % gsz) / gm;
-  const int i0 = ti * kBM, t0 = tt * kBN;
+  i0 = (first + (L % gsz) % gm) * kBM;
+  t0 = ((L % gsz) / gm) * kBN;
+}
+
+template <bool BF16, bool FULLK, bool VECY>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileB];  // [buffer][W, X]
+
+  int i0, t0;
+  tile_origin(p, i0, t0);
   if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
     gemm_tile<BF16, FULLK, VECY, false>(p, i0, t0, lds);
   else
     gemm_tile<BF16, FULLK, VECY, true>(p, i0, t0, lds);
+}
+
+// ------------------------------------------------------------ fast path: K % 512 == 0
+// The same tile, with both operands' stages moved from global memory straight into LDS by
+// gfx950's buffer loads to LDS (no registers, no LDS stores: one wave instruction fills 1 KiB
+// of LDS, lane j its 16 bytes at j * 16), so the 4 x 4 fragments of the next k step can be read
+// a whole step ahead. The block scales go through LDS as well: every second stage each row's
+// next 16 scale bytes (two stages' worth, one cache line shared by the 16 k blocks) are
+// loaded once for the workgroup, instead of 8 bytes per stage by every wave that uses the row.
+constexpr int kScaleRowB = 16;                        // scale bytes per row per period
+constexpr int kScaleTileB = kBM * kScaleRowB;         // 4 KiB per operand per period
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+struct DmaLds {
+  uint8_t codes[2][2][kTileB];              // [buffer][W, X]: 128 KiB
+  uint8_t scales[2][2][kScaleTileB];        // [period parity][W, X]: 16 KiB
+};
+
+// One operand's stage into LDS. Wave w fills rows 64 w .. 64 w + 63, 8 rows (1 KiB) per
+// instruction: lane j writes LDS row 8 g + j / 8 at chunk position j % 8, which holds the
+// row's logical chunk (j % 8) ^ swizzle term, so the global read of 8 lanes is one 128-byte
+// row segment. Rows past the end (EDGE) read zero.
+template <bool EDGE>
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int row0,
+                                          int rows, int ldb, int kb0, int wave, int lane) {
+  const int lr = lane >> 3;
+  const uint32_t rbase = (uint32_t)(row0 + wave * 64 + lr) * (uint32_t)ldb;
+  // logical chunk for even and odd groups (the swizzle term flips with bit 3 of the row)
+  const uint32_t ve = rbase + (uint32_t)(((lane & 7) ^ lr) * 16);
+  const uint32_t vo = rbase + (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    uint32_t v = (j & 1) ? vo : ve;
+    if (EDGE && row0 + wave * 64 + j * 8 + lr >= rows) v = kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_ptr_t)(dst + (wave * 8 + j) * 1024), 16, (int)v,
+        (int)(uint32_t)(j * 8 * ldb + kb0), 0, 0);
+  }
+}
+
+// The next 16 scale bytes of the operand's 256 rows (period q: k blocks 16 q .. 16 q + 15)
+// into LDS, row r at r * 16: wave w loads rows 64 w .. 64 w + 63.
+template <bool EDGE>
+__device__ __forceinline__ void dma_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int row0,
+                                           int rows, int nkb, int q, int wave, int lane) {
+  const int r = row0 + wave * 64 + lane;
+  const uint32_t v = (EDGE && r >= rows) ? kOob : (uint32_t)r * (uint32_t)nkb;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + wave * 1024), 16, (int)v,
+                                           (int)(uint32_t)(q * 16), 0, 0);
+}
+
+// The packed scale bytes of one row for stage s from its period's LDS copy (see
+// unpack_scales: byte ks is k block 8 s + 2 ks + lane / 32).
+__device__ __forceinline__ uint32_t lds_scales(const uint8_t* row16, int s, int lane) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(row16 + (s & 1) * 8);
+  return unpack_scales(w, true, lane);
+}
+
+template <bool BF16, bool VECY, bool EDGE>
+__device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, int i0, int t0, DmaLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
+  const int ldb = p.K / 2, nkb = p.K / 32;
+  const int nst = p.K / kBK;  // even: K % 512 == 0
+  const int rows_w = EDGE ? p.out : INT32_MAX, rows_x = EDGE ? p.tokens : INT32_MAX;
+
+  const __amdgpu_buffer_rsrc_t rwc = rsrc(p.wc, (uint32_t)p.out * (uint32_t)ldb);
+  const __amdgpu_buffer_rsrc_t rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
+  const __amdgpu_buffer_rsrc_t rws = rsrc(p.ws, (uint32_t)p.out * (uint32_t)nkb);
+  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[m][n] = v16f{};
+
+  const int rl = lane & 31;
+  const int sterm = (rl & 7) ^ ((rl >> 3) & 1) ^ (lane >> 5);
+  const int rw = (wi + rl) * kRowB, rx = (wt + rl) * kRowB;  // fragment row offsets
+  const int sw_off = (wi + rl) * kScaleRowB, sx_off = (wt + rl) * kScaleRowB;
+
+  // descriptors that read nothing: the loads of the stage after the last one go there (the
+  // loop body stays one basic block, so nothing can move across its barriers)
+  const __amdgpu_buffer_rsrc_t rnone = rsrc(p.wc, 0u);
+
+  // prologue: stage 0 and the scales of period 0 (stages 0 and 1)
+  dma_stage<EDGE>(rwc, L.codes[0][0], i0, rows_w, ldb, 0, wave, lane);
+  dma_stage<EDGE>(rxc, L.codes[0][1], t0, rows_x, ldb, 0, wave, lane);
+  dma_scales<EDGE>(rws, L.scales[0][0], i0, rows_w, nkb, 0, wave, lane);
+  dma_scales<EDGE>(rxs, L.scales[0][1], t0, rows_x, nkb, 0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  uint32_t sw[4], sx[4];
+  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto stage_scales = [&](int par, int half) {
+    const uint8_t* bw = L.scales[par][0];
+    const uint8_t* bx = L.scales[par][1];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      sw[m] = lds_scales(bw + sw_off + m * 32 * kScaleRowB, half, lane);
+      sx[m] = lds_scales(bx + sx_off + m * 32 * kScaleRowB, half, lane);
+    }
+  };
+  // the 64 products of the stage in buffer `buf`, fa0 / fb0 holding its first k step
+  auto products = [&](int buf) {
+    const uint8_t* lw = L.codes[buf][0] + rw;
+    const uint8_t* lx = L.codes[buf][1] + rx;
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(lw, lx, (2 ^ sterm) * 16, fa1, fb1);
+    mfma_step(acc, fa0, fb0, sw, sx, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(lw, lx, (4 ^ sterm) * 16, fa0, fb0);
+    mfma_step(acc, fa1, fb1, sw, sx, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(lw, lx, (6 ^ sterm) * 16, fa1, fb1);
+    mfma_step(acc, fa0, fb0, sw, sx, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, fa1, fb1, sw, sx, 3);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // every wave's loads are in LDS after this
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  stage_scales(0, 0);
+  read_frags(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+
+  // two stages (one scale period) per trip: stage 2 q from buffer 0, stage 2 q + 1 from
+  // buffer 1; each stage's successor goes out before its products
+  for (int q = 0; q < nst / 2; q++) {
+    const bool more = 2 * q + 2 < nst;
+    const int par = q & 1;
+    dma_stage<EDGE>(rwc, L.codes[1][0], i0, rows_w, ldb, (2 * q + 1) * kRowB, wave, lane);
+    dma_stage<EDGE>(rxc, L.codes[1][1], t0, rows_x, ldb, (2 * q + 1) * kRowB, wave, lane);
+    dma_scales<EDGE>(more ? rws : rnone, L.scales[par ^ 1][0], i0, rows_w, nkb, q + 1, wave,
+                     lane);
+    dma_scales<EDGE>(more ? rxs : rnone, L.scales[par ^ 1][1], t0, rows_x, nkb, q + 1, wave,
+                     lane);
+    products(0);
+    publish();
+    stage_scales(par, 1);
+    read_frags(L.codes[1][0] + rw, L.codes[1][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+
+    dma_stage<EDGE>(more ? rwc : rnone, L.codes[0][0], i0, rows_w, ldb, (2 * q + 2) * kRowB,
+                    wave, lane);
+    dma_stage<EDGE>(more ? rxc : rnone, L.codes[0][1], t0, rows_x, ldb, (2 * q + 2) * kRowB,
+                    wave, lane);
+    products(1);
+    publish();
+    stage_scales(par ^ 1, 0);
+    read_frags(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+  }
+  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0);
+}
+
+template <bool BF16, bool VECY>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_dma(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) DmaLds lds;
+  int i0, t0;
+  tile_origin(p, i0, t0);
+  if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
+    gemm_tile_dma<BF16, VECY, false>(p, i0, t0, lds);
+  else
+    gemm_tile_dma<BF16, VECY, true>(p, i0, t0, lds);
 }
 
 template <bool BF16, bool FULLK, bool VECY>
@@ -347,7 +529,18 @@ hipError_t launch_t(const GemmArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch(const GemmArgs& p, bool bf16, bool fullk, bool vecy, hipStream_t s) {
+template <bool BF16, bool VECY>
+hipError_t launch_dma_t(const GemmArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_mx_dma<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch(const GemmArgs& p, bool bf16, bool fullk, bool dma, bool vecy,
+                  hipStream_t s) {
+  if (dma) {
+    if (bf16) return vecy ? launch_dma_t<true, true>(p, s) : launch_dma_t<true, false>(p, s);
+    return vecy ? launch_dma_t<false, true>(p, s) : launch_dma_t<false, false>(p, s);
+  }
   if (bf16) {
     if (fullk) return vecy ? launch_t<true, true, true>(p, s) : launch_t<true, true, false>(p, s);
     return vecy ? launch_t<true, false, true>(p, s) : launch_t<true, false, false>(p, s);
@@ -381,6 +574,9 @@ dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_
   const bool fullk = K % kBK == 0 && ((uintptr_t)act_scales & 7u) == 0 &&
                      ((uintptr_t)w_scales & 7u) == 0;
   const bool vecy = out % 4 == 0 && ((uintptr_t)Y & (4 * esz - 1)) == 0;
+  // the fast path loads 16 scale bytes per row at a time: K % 512 == 0, 16-byte aligned scales
+  const bool dma = K % (2 * kBK) == 0 && ((uintptr_t)act_scales & 15u) == 0 &&
+                   ((uintptr_t)w_scales & 15u) == 0;
   for (int64_t tb = 0; tb < tokens; tb += tchunk) {
     for (int64_t ob = 0; ob < out; ob += ochunk) {
       GemmArgs p{};
@@ -396,7 +592,7 @@ dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_
       p.ldy = out;
       p.nti = (p.out + kBM - 1) / kBM;
       p.ntt = (p.tokens + kBN - 1) / kBN;
-      if (launch(p, bf16, fullk, vecy, stream) != hipSuccess) return DQ_ERR_HIP;
+      if (launch(p, bf16, fullk, dma, vecy, stream) != hipSuccess) return DQ_ERR_HIP;
     }
   }
   return DQ_OK;
