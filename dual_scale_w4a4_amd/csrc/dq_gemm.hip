@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/dq.h"
 
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(GemmArgs p) {
 // The same tile, with both operands' stages moved from global memory straight into LDS by
 // gfx950's buffer loads to LDS (no registers, no LDS stores: one wave instruction fills 1 KiB
 // of LDS, lane j its 16 bytes at j * 16), so the 4 x 4 fragments of the next k step can be read
-// a whole step ahead. The block scales go through LDS as well: every second stage each row's
+// a whole step ahead, and every load sits between two matrix instructions. The block scales go through LDS as well: every second stage each row's
 // next 16 scale bytes (two stages' worth, one cache line shared by the 16 k blocks) are
 // loaded once for the workgroup, instead of 8 bytes per stage by every wave that uses the row.
 constexpr int kScaleRowB = 16;                        // scale bytes per row per period
@@ -371,58 +372,146 @@ struct DmaLds {
   uint8_t scales[2][2][kScaleTileB];        // [period parity][W, X]: 16 KiB
 };
 
-// One operand's stage into LDS. Wave w fills rows 64 w .. 64 w + 63, 8 rows (1 KiB) per
-// instruction: lane j writes LDS row 8 g + j / 8 at chunk position j % 8, which holds the
-// row's logical chunk (j % 8) ^ swizzle term, so the global read of 8 lanes is one 128-byte
-// row segment. Rows past the end (EDGE) read zero.
-template <bool EDGE>
-__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int row0,
-                                          int rows, int ldb, int kb0, int wave, int lane) {
-  const int lr = lane >> 3;
-  const uint32_t rbase = (uint32_t)(row0 + wave * 64 + lr) * (uint32_t)ldb;
-  // logical chunk for even and odd groups (the swizzle term flips with bit 3 of the row)
-  const uint32_t ve = rbase + (uint32_t)(((lane & 7) ^ lr) * 16);
-  const uint32_t vo = rbase + (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    uint32_t v = (j & 1) ? vo : ve;
-    if (EDGE && row0 + wave * 64 + j * 8 + lr >= rows) v = kOob;
+// One row's scales for stage s from its period's LDS copy, as two dwords whose bytes 0 and 2
+// are the k blocks 8 s + 2 ks + lane / 32 of k steps ks = 0, 1 (first dword) and 2, 3
+// (second): the matrix instruction picks the byte by its operand select.
+__device__ __forceinline__ u32x2 lds_scales2(const uint8_t* row16, int s, int lane) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(row16 + (s & 1) * 8);
+  const uint64_t v = (((uint64_t)w[1] << 32) | w[0]) >> (8 * (lane >> 5));
+  return u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
+}
+
+template <int KS>
+__device__ __forceinline__ void mfma_one(v16f& acc, const u32x4& fa, const u32x4& fb,
+                                         const u32x2& sa, const u32x2& sb) {
+  const v8i A = {(int)fa[0], (int)fa[1], (int)fa[2], (int)fa[3], 0, 0, 0, 0};
+  const v8i B = {(int)fb[0], (int)fb[1], (int)fb[2], (int)fb[3], 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, (KS & 1) * 2,
+                                                        (int)sa[KS >> 1], (KS & 1) * 2,
+                                                        (int)sb[KS >> 1]);
+}
+
+// Per-wave state of the fast-path tile loop.
+struct DmaCtx {
+  __amdgpu_buffer_rsrc_t rwc, rxc, rws, rxs, rnone;
+  int i0, t0, rows_w, rows_x, ldb, nkb, wave, lane;
+  uint32_t vw[2], vx[2];  // code offsets of this lane's rows for even / odd groups
+  uint32_t sbw, sbx;      // scale offsets of this lane's rows (or kOob)
+};
+
+// Load number L (0..17) of the loads that fill a stage: 0..7 the weight rows' groups,
+// 8..15 the tokens', 16 / 17 the weight / token scales of period q (when `scales`).
+template <bool EDGE, int L>
+__device__ __forceinline__ void dma_one(const DmaCtx& c, DmaLds& lds, int buf, int kb0,
+                                        bool codes_on, int q, bool scales_on) {
+  if (L < 16) {
+    constexpr int op = L / 8, j = L % 8;
+    const int lr = c.lane >> 3;
+    uint32_t v = op == 0 ? c.vw[j & 1] : c.vx[j & 1];
+    if (EDGE && (op == 0 ? c.i0 : c.t0) + c.wave * 64 + j * 8 + lr >= (op == 0 ? c.rows_w : c.rows_x))
+      v = kOob;
+    const __amdgpu_buffer_rsrc_t rs = codes_on ? (op == 0 ? c.rwc : c.rxc) : c.rnone;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (lds_ptr_t)(dst + (wave * 8 + j) * 1024), 16, (int)v,
-        (int)(uint32_t)(j * 8 * ldb + kb0), 0, 0);
+        rs, (lds_ptr_t)(lds.codes[buf][op] + (c.wave * 8 + j) * 1024), 16, (int)v,
+        (int)(uint32_t)(j * 8 * c.ldb + kb0), 0, 0);
+  } else {
+    constexpr int op = L - 16;
+    const __amdgpu_buffer_rsrc_t rs = scales_on ? (op == 0 ? c.rws : c.rxs) : c.rnone;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_ptr_t)(lds.scales[q & 1][op] + c.wave * 1024), 16,
+        (int)(op == 0 ? c.sbw : c.sbx), (int)(uint32_t)(q * 16), 0, 0);
   }
 }
 
-// The next 16 scale bytes of the operand's 256 rows (period q: k blocks 16 q .. 16 q + 15)
-// into LDS, row r at r * 16: wave w loads rows 64 w .. 64 w + 63.
-template <bool EDGE>
-__device__ __forceinline__ void dma_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int row0,
-                                           int rows, int nkb, int q, int wave, int lane) {
-  const int r = row0 + wave * 64 + lane;
-  const uint32_t v = (EDGE && r >= rows) ? kOob : (uint32_t)r * (uint32_t)nkb;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + wave * 1024), 16, (int)v,
-                                           (int)(uint32_t)(q * 16), 0, 0);
+// Fragment reads in the order the products use them: A0, B0..B3, A1..A3.
+__device__ __forceinline__ void read_frags_ordered(const uint8_t* lw, const uint8_t* lx, int co,
+                                                   u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+  fa[0] = *reinterpret_cast<const u32x4*>(lw + co);
+#pragma unroll
+  for (int n = 0; n < 4; n++) fb[n] = *reinterpret_cast<const u32x4*>(lx + n * 32 * kRowB + co);
+#pragma unroll
+  for (int m = 1; m < 4; m++) fa[m] = *reinterpret_cast<const u32x4*>(lw + m * 32 * kRowB + co);
 }
 
-// The packed scale bytes of one row for stage s from its period's LDS copy (see
-// unpack_scales: byte ks is k block 8 s + 2 ks + lane / 32).
-__device__ __forceinline__ uint32_t lds_scales(const uint8_t* row16, int s, int lane) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(row16 + (s & 1) * 8);
-  return unpack_scales(w, true, lane);
+// k step KS of a stage: its 16 products in the order (m, n), the next step's 8 fragment reads
+// (KS < 3) and up to 8 of the next stage's NL loads (16: codes only; 18: codes and a scale
+// period) placed between them, one instruction group at a time so that the matrix pipe never
+// waits behind a batch of other work. A load that reads nothing still writes its (zero)
+// bytes to LDS, so loads a stage does not need are not issued at all.
+template <bool EDGE, int KS, int NL>
+__device__ __forceinline__ void kstep(v16f (&acc)[4][4], const u32x4 (&fa)[4],
+                                      const u32x4 (&fb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
+                                      const uint8_t* lw, const uint8_t* lx, int sterm,
+                                      const u32x2 (&sw)[4], const u32x2 (&sx)[4],
+                                      const DmaCtx& c, DmaLds& lds, int nbuf, int kb0,
+                                      bool codes_on, int q, bool scales_on) {
+  const int co = ((2 * (KS + 1)) ^ sterm) * 16;
+#pragma unroll
+  for (int t = 0; t < 16; t++) {
+    const int m = t / 4, n = t % 4;
+    mfma_one<KS>(acc[m][n], fa[m], fb[n], sw[m], sx[n]);
+    if (KS < 3 && t % 2 == 0) {  // next step's fragment t / 2 (A0, B0..B3, A1..A3)
+      const int f = t / 2;
+      if (f == 0) na[0] = *reinterpret_cast<const u32x4*>(lw + co);
+      else if (f <= 4) nb[f - 1] = *reinterpret_cast<const u32x4*>(lx + (f - 1) * 32 * kRowB + co);
+      else na[f - 4] = *reinterpret_cast<const u32x4*>(lw + (f - 4) * 32 * kRowB + co);
+    }
+    if (KS < 3 && t % 2 == 1 && KS * 8 + t / 2 < NL) {
+      // loads KS * 8 + t / 2; the compiler folds the switch (everything is unrolled)
+      switch (KS * 8 + t / 2) {
+#define DQ_DMA_CASE(x) \
+  case x: dma_one<EDGE, x>(c, lds, nbuf, kb0, codes_on, q, scales_on); break;
+        DQ_DMA_CASE(0) DQ_DMA_CASE(1) DQ_DMA_CASE(2) DQ_DMA_CASE(3) DQ_DMA_CASE(4)
+        DQ_DMA_CASE(5) DQ_DMA_CASE(6) DQ_DMA_CASE(7) DQ_DMA_CASE(8) DQ_DMA_CASE(9)
+        DQ_DMA_CASE(10) DQ_DMA_CASE(11) DQ_DMA_CASE(12) DQ_DMA_CASE(13) DQ_DMA_CASE(14)
+        DQ_DMA_CASE(15) DQ_DMA_CASE(16) DQ_DMA_CASE(17)
+#undef DQ_DMA_CASE
+        default: break;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <bool BF16, bool VECY, bool EDGE>
 __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, int i0, int t0, DmaLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
   const int ldb = p.K / 2, nkb = p.K / 32;
   const int nst = p.K / kBK;  // even: K % 512 == 0
-  const int rows_w = EDGE ? p.out : INT32_MAX, rows_x = EDGE ? p.tokens : INT32_MAX;
 
-  const __amdgpu_buffer_rsrc_t rwc = rsrc(p.wc, (uint32_t)p.out * (uint32_t)ldb);
-  const __amdgpu_buffer_rsrc_t rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
-  const __amdgpu_buffer_rsrc_t rws = rsrc(p.ws, (uint32_t)p.out * (uint32_t)nkb);
-  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+  DmaCtx c;
+  c.rwc = rsrc(p.wc, (uint32_t)p.out * (uint32_t)ldb);
+  c.rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
+  c.rws = rsrc(p.ws, (uint32_t)p.out * (uint32_t)nkb);
+  c.rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+  // a descriptor that reads nothing: the loads of the stage after the last go there (the loop
+  // body stays one basic block, so nothing can move across its barriers)
+  c.rnone = rsrc(p.wc, 0u);
+  c.i0 = i0;
+  c.t0 = t0;
+  c.rows_w = EDGE ? p.out : INT32_MAX;
+  c.rows_x = EDGE ? p.tokens : INT32_MAX;
+  c.ldb = ldb;
+  c.nkb = nkb;
+  c.wave = wave;
+  c.lane = lane;
+  {
+    // lane j of a load writes LDS row 8 g + j / 8 at chunk position j % 8, which holds the
+    // row's logical chunk (j % 8) ^ swizzle term (the term's bit 3 part flips with g)
+    const int lr = lane >> 3;
+    const uint32_t bw = (uint32_t)(i0 + wave * 64 + lr) * (uint32_t)ldb;
+    const uint32_t bx = (uint32_t)(t0 + wave * 64 + lr) * (uint32_t)ldb;
+    const uint32_t ce = (uint32_t)(((lane & 7) ^ lr) * 16), co = (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
+    c.vw[0] = bw + ce;
+    c.vw[1] = bw + co;
+    c.vx[0] = bx + ce;
+    c.vx[1] = bx + co;
+    const int rw = i0 + wave * 64 + lane, rx = t0 + wave * 64 + lane;
+    c.sbw = (EDGE && rw >= p.out) ? kOob : (uint32_t)rw * (uint32_t)nkb;
+    c.sbx = (EDGE && rx >= p.tokens) ? kOob : (uint32_t)rx * (uint32_t)nkb;
+  }
 
   v16f acc[4][4];
 #pragma unroll
@@ -435,79 +524,69 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, int i0, int t0,
   const int rw = (wi + rl) * kRowB, rx = (wt + rl) * kRowB;  // fragment row offsets
   const int sw_off = (wi + rl) * kScaleRowB, sx_off = (wt + rl) * kScaleRowB;
 
-  // descriptors that read nothing: the loads of the stage after the last one go there (the
-  // loop body stays one basic block, so nothing can move across its barriers)
-  const __amdgpu_buffer_rsrc_t rnone = rsrc(p.wc, 0u);
-
-  // prologue: stage 0 and the scales of period 0 (stages 0 and 1)
-  dma_stage<EDGE>(rwc, L.codes[0][0], i0, rows_w, ldb, 0, wave, lane);
-  dma_stage<EDGE>(rxc, L.codes[0][1], t0, rows_x, ldb, 0, wave, lane);
-  dma_scales<EDGE>(rws, L.scales[0][0], i0, rows_w, nkb, 0, wave, lane);
-  dma_scales<EDGE>(rxs, L.scales[0][1], t0, rows_x, nkb, 0, wave, lane);
+  // prologue: stage 0 into buffer 0 and the scales of period 0
+  dma_one<EDGE, 0>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 1>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 2>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 3>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 4>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 5>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 6>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 7>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 8>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 9>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 10>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 11>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 12>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 13>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 14>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 15>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 16>(c, L, 0, 0, true, 0, true);
+  dma_one<EDGE, 17>(c, L, 0, 0, true, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  uint32_t sw[4], sx[4];
+  u32x2 sw[4], sx[4];
   u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
   auto stage_scales = [&](int par, int half) {
     const uint8_t* bw = L.scales[par][0];
     const uint8_t* bx = L.scales[par][1];
 #pragma unroll
     for (int m = 0; m < 4; m++) {
-      sw[m] = lds_scales(bw + sw_off + m * 32 * kScaleRowB, half, lane);
-      sx[m] = lds_scales(bx + sx_off + m * 32 * kScaleRowB, half, lane);
+      sw[m] = lds_scales2(bw + sw_off + m * 32 * kScaleRowB, half, lane);
+      sx[m] = lds_scales2(bx + sx_off + m * 32 * kScaleRowB, half, lane);
     }
   };
-  // the 64 products of the stage in buffer `buf`, fa0 / fb0 holding its first k step
-  auto products = [&](int buf) {
+  // the stage in buffer `buf` (fa0 / fb0 holding its first k step), the next stage's loads
+  // into buffer nbuf between its products
+  auto stage = [&](auto nl, int buf, int nbuf, int kb0, bool codes_on, int q, bool scales_on) {
+    constexpr int NL = decltype(nl)::value;
     const uint8_t* lw = L.codes[buf][0] + rw;
     const uint8_t* lx = L.codes[buf][1] + rx;
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(lw, lx, (2 ^ sterm) * 16, fa1, fb1);
-    mfma_step(acc, fa0, fb0, sw, sx, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(lw, lx, (4 ^ sterm) * 16, fa0, fb0);
-    mfma_step(acc, fa1, fb1, sw, sx, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(lw, lx, (6 ^ sterm) * 16, fa1, fb1);
-    mfma_step(acc, fa0, fb0, sw, sx, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(acc, fa1, fb1, sw, sx, 3);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // every wave's loads are in LDS after this
-  auto publish = [&]() {
+    kstep<EDGE, 0, NL>(acc, fa0, fb0, fa1, fb1, lw, lx, sterm, sw, sx, c, L, nbuf, kb0, codes_on, q, scales_on);
+    kstep<EDGE, 1, NL>(acc, fa1, fb1, fa0, fb0, lw, lx, sterm, sw, sx, c, L, nbuf, kb0, codes_on, q, scales_on);
+    kstep<EDGE, 2, NL>(acc, fa0, fb0, fa1, fb1, lw, lx, sterm, sw, sx, c, L, nbuf, kb0, codes_on, q, scales_on);
+    kstep<EDGE, 3, NL>(acc, fa1, fb1, fa0, fb0, lw, lx, sterm, sw, sx, c, L, nbuf, kb0, codes_on, q, scales_on);
+    // every wave's loads are in LDS after this
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
   stage_scales(0, 0);
-  read_frags(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+  read_frags_ordered(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
 
   // two stages (one scale period) per trip: stage 2 q from buffer 0, stage 2 q + 1 from
-  // buffer 1; each stage's successor goes out before its products
+  // buffer 1; the scales of period q + 1 load during stage 2 q
   for (int q = 0; q < nst / 2; q++) {
     const bool more = 2 * q + 2 < nst;
     const int par = q & 1;
-    dma_stage<EDGE>(rwc, L.codes[1][0], i0, rows_w, ldb, (2 * q + 1) * kRowB, wave, lane);
-    dma_stage<EDGE>(rxc, L.codes[1][1], t0, rows_x, ldb, (2 * q + 1) * kRowB, wave, lane);
-    dma_scales<EDGE>(more ? rws : rnone, L.scales[par ^ 1][0], i0, rows_w, nkb, q + 1, wave,
-                     lane);
-    dma_scales<EDGE>(more ? rxs : rnone, L.scales[par ^ 1][1], t0, rows_x, nkb, q + 1, wave,
-                     lane);
-    products(0);
-    publish();
+    stage(std::integral_constant<int, 18>{}, 0, 1, (2 * q + 1) * kRowB, true, q + 1, more);
     stage_scales(par, 1);
-    read_frags(L.codes[1][0] + rw, L.codes[1][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
-
-    dma_stage<EDGE>(more ? rwc : rnone, L.codes[0][0], i0, rows_w, ldb, (2 * q + 2) * kRowB,
-                    wave, lane);
-    dma_stage<EDGE>(more ? rxc : rnone, L.codes[0][1], t0, rows_x, ldb, (2 * q + 2) * kRowB,
-                    wave, lane);
-    products(1);
-    publish();
+    read_frags_ordered(L.codes[1][0] + rw, L.codes[1][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+    stage(std::integral_constant<int, 16>{}, 1, 0, (2 * q + 2) * kRowB, more, q + 1, false);
     stage_scales(par ^ 1, 0);
-    read_frags(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
+    read_frags_ordered(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
   }
   store_tile<BF16, VECY, EDGE>(p, acc, i0, t0);
 }
