@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
         L.dq_quantize_act_async.restype = I
         L.dq_gemm_mx.argtypes = [P, P, I64, I64, P, P, P, I64, I, P, P]
         L.dq_gemm_mx.restype = I
+        L.dq_gemm_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+        L.dq_gemm_pack_bytes.restype = I
+        L.dq_gemm_pack_weights.argtypes = [P, P, I64, I64, P, P, P]
+        L.dq_gemm_pack_weights.restype = I
+        L.dq_gemm_mx_packed.argtypes = [P, P, I64, I64, P, P, P, I64, I, P, P]
+        L.dq_gemm_mx_packed.restype = I
         L.dq_status_str.argtypes = [I]
         L.dq_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -263,6 +269,53 @@ def gemm_mx(act_codes, act_scales, w_codes, w_scales, a=None, out_dtype: str = "
                           DTYPE[out_dtype], y.data_ptr(), _stream(stream))
     if st != 0:
         raise DQError(st, "dq_gemm_mx")
+    return y
+
+
+def gemm_pack_weights(w_codes, w_scales, stream=None) -> Dict[str, object]:
+    """dq_gemm_pack_weights: the MXFP4 weight codes / E8M0 scales (out x K/2, out x K/32 uint8,
+    as solve returns them) laid out for gemm_mx_packed. Returns {"codes", "scales", "out",
+    "K"} (device uint8 tensors)."""
+    torch = _torch()
+    out, K = w_codes.shape[0], w_codes.shape[1] * 2
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib().dq_gemm_pack_bytes(out, K, ctypes.byref(cb), ctypes.byref(sb))
+    if st != 0:
+        raise DQError(st, "dq_gemm_pack_bytes")
+    for t, shape in ((w_codes, (out, K // 2)), (w_scales, (out, K // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"expected a contiguous CUDA uint8 tensor of shape {shape}")
+    codes = torch.empty(cb.value, dtype=torch.uint8, device=w_codes.device)
+    scales = torch.empty(sb.value, dtype=torch.uint8, device=w_codes.device)
+    st = lib().dq_gemm_pack_weights(w_codes.data_ptr(), w_scales.data_ptr(), out, K,
+                                    codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_gemm_pack_weights")
+    return {"codes": codes, "scales": scales, "out": out, "K": K}
+
+
+def gemm_mx_packed(act_codes, act_scales, packed, a=None, out_dtype: str = "bf16", y=None,
+                   stream=None):
+    """dq_gemm_mx_packed: gemm_mx with weights from gemm_pack_weights."""
+    torch = _torch()
+    tokens, K, out = act_codes.shape[0], act_codes.shape[1] * 2, packed["out"]
+    if K != packed["K"]:
+        raise ValueError("activations and packed weights disagree on K")
+    for t, shape in ((act_codes, (tokens, K // 2)), (act_scales, (tokens, K // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"expected a contiguous CUDA uint8 tensor of shape {shape}")
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
+    if y is None:
+        y = torch.empty((tokens, out), dtype=dt, device=act_codes.device)
+    elif y.dtype != dt or tuple(y.shape) != (tokens, out) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tokens x out tensor of the output dtype")
+    if a is not None and (a.dtype != torch.float32 or a.numel() != out or not a.is_contiguous()):
+        raise ValueError("a must be a contiguous float32 vector of the output channels")
+    st = lib().dq_gemm_mx_packed(act_codes.data_ptr(), act_scales.data_ptr(), tokens, K,
+                                 packed["codes"].data_ptr(), packed["scales"].data_ptr(), _ptr(a),
+                                 out, DTYPE[out_dtype], y.data_ptr(), _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_gemm_mx_packed")
     return y
 
 

@@ -165,59 +165,79 @@ __device__ __forceinline__ void read_frags(const uint8_t* lw, const uint8_t* lx,
   }
 }
 
-// The epilogue: result v of block (m, n) of the wave is output channel i0 + wi + 32 m +
-// 8 (v / 4) + 4 (lane / 32) + v % 4 of token t0 + wt + 32 n + lane % 32; a lane stores its four
-// consecutive channels at once, times their a.
+// The epilogue. Result v of block (m, n) of the wave is output channel i0 + wi + 32 m +
+// 8 (v / 4) + 4 (lane / 32) + v % 4 of token t0 + wt + 32 n + lane % 32, so a lane holds runs
+// of 4 channels of one token, and storing them directly would write to 32 rows of Y per
+// instruction. Instead the wave's 128 x 128 results go out through LDS, 32 tokens at a time:
+// every lane writes its fp32 sums into the wave's region as rows of tokens (128 channels,
+// padded by 16 bytes so that the 32 tokens of one write hit distinct banks), then reads back
+// 4 channels of one row, 32 lanes to a row, always the same 4 channels: it applies their a
+// and stores 8 (bf16) or 16 (fp32) bytes, and each store instruction writes two whole rows
+// of 256 or 512 bytes. `stage` is LDS of at least 4 * 32 * 528 bytes, free once the main
+// loop is done. VECY: out % 4 == 0 and Y aligned to 4 elements.
+constexpr int kRowStage = 128 * 4 + 16;  // padded LDS row of 128 fp32 channels
+constexpr int kStageBytes = 4 * 32 * kRowStage;
+
 template <bool BF16, bool VECY, bool EDGE>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f (&acc)[4][4], int i0,
-                                           int t0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rl = lane & 31;
+                                           int t0, uint8_t* stage) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rl = lane & 31, h = lane >> 5;
   const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
-  const int ib = i0 + wi + (lane >> 5) * 4;
+  uint8_t* region = stage + wave * 32 * kRowStage;
+  const int ich = i0 + wi + rl * 4;  // the 4 channels this lane stores
+  f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (p.a) {
+    if (!EDGE || ich + 3 < p.out) {
+      av = *reinterpret_cast<const f32x4*>(p.a + ich);
+    } else {
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
+      for (int e = 0; e < 4; e++) av[e] = ich + e < p.out ? p.a[ich + e] : 1.0f;
+    }
+  }
+  __syncthreads();  // every wave is done with the main loop's LDS
+
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const int i = ib + m * 32 + g * 8;
-      const bool vec = VECY && (!EDGE || i < p.out);
-      f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (p.a) {
-        if (vec) {
-          av = *reinterpret_cast<const f32x4*>(p.a + i);
-        } else {
+  for (int n = 0; n < 4; n++) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) av[e] = i + e < p.out ? p.a[i + e] : 1.0f;
-        }
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const f32x4 y = {acc[m][n][g * 4], acc[m][n][g * 4 + 1], acc[m][n][g * 4 + 2],
+                         acc[m][n][g * 4 + 3]};
+        *reinterpret_cast<f32x4*>(region + rl * kRowStage + (m * 32 + g * 8 + h * 4) * 4) = y;
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
 #pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const int t = t0 + wt + n * 32 + rl;
-        if (EDGE && t >= p.tokens) continue;
-        f32x4 y;
+    for (int r = 0; r < 16; r++) {
+      const int row = h + 2 * r;
+      f32x4 y = *reinterpret_cast<const f32x4*>(region + row * kRowStage + rl * 16);
+      const int t = t0 + wt + n * 32 + row;
+      if (EDGE && t >= p.tokens) continue;
 #pragma unroll
-        for (int e = 0; e < 4; e++) y[e] = acc[m][n][g * 4 + e] * av[e];
-        if (BF16) {
-          __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + i;
-          if (vec) {
-            const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-            *reinterpret_cast<bf16x4*>(yp) = hv;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              if (i + e < p.out) yp[e] = (__bf16)y[e];
-          }
+      for (int e = 0; e < 4; e++) y[e] *= av[e];
+      const bool vec = VECY && (!EDGE || ich + 3 < p.out);
+      if (BF16) {
+        __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + ich;
+        const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+        if (vec) {
+          *reinterpret_cast<bf16x4*>(yp) = hv;
         } else {
-          float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + i;
-          if (vec) {
-            *reinterpret_cast<f32x4*>(yp) = y;
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-              if (i + e < p.out) yp[e] = y[e];
-          }
+          for (int e = 0; e < 4; e++)
+            if (ich + e < p.out) yp[e] = hv[e];
+        }
+      } else {
+        float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + ich;
+        if (vec) {
+          *reinterpret_cast<f32x4*>(yp) = y;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (ich + e < p.out) yp[e] = y[e];
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next chunk's writes
   }
 }
 
@@ -324,7 +344,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int i0, int t0,
   stage_products(acc, lw0 + ((nst - 1) & 1) * kBufB, lx0 + ((nst - 1) & 1) * kBufB, sterm, sw,
                  sx);
 
-  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0);
+  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0, &lds[0][0][0]);
 }
 
 // Tile order: workgroups are dealt round-robin to the eight XCDs, so consecutive ids are
@@ -371,6 +391,7 @@ struct DmaLds {
   uint8_t codes[2][2][kTileB];              // [buffer][W, X]: 128 KiB
   uint8_t scales[2][2][kScaleTileB];        // [period parity][W, X]: 16 KiB
 };
+static_assert(sizeof(DmaLds::codes) >= kStageBytes, "epilogue staging does not fit");
 
 // One row's scales for stage s from its period's LDS copy, as two dwords whose bytes 0 and 2
 // are the k blocks 8 s + 2 ks + lane / 32 of k steps ks = 0, 1 (first dword) and 2, 3
@@ -588,7 +609,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmArgs& p, int i0, int t0,
     stage_scales(par ^ 1, 0);
     read_frags_ordered(L.codes[0][0] + rw, L.codes[0][1] + rx, (0 ^ sterm) * 16, fa0, fb0);
   }
-  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0);
+  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0, &L.codes[0][0][0]);
 }
 
 template <bool BF16, bool VECY>
@@ -600,6 +621,279 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_dma(GemmArgs p) {
     gemm_tile_dma<BF16, VECY, false>(p, i0, t0, lds);
   else
     gemm_tile_dma<BF16, VECY, true>(p, i0, t0, lds);
+}
+
+// ------------------------------------------------------------ packed weights
+// Weights are static, so they can be laid out once in the order the matrix instructions read
+// them; the product then loads its weight fragments straight from global memory into
+// registers (a wave instruction reads 1 KiB contiguously) and LDS serves only the token
+// operand: with both operands' fragments read from LDS, the reads (512 bytes per product),
+// not the matrix cores, set the pace.
+//
+// Within a stage the k values are assigned to the k steps so that a lane's share is
+// contiguous: k step ks, lane half h, takes the stage's 32-value chunk 4 h + ks (the sum over
+// the stage is the same; only the order of the fp32 additions differs). Packed codes: for
+// each block of 32 rows rb, stage s and k step i, 1 KiB in which lane L holds 16 bytes: row
+// 32 rb + L % 32, chunk 4 (L / 32) + i of stage s. Packed scales: for each rb and s, 256 bytes
+// in which lane L holds the dword of k blocks 8 s + 4 (L / 32) .. + 3 of row 32 rb + L % 32
+// (the matrix instruction selects byte ks). Rows past `out` up to the next multiple of 32
+// hold zero codes and scale 2^0.
+constexpr int kPackBlockB = 1024;                     // codes of (rb, s, i)
+constexpr int kPackScaleB = 256;                      // scales of (rb, s)
+constexpr int kXTileB = kBN * kRowB;                  // 32 KiB: the token operand's stage
+
+__global__ void k_pack_codes(const uint8_t* __restrict__ wc, uint8_t* __restrict__ out_codes,
+                             int out, int ldb, int nst, int64_t nchunks) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 16-byte output chunk
+  if (g >= nchunks) return;
+  const int L = (int)(g % 64);
+  const int64_t blk = g / 64;  // (rb * nst + s) * 4 + i
+  const int i = (int)(blk % 4);
+  const int s = (int)((blk / 4) % nst);
+  const int64_t rb = blk / 4 / nst;
+  const int64_t row = rb * 32 + L % 32;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < out)
+    v = *reinterpret_cast<const u32x4*>(wc + row * ldb + s * kRowB + (4 * (L / 32) + i) * 16);
+  *reinterpret_cast<u32x4*>(out_codes + g * 16) = v;
+}
+
+__global__ void k_pack_scales(const uint8_t* __restrict__ ws, uint32_t* __restrict__ out_scales,
+                              int out, int nkb, int nst, int64_t ndwords) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // output dword
+  if (g >= ndwords) return;
+  const int L = (int)(g % 64);
+  const int s = (int)((g / 64) % nst);
+  const int64_t rb = g / 64 / nst;
+  const int64_t row = rb * 32 + L % 32;
+  uint32_t v = 0x7F7F7F7Fu;
+  if (row < out) v = *reinterpret_cast<const uint32_t*>(ws + row * nkb + 8 * s + 4 * (L / 32));
+  out_scales[g] = v;
+}
+
+struct PackedLds {
+  uint8_t x[2][kXTileB];                    // [buffer]: token stages, 64 KiB
+  uint8_t xs[2][kScaleTileB];               // [period parity]: token scales, 8 KiB
+};
+// the epilogue stages fp32 results of 4 waves x 32 tokens in the same memory
+static_assert(sizeof(PackedLds) >= kStageBytes, "epilogue staging does not fit");
+
+// Per-wave state of the packed-weight tile loop.
+struct PackedCtx {
+  __amdgpu_buffer_rsrc_t rwc, rxc, rws, rxs, rnone;
+  int t0, rows_x, ldb, nst, wave, lane;
+  uint32_t va[4];     // packed-code offsets of this wave's row blocks m (+ lane), or kOob
+  uint32_t vs[4];     // packed-scale offsets of the same, or kOob
+  uint32_t vx[2];     // token-stage offsets of this lane's load rows, even / odd groups
+  uint32_t sbx;       // token-scale offset of this lane's row in the scale loads
+};
+
+// Token stage load j (0..7) of this wave: LDS rows 8 (8 wave + j) .. + 7, lane j' writing row
+// 8 g + j' / 8 at chunk position j' % 8, which holds the row's logical chunk
+// (j' % 8) ^ swizzle term (the term's bit-3 part flips with the group's parity).
+template <bool EDGE>
+__device__ __forceinline__ void packed_load_x(const PackedCtx& c, PackedLds& lds, int buf, int j,
+                                              int kb0, bool on) {
+  uint32_t v = c.vx[j & 1];
+  if (EDGE && c.t0 + c.wave * 64 + j * 8 + (c.lane >> 3) >= c.rows_x) v = kOob;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(on ? c.rxc : c.rnone,
+                                           (lds_ptr_t)(lds.x[buf] + (c.wave * 8 + j) * 1024),
+                                           16, (int)v, (int)(uint32_t)(j * 8 * c.ldb + kb0), 0,
+                                           0);
+}
+
+// Token scale period q: rows 64 wave .. + 63, 16 bytes each.
+__device__ __forceinline__ void packed_load_xs(const PackedCtx& c, PackedLds& lds, int q,
+                                               bool on) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(on ? c.rxs : c.rnone,
+                                           (lds_ptr_t)(lds.xs[q & 1] + c.wave * 1024), 16,
+                                           (int)c.sbx, (int)(uint32_t)(q * 16), 0, 0);
+}
+
+template <int KS>
+__device__ __forceinline__ void mfma_sel(v16f& acc, const u32x4& fa, const u32x4& fb, uint32_t sa,
+                                         uint32_t sb) {
+  const v8i A = {(int)fa[0], (int)fa[1], (int)fa[2], (int)fa[3], 0, 0, 0, 0};
+  const v8i B = {(int)fb[0], (int)fb[1], (int)fb[2], (int)fb[3], 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, KS, (int)sa, KS, (int)sb);
+}
+
+// k step KS of a stage: 16 products in the order (m, n). Between them, one at a time: the
+// next step's four token fragments (KS < 3) and, in the first two steps only, all of the next
+// stage's loads, so that they have half a stage to land before the barrier that ends it
+// waits for them: step 0 the weight fragments of row blocks 0 and 1, token loads 0..3 and the
+// weight scales of blocks 0 and 1; step 1 the same for blocks 2 and 3 and token loads 4..7,
+// and the token scale period (NX > 8: on the first stage of a period). A load to LDS that
+// reads nothing still writes its (zero) bytes, so loads a stage does not need are not issued.
+template <bool EDGE, int KS, int NX>
+__device__ __forceinline__ void packed_kstep(v16f (&acc)[4][4], const u32x4 (&fa)[4][4],
+                                             u32x4 (&fa_next)[4][4], const u32x4 (&fb)[4],
+                                             u32x4 (&fb_next)[4], const uint8_t* lx, int xterm,
+                                             const uint32_t (&sw)[4], uint32_t (&sw_next)[4],
+                                             const uint32_t (&sx)[4], const PackedCtx& c,
+                                             PackedLds& lds, int nbuf, int ns, int kb0, bool on,
+                                             int q, bool xs_on) {
+#pragma unroll
+  for (int t = 0; t < 16; t++) {
+    const int m = t / 4, n = t % 4;
+    mfma_sel<KS>(acc[m][n], fa[m][KS], fb[n], sw[m], sx[n]);
+    if (t % 4 == 0 && KS < 3)
+      fb_next[t / 4] =
+          *reinterpret_cast<const u32x4*>(lx + (t / 4) * 32 * kRowB + (((KS + 1) ^ xterm) * 16));
+    if (KS < 2) {
+      if (t % 2 == 1) {  // weight fragment (row block 2 KS + t / 8, k step (t / 2) % 4)
+        const int mb = 2 * KS + t / 8, i = (t / 2) % 4;
+        fa_next[mb][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            on ? c.rwc : c.rnone, c.va[mb], (uint32_t)((ns * 4 + i) * kPackBlockB), 0);
+      }
+      if (t % 4 == 2) packed_load_x<EDGE>(c, lds, nbuf, KS * 4 + t / 4, kb0, on);
+      if (t == 0 || t == 4) {
+        const int mb = 2 * KS + t / 4;
+        sw_next[mb] = __builtin_amdgcn_raw_buffer_load_b32(on ? c.rws : c.rnone, c.vs[mb],
+                                                           (uint32_t)(ns * kPackScaleB), 0);
+      }
+      if (KS == 1 && t == 8 && NX > 8) packed_load_xs(c, lds, q, xs_on);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <bool BF16, bool VECY, bool EDGE>
+__device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int t0,
+                                                 PackedLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
+  const int ldb = p.K / 2, nkb = p.K / 32;
+  const int nst = p.K / kBK;  // even: K % 512 == 0
+  const int nrb = (p.out + 31) / 32;
+  const int rl = lane & 31, h = lane >> 5;
+
+  PackedCtx c;
+  c.rwc = rsrc(p.wc, (uint32_t)nrb * (uint32_t)nst * 4u * kPackBlockB);
+  c.rws = rsrc(p.ws, (uint32_t)nrb * (uint32_t)nst * kPackScaleB);
+  c.rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
+  c.rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+  // a descriptor that reads nothing: the loads of the stage after the last go there (the loop
+  // body stays one basic block, so nothing can move across its barriers)
+  c.rnone = rsrc(p.wc, 0u);
+  c.t0 = t0;
+  c.rows_x = EDGE ? p.tokens : INT32_MAX;
+  c.ldb = ldb;
+  c.nst = nst;
+  c.wave = wave;
+  c.lane = lane;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const int rb = (i0 + wi) / 32 + m;
+    const bool in = !EDGE || rb < nrb;
+    c.va[m] = in ? (uint32_t)rb * (uint32_t)nst * 4u * kPackBlockB + (uint32_t)(lane * 16) : kOob;
+    c.vs[m] = in ? (uint32_t)rb * (uint32_t)nst * kPackScaleB + (uint32_t)(lane * 4) : kOob;
+  }
+  {
+    const int lr = lane >> 3;
+    const uint32_t bx = (uint32_t)(t0 + wave * 64 + lr) * (uint32_t)ldb;
+    c.vx[0] = bx + (uint32_t)(((lane & 7) ^ lr) * 16);
+    c.vx[1] = bx + (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
+    const int rx = t0 + wave * 64 + lane;
+    c.sbx = (EDGE && rx >= p.tokens) ? kOob : (uint32_t)rx * (uint32_t)nkb;
+  }
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[m][n] = v16f{};
+
+  // token fragment reads: row wt + 32 n + lane % 32 of the buffer, chunk 4 h + ks at its
+  // swizzled position (4 h + ks) ^ term = ks ^ (term ^ 4 h)
+  const int xterm = (rl & 7) ^ ((rl >> 3) & 1) ^ (4 * h);
+  const int rx = (wt + rl) * kRowB;
+  const int sx_off = (wt + rl) * kScaleRowB + 4 * h;
+
+  u32x4 fa[2][4][4];  // [stage parity][m][ks]: the weight fragments of a whole stage
+  uint32_t sw[2][4];  // [stage parity][m]: their scale dwords
+  u32x4 fb0[4], fb1[4];
+  uint32_t sx[4];
+
+  // prologue: stage 0 (weights and their scales into registers, tokens into buffer 0) and
+  // token scale period 0
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      fa[0][m][i] = __builtin_amdgcn_raw_buffer_load_b128(c.rwc, c.va[m],
+                                                          (uint32_t)(i * kPackBlockB), 0);
+    sw[0][m] = __builtin_amdgcn_raw_buffer_load_b32(c.rws, c.vs[m], 0u, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L, 0, j, 0, true);
+  packed_load_xs(c, L, 0, true);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto stage_xs = [&](int par, int half) {
+    const uint8_t* bx = L.xs[par] + sx_off + half * 8;
+#pragma unroll
+    for (int n = 0; n < 4; n++) sx[n] = *reinterpret_cast<const uint32_t*>(bx + n * 32 * kScaleRowB);
+  };
+  auto first_frags = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < 4; n++)
+      fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
+  };
+  // one stage: products from registers fa[P] / sw[P] and token buffer `buf`; the next stage
+  // (ns) into fa[P ^ 1] / sw[P ^ 1] and the other buffer
+  auto stage = [&](auto pc, auto nxc, int buf, int ns, bool on, int q, bool xs_on) {
+    constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
+    const uint8_t* lx = L.x[buf] + rx;
+    const int kb0 = ns * kRowB;
+    __builtin_amdgcn_sched_barrier(0);
+    packed_kstep<EDGE, 0, NX>(acc, fa[P], fa[P ^ 1], fb0, fb1, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
+    packed_kstep<EDGE, 1, NX>(acc, fa[P], fa[P ^ 1], fb1, fb0, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
+    packed_kstep<EDGE, 2, NX>(acc, fa[P], fa[P ^ 1], fb0, fb1, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
+    packed_kstep<EDGE, 3, NX>(acc, fa[P], fa[P ^ 1], fb1, fb0, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
+    // this wave's loads (registers and LDS) are complete; after the barrier, everyone's
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  stage_xs(0, 0);
+  first_frags(0);
+
+  // two stages (one token scale period) per trip: stage 2 q (registers [0], buffer 0) and
+  // stage 2 q + 1 (registers [1], buffer 1); token scales of period q + 1 load during 2 q
+  for (int q = 0; q < nst / 2; q++) {
+    const bool more = 2 * q + 2 < nst;
+    const int par = q & 1;
+    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 0, 2 * q + 1, true,
+          q + 1, more);
+    stage_xs(par, 1);
+    first_frags(1);
+    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 1, 2 * q + 2, more,
+          q + 1, false);
+    stage_xs(par ^ 1, 0);
+    first_frags(0);
+  }
+  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
+}
+
+template <bool BF16, bool VECY>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) PackedLds lds;
+  int i0, t0;
+  tile_origin(p, i0, t0);
+  if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
+    gemm_tile_packed<BF16, VECY, false>(p, i0, t0, lds);
+  else
+    gemm_tile_packed<BF16, VECY, true>(p, i0, t0, lds);
+}
+
+template <bool BF16, bool VECY>
+hipError_t launch_packed_t(const GemmArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_mx_packed<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s,
+                     p);
+  return hipGetLastError();
 }
 
 template <bool BF16, bool FULLK, bool VECY>
@@ -672,6 +966,85 @@ dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_
       p.nti = (p.out + kBM - 1) / kBM;
       p.ntt = (p.tokens + kBN - 1) / kBN;
       if (launch(p, bf16, fullk, dma, vecy, stream) != hipSuccess) return DQ_ERR_HIP;
+    }
+  }
+  return DQ_OK;
+}
+
+dq_status dq_gemm_pack_bytes(int64_t out, int64_t K, size_t* codes_bytes, size_t* scales_bytes) {
+  using namespace dqg;
+  if (!codes_bytes || !scales_bytes || out < 1 || K < 512 || K % 512 != 0 || K > (1 << 22))
+    return DQ_ERR_ARG;
+  const int64_t nrb = (out + 31) / 32, nst = K / kBK;
+  *codes_bytes = (size_t)(nrb * nst * 4 * kPackBlockB);
+  *scales_bytes = (size_t)(nrb * nst * kPackScaleB);
+  return DQ_OK;
+}
+
+dq_status dq_gemm_pack_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t out,
+                               int64_t K, uint8_t* packed_codes, uint8_t* packed_scales,
+                               hipStream_t stream) {
+  using namespace dqg;
+  size_t cb = 0, sb = 0;
+  if (dq_gemm_pack_bytes(out, K, &cb, &sb) != DQ_OK) return DQ_ERR_ARG;
+  if (!w_codes || !w_scales || !packed_codes || !packed_scales) return DQ_ERR_ARG;
+  if (((uintptr_t)w_codes & 15u) || ((uintptr_t)w_scales & 3u) || ((uintptr_t)packed_codes & 15u) ||
+      ((uintptr_t)packed_scales & 3u))
+    return DQ_ERR_ARG;
+  const int nst = (int)(K / kBK);
+  const int64_t nchunks = (int64_t)(cb / 16), ndw = (int64_t)(sb / 4);
+  hipLaunchKernelGGL(k_pack_codes, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, stream,
+                     w_codes, packed_codes, (int)out, (int)(K / 2), nst, nchunks);
+  if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
+  hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, stream,
+                     w_scales, reinterpret_cast<uint32_t*>(packed_scales), (int)out, (int)(K / 32),
+                     nst, ndw);
+  if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
+  return DQ_OK;
+}
+
+dq_status dq_gemm_mx_packed(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                            int64_t K, const uint8_t* packed_codes, const uint8_t* packed_scales,
+                            const float* a, int64_t out, dq_dtype yt, void* Y,
+                            hipStream_t stream) {
+  using namespace dqg;
+  if (!act_codes || !act_scales || !packed_codes || !packed_scales || !Y) return DQ_ERR_ARG;
+  if (tokens < 1 || out < 1 || K < 512 || K % 512 != 0 || K > (1 << 22)) return DQ_ERR_ARG;
+  if (yt != DQ_F32 && yt != DQ_BF16) return DQ_ERR_UNSUPPORTED;
+  if (((uintptr_t)act_codes & 15u) || ((uintptr_t)act_scales & 15u) ||
+      ((uintptr_t)packed_codes & 15u) || ((uintptr_t)packed_scales & 3u) ||
+      ((uintptr_t)a & 15u))
+    return DQ_ERR_ARG;
+  // per launch, every buffer offset stays below 2^31: tokens and output channels are split
+  // into chunks of whole tiles that keep it so (a chunk of channels is a whole number of
+  // 32-row packed blocks)
+  const int64_t ldb = K / 2, nkb = K / 32, nst = K / kBK;
+  const int64_t lim = (int64_t(1) << 31) - ldb * (kBM + 1);
+  const int64_t tchunk = std::max<int64_t>(kBN, (lim / ldb) / kBN * kBN);
+  const int64_t ochunk = std::max<int64_t>(kBM, (lim / ldb) / kBM * kBM);
+  const bool bf16 = yt == DQ_BF16;
+  const size_t esz = bf16 ? 2 : 4;
+  const bool vecy = out % 4 == 0 && ((uintptr_t)Y & (4 * esz - 1)) == 0;
+  for (int64_t tb = 0; tb < tokens; tb += tchunk) {
+    for (int64_t ob = 0; ob < out; ob += ochunk) {
+      GemmArgs p{};
+      p.xc = act_codes + tb * ldb;
+      p.xs = act_scales + tb * nkb;
+      p.wc = packed_codes + (ob / 32) * nst * 4 * kPackBlockB;
+      p.ws = packed_scales + (ob / 32) * nst * kPackScaleB;
+      p.a = a ? a + ob : nullptr;
+      p.y = static_cast<char*>(Y) + (size_t)(tb * out + ob) * esz;
+      p.tokens = (int)std::min(tchunk, tokens - tb);
+      p.out = (int)std::min(ochunk, out - ob);
+      p.K = (int)K;
+      p.ldy = out;
+      p.nti = (p.out + kBM - 1) / kBM;
+      p.ntt = (p.tokens + kBN - 1) / kBN;
+      const hipError_t e = bf16 ? (vecy ? launch_packed_t<true, true>(p, stream)
+                                        : launch_packed_t<true, false>(p, stream))
+                                : (vecy ? launch_packed_t<false, true>(p, stream)
+                                        : launch_packed_t<false, false>(p, stream));
+      if (e != hipSuccess) return DQ_ERR_HIP;
     }
   }
   return DQ_OK;

@@ -249,6 +249,30 @@ dq_status dq_gemm_mx(const uint8_t* act_codes, const uint8_t* act_scales, int64_
                      int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, const float* a,
                      int64_t out, dq_dtype yt, void* Y, hipStream_t stream);
 
+/* The same product with the weights packed once (dq_gemm_pack_weights) into the order the
+ * matrix instructions read them, so that the weight operand goes straight from memory into
+ * registers and LDS serves only the activations: the faster form for static weights. The
+ * packed product sums each 256-k stage in another order than dq_gemm_mx (the results agree
+ * to fp32 rounding, not bit for bit). K % 512 == 0 and 512 <= K <= 2^22.
+ *
+ * dq_gemm_pack_bytes: the sizes of the packed codes and scales for out x K weights (out
+ * padded to a multiple of 32 rows). dq_gemm_pack_weights: writes them (device buffers of
+ * those sizes; codes 16-byte and scales 4-byte aligned, as are w_codes and w_scales) from the
+ * weight codes and E8M0 scales as dq_solve writes them; padding rows get zero codes and scale
+ * 2^0. Layout: for each 32-row block rb, 256-k stage s and k step i (0..3), 1 KiB in which
+ * lane L (0..63) holds the 16 code bytes of row 32 rb + L % 32, k values
+ * 256 s + 32 (4 (L / 32) + i) .. + 31; for each rb and s, 256 bytes in which lane L holds the 4
+ * scale bytes of row 32 rb + L % 32, k blocks 8 s + 4 (L / 32) .. + 3. Only enqueues.
+ * dq_gemm_mx_packed: as dq_gemm_mx with the packed weights (act_scales 16-byte aligned). */
+dq_status dq_gemm_pack_bytes(int64_t out, int64_t K, size_t* codes_bytes, size_t* scales_bytes);
+dq_status dq_gemm_pack_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t out,
+                               int64_t K, uint8_t* packed_codes, uint8_t* packed_scales,
+                               hipStream_t stream);
+dq_status dq_gemm_mx_packed(const uint8_t* act_codes, const uint8_t* act_scales, int64_t tokens,
+                            int64_t K, const uint8_t* packed_codes, const uint8_t* packed_scales,
+                            const float* a, int64_t out, dq_dtype yt, void* Y,
+                            hipStream_t stream);
+
 /* Static string for a status code. */
 const char* dq_status_str(dq_status status);
 

@@ -10,7 +10,9 @@ fp32's 24 bits the product is exact, whatever the order, and the test asks for b
 Cases: ragged token / channel counts and K not a multiple of the 256-k stage (the slow
 path), the fast path at tile multiples, both output types, a = None, the exact case, NaN
 block scales, the quantizers' own outputs, the Llama-3.1-8B MLP shapes at full size on
-sampled outputs, and a K large enough that a call is split into several launches."""
+sampled outputs, and a K large enough that a call is split into several launches; the same
+for the product with packed weights, whose packing is checked byte for byte against the
+documented layout restated here with numpy."""
 import numpy as np
 import pytest
 
@@ -42,12 +44,19 @@ def _bound(oracle, xc, xs, wc, ws, a, K):
     return (K / 64 + 2) * 2.0 * 2.0 ** -24 * S
 
 
-def _check(dq, oracle, xc, xs, wc, ws, a, out_dtype, name=""):
+def _gemm(dq, xc, xs, wc, ws, a, out_dtype, packed):
+    ad = None if a is None else _dev(a)
+    if packed:
+        pk = dq.gemm_pack_weights(_dev(wc), _dev(ws))
+        return dq.gemm_mx_packed(_dev(xc), _dev(xs), pk, ad, out_dtype=out_dtype)
+    return dq.gemm_mx(_dev(xc), _dev(xs), _dev(wc), _dev(ws), ad, out_dtype=out_dtype)
+
+
+def _check(dq, oracle, xc, xs, wc, ws, a, out_dtype, name="", packed=False):
     K = xc.shape[1] * 2
     print(f"[gemm] {name} tokens={xc.shape[0]} out={wc.shape[0]} K={K} {out_dtype} "
-          f"a={'yes' if a is not None else 'no'}", flush=True)
-    y = dq.gemm_mx(_dev(xc), _dev(xs), _dev(wc), _dev(ws), None if a is None else _dev(a),
-                   out_dtype=out_dtype)
+          f"a={'yes' if a is not None else 'no'} packed={packed}", flush=True)
+    y = _gemm(dq, xc, xs, wc, ws, a, out_dtype, packed)
     got = host(y).astype(np.float64) if out_dtype == "f32" else _bf16_host(y)
     ref = oracle.gemm_mx(xc, xs, wc, ws, a)
     tol = _bound(oracle, xc, xs, wc, ws, a, K)
@@ -82,15 +91,66 @@ def test_gemm_matches_oracle(dq, oracle_lib, tokens, out, K, out_dtype):
         _check(dq, oracle_lib, xc, xs, wc, ws, None, out_dtype, name="a=None")
 
 
+def _pack_reference(codes, scales, K):
+    """The packed layout as dq.h states it: per 32-row block rb, stage s and k step i, 64 lanes
+    x 16 bytes (lane L: row 32 rb + L % 32, chunk 4 (L / 32) + i of the stage); per rb and s,
+    64 lanes x 4 scale bytes (k blocks 8 s + 4 (L / 32) .. + 3); padding rows zero / 127."""
+    out, nst = codes.shape[0], K // 256
+    nrb = -(-out // 32)
+    c = np.zeros((nrb * 32, K // 2), np.uint8)
+    c[:out] = codes
+    sc = np.full((nrb * 32, K // 32), 127, np.uint8)
+    sc[:out] = scales
+    pc = np.empty((nrb, nst, 4, 64, 16), np.uint8)
+    ps = np.empty((nrb, nst, 64, 4), np.uint8)
+    for L in range(64):
+        rl, h = L % 32, L // 32
+        rows_c = c[rl::32].reshape(nrb, nst, 8, 16)
+        for i in range(4):
+            pc[:, :, i, L, :] = rows_c[:, :, 4 * h + i, :]
+        ps[:, :, L, :] = sc[rl::32].reshape(nrb, nst, 8)[:, :, 4 * h:4 * h + 4]
+    return pc.reshape(-1), ps.reshape(-1)
+
+
+@pytest.mark.parametrize("out,K", [(70, 1024), (256, 512), (33, 2048)])
+def test_pack_weights_layout(dq, out, K):
+    wc, ws = workloads.mx_operands(out, K, seed=out)
+    print(f"[gemm] pack out={out} K={K}", flush=True)
+    pk = dq.gemm_pack_weights(_dev(wc), _dev(ws))
+    want_c, want_s = _pack_reference(wc, ws, K)
+    assert np.array_equal(host(pk["codes"]), want_c)
+    assert np.array_equal(host(pk["scales"]), want_s)
+
+
+@pytest.mark.parametrize("tokens,out,K", [
+    (256, 256, 512),     # one tile
+    (300, 520, 1024),    # ragged tokens and channels
+    (97, 70, 512),       # channels neither a multiple of 32 nor of 4
+    (33, 1000, 1536),    # several channel tiles, an odd number of stage pairs
+    (1, 4, 512),         # the smallest call
+])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_packed_gemm_matches_oracle(dq, oracle_lib, tokens, out, K, out_dtype):
+    xc, xs = workloads.mx_operands(tokens, K, seed=5)
+    wc, ws = workloads.mx_operands(out, K, seed=6)
+    a = np.random.default_rng(out + 1).uniform(0.02, 2.0, out).astype(np.float32)
+    _check(dq, oracle_lib, xc, xs, wc, ws, a, out_dtype, name="random", packed=True)
+    if out_dtype == "f32":
+        _check(dq, oracle_lib, xc, xs, wc, ws, None, out_dtype, name="a=None", packed=True)
+
+
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("tokens,out,K", [(256, 512, 2048), (97, 131, 224)])
-def test_gemm_exact_when_the_sums_fit_fp32(dq, oracle_lib, tokens, out, K):
+def test_gemm_exact_when_the_sums_fit_fp32(dq, oracle_lib, tokens, out, K, packed):
+    if packed and K % 512:
+        pytest.skip("the packed form needs K % 512 == 0")
     # scales 2^-1 .. 2^1: products are multiples of 2^-4 below 2^7.2, sums of K of them stay
     # within 24 significant bits, so fp32 accumulation in any order is exact
     xc, xs = workloads.mx_operands(tokens, K, seed=3, lo=126, hi=129)
     wc, ws = workloads.mx_operands(out, K, seed=4, lo=126, hi=129)
     a = (2.0 ** np.random.default_rng(5).integers(-3, 4, out)).astype(np.float32)
-    print(f"[gemm] exact tokens={tokens} out={out} K={K}", flush=True)
-    y = host(dq.gemm_mx(_dev(xc), _dev(xs), _dev(wc), _dev(ws), _dev(a), out_dtype="f32"))
+    print(f"[gemm] exact tokens={tokens} out={out} K={K} packed={packed}", flush=True)
+    y = host(_gemm(dq, xc, xs, wc, ws, a, "f32", packed))
     ref = oracle_lib.gemm_mx(xc, xs, wc, ws, a)
     assert np.array_equal(y.astype(np.float64), ref)
 
@@ -131,8 +191,9 @@ def test_gemm_on_the_quantizers_outputs(dq, oracle_lib):
     assert np.linalg.norm(y - full) / np.linalg.norm(full) < 0.6
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("which", ["up", "down"])
-def test_gemm_full_size_llama8b_mlp_sampled(dq, oracle_lib, which):
+def test_gemm_full_size_llama8b_mlp_sampled(dq, oracle_lib, which, packed):
     # up / gate: 8192 tokens x 4096 -> 14336 channels; down: 8192 x 14336 -> 4096; bf16 out,
     # checked on sampled token rows x channel columns
     tokens = 8192
@@ -140,8 +201,8 @@ def test_gemm_full_size_llama8b_mlp_sampled(dq, oracle_lib, which):
     xc, xs = workloads.mx_operands(tokens, K, seed=21)
     wc, ws = workloads.mx_operands(out, K, seed=22)
     a = np.random.default_rng(23).uniform(0.5, 2.0, out).astype(np.float32)
-    print(f"[gemm] full size {which}", flush=True)
-    y = dq.gemm_mx(_dev(xc), _dev(xs), _dev(wc), _dev(ws), _dev(a), out_dtype="bf16")
+    print(f"[gemm] full size {which} packed={packed}", flush=True)
+    y = _gemm(dq, xc, xs, wc, ws, a, "bf16", packed)
     rng = np.random.default_rng(24)
     ts = np.sort(rng.choice(tokens, 24, replace=False))
     ts[0], ts[-1] = 0, tokens - 1
@@ -154,7 +215,8 @@ def test_gemm_full_size_llama8b_mlp_sampled(dq, oracle_lib, which):
     assert np.all(np.abs(got - ref) <= tol)
 
 
-def test_gemm_split_into_launches_at_the_largest_k(dq, oracle_lib):
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_split_into_launches_at_the_largest_k(dq, oracle_lib, packed):
     # K = 2^22: 2 MiB of codes per row; a launch keeps every offset below 2^31, so the 1100
     # tokens run as launches over chunks of 512 tokens
     import torch
@@ -165,8 +227,11 @@ def test_gemm_split_into_launches_at_the_largest_k(dq, oracle_lib):
     xs = torch.randint(124, 131, (tokens, K // 32), dtype=torch.uint8, device="cuda", generator=g)
     wc = torch.randint(0, 256, (out, K // 2), dtype=torch.uint8, device="cuda", generator=g)
     ws = torch.randint(124, 131, (out, K // 32), dtype=torch.uint8, device="cuda", generator=g)
-    print(f"[gemm] K=2^22 tokens={tokens} out={out}", flush=True)
-    y = host(dq.gemm_mx(xc, xs, wc, ws, out_dtype="f32"))
+    print(f"[gemm] K=2^22 tokens={tokens} out={out} packed={packed}", flush=True)
+    if packed:
+        y = host(dq.gemm_mx_packed(xc, xs, dq.gemm_pack_weights(wc, ws), out_dtype="f32"))
+    else:
+        y = host(dq.gemm_mx(xc, xs, wc, ws, out_dtype="f32"))
     ts = np.array([0, 511, 512, 767, 768, 1023, 1024, 1099])  # around every chunk edge
     xch, xsh = host(xc[ts]), host(xs[ts])
     wch, wsh = host(wc), host(ws)

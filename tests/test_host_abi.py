@@ -31,6 +31,7 @@ def dqlib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_gemm_mx",
+                     "dq_gemm_mx_packed", "dq_gemm_pack_bytes", "dq_gemm_pack_weights",
                      "dq_quantize", "dq_quantize_act", "dq_quantize_act_async", "dq_solve",
                      "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
 
@@ -151,6 +152,25 @@ def test_gemm_arguments_are_rejected_on_the_host(dqlib):
     assert call(xc=ctypes.c_void_p(0x1008)) == 1     # codes not 16-byte aligned
     assert call(wc=ctypes.c_void_p(0x1004)) == 1
     assert call(a=ctypes.c_void_p(0x1004)) == 1      # a not 16-byte aligned
+
+    # the packed form: K a multiple of 512, sizes, and the same argument checks
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.dq_gemm_pack_bytes(100, 1024, ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 4 * 4 * 4 * 1024 and sb.value == 4 * 4 * 256  # 4 row blocks, 4 stages
+    assert L.dq_gemm_pack_bytes(100, 768, ctypes.byref(cb), ctypes.byref(sb)) == 1
+    assert L.dq_gemm_pack_bytes(0, 1024, ctypes.byref(cb), ctypes.byref(sb)) == 1
+    assert L.dq_gemm_pack_weights(fake, fake, 100, 768, fake, fake, None) == 1
+    assert L.dq_gemm_pack_weights(ctypes.c_void_p(0x1008), fake, 100, 1024, fake, fake, None) == 1
+
+    def callp(**kw):
+        a = dict(args, **kw)
+        return L.dq_gemm_mx_packed(a["xc"], a["xs"], a["tokens"], a["K"], a["wc"], a["ws"],
+                                   a["a"], a["out"], a["yt"], a["Y"], None)
+
+    assert callp(K=256) == 1
+    assert callp(K=1024, xs=ctypes.c_void_p(0x1008)) == 1   # scales not 16-byte aligned
+    assert callp(K=1024, yt=7) == 2
+    assert callp(K=1024, Y=None) == 1
 
 
 def test_batch_arguments_are_rejected_on_the_host(dqlib):
