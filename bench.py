@@ -397,14 +397,33 @@ def bench_act(args, dq) -> None:
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
+GEMM_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_gemm.hip",)
+# HBM bytes of one W4A4 step (up and down with packed weights) from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs (KiB per dispatch, summed over the two products), scaled as above; valid
+# only for the kernel source they were taken on.
+GEMM_COUNTERS = {
+    "fetch_kib": 183028.5 + 183971.0, "fetch_scale": 2.0,
+    "write_kib": 229376.0 + 65536.0, "write_scale": 1.0,
+    "sources_sha256": "405415a0eb0fd958c70395fa9d1a21ab60667f540da77021cbd34de1ed3edc9f",
+}
+
+
+def gemm_traffic():
+    c = GEMM_COUNTERS
+    if sources_sha256(GEMM_SOURCES) != c["sources_sha256"]:
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 
 
 def bench_gemm(args, dq) -> None:
     """The W4A4 product on the chain it serves: the Llama-3.1-8B MLP up (14336x4096) and down
-    (4096x14336) weights solved on the GPU (MXFP4 G32, T = 20), the MLP inputs of 8192 tokens
-    quantized with the solver's b, and a step = both products Y = (xhat Qhat^T) D_a, bf16 out.
-    Kernel time: back-to-back calls between one pair of HIP events on the calling stream, and
-    each product alone the same way. Algorithmic flops: 2 * tokens * out * K per product."""
+    (4096x14336) weights solved on the GPU (MXFP4 G32, T = 20) and packed once for the matrix
+    cores (dq_gemm_pack_weights: static weights, like the solve itself outside the timed
+    region), the MLP inputs of 8192 tokens quantized with the solver's b, and a step = both
+    products Y = (xhat Qhat^T) D_a with the packed weights, bf16 out. The same products from
+    the weights as the solver writes them (dq_gemm_mx) are timed alongside. Kernel time:
+    back-to-back calls between one pair of HIP events on the calling stream. Algorithmic
+    flops: 2 * tokens * out * K per product."""
     import numpy as np
     import torch
 
@@ -420,35 +439,43 @@ def bench_gemm(args, dq) -> None:
         tokens, K = act["codes"].shape[0], act["codes"].shape[1] * 2
         out = sol["codes"].shape[0]
         y = torch.empty((tokens, out), dtype=torch.bfloat16, device="cuda")
+        packed = dq.gemm_pack_weights(sol["codes"], sol["scales"])
         mats.append(dict(name=name, xc=act["codes"], xs=act["scales"], wc=sol["codes"],
                          ws=sol["scales"], a=sol["a"], y=y, flops=2.0 * tokens * out * K,
-                         shape=(tokens, out, K)))
+                         shape=(tokens, out, K), packed=packed))
 
-    def run(ms_list):
+    def run(ms_list, packed):
         for m in ms_list:
-            dq.gemm_mx(m["xc"], m["xs"], m["wc"], m["ws"], m["a"], out_dtype="bf16", y=m["y"],
-                       stream=stream)
+            if packed:
+                dq.gemm_mx_packed(m["xc"], m["xs"], m["packed"], m["a"], out_dtype="bf16",
+                                  y=m["y"], stream=stream)
+            else:
+                dq.gemm_mx(m["xc"], m["xs"], m["wc"], m["ws"], m["a"], out_dtype="bf16",
+                           y=m["y"], stream=stream)
 
-    def timed(ms_list, steps):
+    def timed(ms_list, steps, packed):
         for _ in range(args.warmup):
-            run(ms_list)
+            run(ms_list, packed)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(steps):
-            run(ms_list)
+            run(ms_list, packed)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    ms = timed(mats, args.steps)
+    ms = timed(mats, args.steps, True)
+    ms_natural = timed(mats, args.steps, False)
     flops = sum(m["flops"] for m in mats)
     per = {}
     for m in mats:
-        t = timed([m], args.steps)
-        per[m["name"]] = {"shape_tokens_out_k": m["shape"], "ms": t,
-                          "tflops": m["flops"] / (t * 1e-3) / 1e12,
-                          "frac": m["flops"] / (t * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
+        for packed in (True, False):
+            t = timed([m], args.steps, packed)
+            per[m["name"] + ("" if packed else " (unpacked weights)")] = {
+                "shape_tokens_out_k": m["shape"], "ms": t,
+                "tflops": m["flops"] / (t * 1e-3) / 1e12,
+                "frac": m["flops"] / (t * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
     tf = flops / (ms * 1e-3) / 1e12
     line = {
         "metric": "W4A4 MXFP4 product TFLOP/s (dense-equivalent), % FP4 matrix-core peak",
@@ -459,11 +486,13 @@ def bench_gemm(args, dq) -> None:
                 "quantized on the GPU by the solver and the activation quantizer",
         "config": {"workload": "llama3.1-8b MLP at 8192 tokens: up 8192x4096 x (14336x4096)^T "
                                "+ down 8192x14336 x (4096x14336)^T, MXFP4 G32, bf16 out"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_mx", "achieved": tf,
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_mx_packed", "achieved": tf,
                      "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP4_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "frac": tf / FP4_MFMA_PEAK_TFLOPS, "traffic": gemm_traffic(),
+                     "traffic_unit": "HBM bytes per step",
                      "timing": "back-to-back asynchronous calls between one pair of events"},
         "products": per,
+        "unpacked_weights_tflops": flops / (ms_natural * 1e-3) / 1e12,
     }
     if args.no_cpu:
         print(json.dumps(line), flush=True)
@@ -480,6 +509,8 @@ def bench_gemm(args, dq) -> None:
     ref = oracle.gemm_mx(xc, xs, wc, ws, a)
     dt = time.perf_counter() - t0
     oracle.set_threads(1)
+    run([m], True)
+    torch.cuda.synchronize()
     got = m["y"][ts].float().cpu().numpy().astype(np.float64)
     rel = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)))
     sample_flops = 2.0 * len(ts) * wc.shape[0] * xc.shape[1] * 2
