@@ -239,3 +239,19 @@ def test_gemm_split_into_launches_at_the_largest_k(dq, oracle_lib, packed):
     tol = _bound(oracle_lib, xch, xsh, wch, wsh, None, K)
     assert np.all(np.abs(y[ts] - ref) <= tol)
     del xc, wc
+
+
+def test_gemm_random_shapes(dq, oracle_lib):
+    # seeded random shapes through both forms and both output types: tokens and channels
+    # anywhere in 1..600, K any multiple of 32 (of 512 for the packed form)
+    rng = np.random.default_rng(2024)
+    for case in range(16):
+        tokens, out = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+        packed = bool(case % 2)
+        K = int(rng.integers(1, 5)) * 512 if packed else int(rng.integers(1, 48)) * 32
+        out_dtype = "bf16" if case % 3 == 0 else "f32"
+        xc, xs = workloads.mx_operands(tokens, K, seed=100 + case)
+        wc, ws = workloads.mx_operands(out, K, seed=200 + case)
+        a = rng.uniform(0.05, 3.0, out).astype(np.float32) if case % 4 else None
+        _check(dq, oracle_lib, xc, xs, wc, ws, a, out_dtype, name=f"random case {case}",
+               packed=packed)
