@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.dq_quantize_act_async.argtypes = [P, I, I64, I64, I, I, P, ctypes.c_float, P, P, P, P,
                                             P, SZ, P]
         L.dq_quantize_act_async.restype = I
+        L.dq_solve_async.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P, P, P, P,
+                                     P, P, P, SZ, P]
+        L.dq_solve_async.restype = I
         L.dq_gemm_mx.argtypes = [P, P, I64, I64, P, P, P, I64, I, P, P]
         L.dq_gemm_mx.restype = I
         L.dq_gemm_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
@@ -179,6 +182,43 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
         out["isolated"] = (tm.isolated_ms, tm.isolated_launches)
         out["cold_warm"] = (tm.cold_ms, tm.warm_ms, tm.per_launch)
     return out
+
+
+def solve_outputs(W, fmt: str, group: int, T: int) -> Dict[str, object]:
+    """Output tensors for solve_async on W: codes, scales, a, b, mse (T + 1), g."""
+    torch = _torch()
+    rows, cols = W.shape
+    dev = W.device
+    codes, scales = _outputs(W, fmt, group)
+    return {"codes": codes, "scales": scales,
+            "a": torch.empty(rows, dtype=torch.float32, device=dev),
+            "b": torch.empty(cols, dtype=torch.float32, device=dev),
+            "mse": torch.empty(T + 1, dtype=torch.float64, device=dev),
+            "g": torch.zeros(1, dtype=torch.float32, device=dev)}
+
+
+def solve_async(W, fmt: str, group: int, T: int, out, status, a0=None, b0=None, g0: float = 0.0,
+                two_sweep: bool = False, per_pass_g: bool = False, workspace=None,
+                stream=None) -> None:
+    """dq_solve_async into ``out`` (from solve_outputs): enqueued on the stream, no wait;
+    device errors are OR-ed into ``status`` (an int32 CUDA tensor the caller clears)."""
+    dt = _check_w(W)
+    rows, cols = W.shape
+    if out["mse"].numel() != T + 1:
+        raise ValueError("out was made for another T")
+    a0 = _vec(a0, rows, W.device)
+    b0 = _vec(b0, cols, W.device)
+    flags = (SOLVE_TWO_SWEEP if two_sweep else 0) | (SOLVE_PER_PASS_G if per_pass_g else 0)
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags, None)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
+    st = lib().dq_solve_async(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T,
+                              ctypes.byref(init), out["codes"].data_ptr(),
+                              out["scales"].data_ptr(), out["g"].data_ptr(), out["a"].data_ptr(),
+                              out["b"].data_ptr(), out["mse"].data_ptr(), status.data_ptr(),
+                              ws_ptr, ws_bytes, _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_solve_async")
 
 
 def quantize(W, fmt: str, group: int, a=None, b=None, g: float = 0.0, workspace=None,

@@ -732,6 +732,12 @@ struct WsGuard {
   }
 };
 
+// OR a finished solve's status word into a caller's (one lane; integer atomic, so calls on
+// several streams may share the caller's word)
+__global__ void k_status_or(const int* src, int* dst) {
+  if (threadIdx.x == 0 && src[0] != 0) atomicOr(dst, src[0]);
+}
+
 dq_status get_workspace(const Plan& p, void* workspace, size_t bytes, hipStream_t s, WsGuard& g) {
   g.s = s;
   if (workspace) {
@@ -799,6 +805,36 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
     break;
   }
   return map_status(flags & ~dq::kStGauge);
+}
+
+dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                         int group, int T, const dq_init* init, uint8_t* codes,
+                         void* inner_scales, float* tensor_scale, float* a, float* b,
+                         double* mse, int* status, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  dq_status st = check_common(W, wt, rows, cols, fmt, group, codes, inner_scales);
+  if (st != DQ_OK) return st;
+  if (T < 0 || !a || !b || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale)) return DQ_ERR_ARG;
+  if (!status || ((uintptr_t)status & 3u) != 0) return DQ_ERR_ARG;
+  if (init && init->timing) return DQ_ERR_ARG;  // timing needs the host to wait
+  if (init && (init->g0 != init->g0 || (init->g0 > 0.0f && init->g0 > 3.4028234663852886e38f)))
+    return DQ_ERR_ARG;
+  if (init && fmt == DQ_FMT_NVFP4 && (init->flags & DQ_SOLVE_PER_PASS_G) && init->g0 > 0.0f)
+    return DQ_ERR_ARG;
+  const Plan p = make_plan(rows, cols, fmt, group);
+  WsGuard ws;  // an owned workspace is freed stream-ordered, after the solve's kernels
+  st = get_workspace(p, workspace, workspace_bytes, stream, ws);
+  if (st != DQ_OK) return st;
+  SolveIo io{W, wt == DQ_BF16, init, codes, inner_scales, tensor_scale, a, b, mse, T};
+  const bool mx = fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4;
+  const bool fused = mx && !(init && (init->flags & DQ_SOLVE_TWO_SWEEP));
+  Timer tm{nullptr, stream};
+  st = enqueue_solve(p, ws.ptr, io, fused, false, tm, stream);
+  if (st != DQ_OK) return st;
+  hipLaunchKernelGGL(k_status_or, dim3(1), dim3(64), 0, stream, at<int>(ws.ptr, p.off_status),
+                     status);
+  DQ_TRY(hipGetLastError());
+  return DQ_OK;
 }
 
 dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,

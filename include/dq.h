@@ -152,6 +152,28 @@ dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq
                       uint8_t* codes, void* inner_scales, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* dq_solve without the wait, for callers that cannot synchronize per call (a pipeline that
+ * solves many matrices, a serving process): the same arguments and results, only enqueued on
+ * `stream`, with no host-side retry. Errors found on the device are OR-ed into *status
+ * (device, caller-owned, 4-byte aligned; the caller clears it and reads it when it wants;
+ * calls on several streams may share it):
+ *   1  W holds a NaN or an infinity (DQ_ERR_NONFINITE)
+ *   2  a scaled value overflowed (DQ_ERR_RANGE)
+ *   4  an init value was not finite and positive (DQ_ERR_ARG)
+ *   8  MX formats: the single-sweep pass could not guarantee its result (a group maximum,
+ *      a scale or a projection decision outside the range where it is exact); the outputs are
+ *      unspecified and the solve must be redone with DQ_SOLVE_TWO_SWEEP, which dq_solve does
+ *      by itself
+ *  16  internal (never expected)
+ * A nonzero status leaves the outputs unspecified. init->timing must be NULL. The workspace
+ * may be NULL (then allocated and freed stream-ordered). Host-side argument checks return
+ * errors as dq_solve does, before anything is enqueued. */
+dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                         int group, int T, const dq_init* init, uint8_t* codes,
+                         void* inner_scales, float* tensor_scale, float* a, float* b,
+                         double* mse, int* status, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Bytes of device workspace dq_quantize_act needs (0 on invalid arguments); scratch only. */
 size_t dq_act_workspace_bytes(int64_t tokens, int64_t cols, dq_format fmt, int group);
 

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_gemm_mx",
                      "dq_gemm_mx_packed", "dq_gemm_pack_bytes", "dq_gemm_pack_weights",
                      "dq_quantize", "dq_quantize_act", "dq_quantize_act_async", "dq_solve",
-                     "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
+                     "dq_solve_async", "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(dqlib):
@@ -90,6 +90,21 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert st == 5
     st = L.dq_quantize(fake, 1, 128, 256, 3, 32, None, None, None, fake, fake, None, 0, None)
     assert st == 1  # NVFP4 needs the tensor-scale pointer
+
+    # the asynchronous solve checks the same, its status pointer, and refuses timing
+    def call_async(status=fake, init_=init, **kw):
+        a = dict(args, **kw)
+        return L.dq_solve_async(a["W"], a["wt"], a["rows"], a["cols"], a["fmt"], a["group"],
+                                a["T"], ctypes.byref(init_), fake, fake, fake, fake, fake, fake,
+                                status, None, 0, None)
+
+    assert call_async(W=None) == 1
+    assert call_async(cols=250) == 1
+    assert call_async(fmt=9) == 2
+    assert call_async(status=None) == 1
+    assert call_async(status=ctypes.c_void_p(0x1002)) == 1
+    tm = dqlib._Timing()
+    assert call_async(init_=dqlib._Init(None, None, 0.0, 0, ctypes.pointer(tm))) == 1
 
 
 def test_act_arguments_are_rejected_on_the_host(dqlib):
