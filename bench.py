@@ -89,6 +89,21 @@ def counted_traffic(workload: int, fused: bool):
     return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 
 
+def settle(run_once, ms: float) -> int:
+    """Repeat run_once (one untimed step) until `ms` of wall time have passed and the GPU is
+    idle again; returns the number of repeats."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        run_once()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def to_device(w_np, dtype: str):
     import numpy as np
     import torch
@@ -107,6 +122,10 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed repeats of the step for this long before the warm-up steps, "
+                         "so that the GPU runs at its steady clock (it takes a few hundred "
+                         "milliseconds of work to reach it from idle)")
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sequential", action="store_true",
@@ -233,7 +252,11 @@ def main() -> None:
             res.append(o)
         return res
 
+    settled = [None]
+
     def timed_steps(T=None):
+        if settled[0] is None:
+            settled[0] = settle(lambda: step(T), args.settle_ms)
         for _ in range(args.warmup):
             step(T)
         torch.cuda.synchronize()
@@ -311,6 +334,8 @@ def main() -> None:
                    "matrices": [w.name for w in mats],
                    "format": mats[0].fmt, "group": mats[0].group, "T": mats[0].T,
                    "weights": mats[0].dtype, "sums": "f64"},
+        "settle": {"ms": args.settle_ms, "untimed_steps": settled[0],
+                   "why": "the GPU reaches its steady clock only after a few hundred ms of work"},
         "solve_calls": "blocking dq_solve" if (blocking[0] or args.batch) else
                        "dq_solve_async, one wait per timed region",
         "device_status": int(status.item()),
@@ -377,6 +402,7 @@ def bench_act(args, dq) -> None:
             for name, Xd, bd, codes, scales in outs:
                 dq.quantize_act_async(Xd, fmt, group, codes, scales, status, b=bd, g=g,
                                       stream=stream)
+        settled = settle(step, args.settle_ms)
         for _ in range(args.warmup):
             step()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -390,6 +416,7 @@ def bench_act(args, dq) -> None:
         elems = sum(Xd.numel() for _, Xd, _, _, _ in outs)
         algo = elems * (2.0 + 0.5 + 1.0 / group)
         results[fmt] = {"group": group, "ms_per_step": ms, "elems_per_s": elems / (ms * 1e-3),
+                        "settle_steps": settled,
                         "achieved_GBps": algo / (ms * 1e-3) / 1e9,
                         "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_step": algo}
@@ -483,6 +510,8 @@ def bench_gemm(args, dq) -> None:
                 dq.gemm_mx(m["xc"], m["xs"], m["wc"], m["ws"], m["a"], out_dtype="bf16",
                            y=m["y"], stream=stream)
 
+    settled = settle(lambda: run(mats, True), args.settle_ms)
+
     def timed(ms_list, steps, packed):
         for _ in range(args.warmup):
             run(ms_list, packed)
@@ -523,6 +552,7 @@ def bench_gemm(args, dq) -> None:
                      "timing": "back-to-back asynchronous calls between one pair of events"},
         "products": per,
         "unpacked_weights_tflops": flops / (ms_natural * 1e-3) / 1e12,
+        "settle": {"ms": args.settle_ms, "untimed_steps": settled},
     }
     if args.no_cpu:
         print(json.dumps(line), flush=True)
