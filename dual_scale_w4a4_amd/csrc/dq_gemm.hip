@@ -672,11 +672,14 @@ __global__ void k_pack_scales(const uint8_t* __restrict__ ws, uint32_t* __restri
 }
 
 struct PackedLds {
-  uint8_t x[2][kXTileB];                    // [buffer]: token stages, 64 KiB
+  uint8_t x[3][kXTileB];                    // [stage % 3]: token stages, 96 KiB
   uint8_t xs[2][kScaleTileB];               // [period parity]: token scales, 8 KiB
 };
 // the epilogue stages fp32 results of 4 waves x 32 tokens in the same memory
 static_assert(sizeof(PackedLds) >= kStageBytes, "epilogue staging does not fit");
+
+// s_waitcnt operand: at most n vector-memory operations outstanding, the other counters free
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Per-wave state of the packed-weight tile loop.
 struct PackedCtx {
@@ -688,18 +691,17 @@ struct PackedCtx {
   uint32_t sbx;       // token-scale offset of this lane's row in the scale loads
 };
 
-// Token stage load j (0..7) of this wave: LDS rows 8 (8 wave + j) .. + 7, lane j' writing row
-// 8 g + j' / 8 at chunk position j' % 8, which holds the row's logical chunk
-// (j' % 8) ^ swizzle term (the term's bit-3 part flips with the group's parity).
+// Token stage load j (0..7) of this wave into stage buffer xb: LDS rows 8 (8 wave + j) .. + 7,
+// lane j' writing row 8 g + j' / 8 at chunk position j' % 8, which holds the row's logical
+// chunk (j' % 8) ^ swizzle term (the term's bit-3 part flips with the group's parity).
 template <bool EDGE>
-__device__ __forceinline__ void packed_load_x(const PackedCtx& c, PackedLds& lds, int buf, int j,
-                                              int kb0, bool on) {
+__device__ __forceinline__ void packed_load_x(const PackedCtx& c, uint8_t* xb, int j, int kb0,
+                                              bool on) {
   uint32_t v = c.vx[j & 1];
   if (EDGE && c.t0 + c.wave * 64 + j * 8 + (c.lane >> 3) >= c.rows_x) v = kOob;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(on ? c.rxc : c.rnone,
-                                           (lds_ptr_t)(lds.x[buf] + (c.wave * 8 + j) * 1024),
-                                           16, (int)v, (int)(uint32_t)(j * 8 * c.ldb + kb0), 0,
-                                           0);
+                                           (lds_ptr_t)(xb + (c.wave * 8 + j) * 1024), 16, (int)v,
+                                           (int)(uint32_t)(j * 8 * c.ldb + kb0), 0, 0);
 }
 
 // Token scale period q: rows 64 wave .. + 63, 16 bytes each.
@@ -718,21 +720,25 @@ __device__ __forceinline__ void mfma_sel(v16f& acc, const u32x4& fa, const u32x4
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, KS, (int)sa, KS, (int)sb);
 }
 
-// k step KS of a stage: 16 products in the order (m, n). Between them, one at a time: the
-// next step's four token fragments (KS < 3) and, in the first two steps only, all of the next
-// stage's loads, so that they have half a stage to land before the barrier that ends it
-// waits for them: step 0 the weight fragments of row blocks 0 and 1, token loads 0..3 and the
-// weight scales of blocks 0 and 1; step 1 the same for blocks 2 and 3 and token loads 4..7,
-// and the token scale period (NX > 8: on the first stage of a period). A load to LDS that
-// reads nothing still writes its (zero) bytes, so loads a stage does not need are not issued.
+// Loads one stage issues (each lane): 16 weight fragments, 4 weight scale dwords, 8 token
+// loads, and on a period's first stage the token scales.
+constexpr int kStageLoads = 16 + 4 + 8;
+
+// k step KS of stage s: 16 products in the order (m, n). Between them: the next step's four
+// token fragments from LDS (KS < 3); after the last product of weight-row block m, that block's
+// fragment of this step is reloaded with stage s + 2's, since its register is free from then on
+// (and at KS 3 the block's scale dword as well); two of stage s + 2's eight token loads into
+// its LDS buffer xb; and at KS 1 of a period's first stage (NX > 8) the next period's token
+// scales. So every load has about two stages to land. Loads of stages past the last read
+// nothing (a load to LDS that reads nothing still writes its zero bytes, into a buffer no
+// longer read), and every stage issues the same number of them.
 template <bool EDGE, int KS, int NX>
-__device__ __forceinline__ void packed_kstep(v16f (&acc)[4][4], const u32x4 (&fa)[4][4],
-                                             u32x4 (&fa_next)[4][4], const u32x4 (&fb)[4],
-                                             u32x4 (&fb_next)[4], const uint8_t* lx, int xterm,
-                                             const uint32_t (&sw)[4], uint32_t (&sw_next)[4],
+__device__ __forceinline__ void packed_kstep(v16f (&acc)[4][4], u32x4 (&fa)[4][4],
+                                             const u32x4 (&fb)[4], u32x4 (&fb_next)[4],
+                                             const uint8_t* lx, int xterm, uint32_t (&sw)[4],
                                              const uint32_t (&sx)[4], const PackedCtx& c,
-                                             PackedLds& lds, int nbuf, int ns, int kb0, bool on,
-                                             int q, bool xs_on) {
+                                             PackedLds& lds, uint8_t* xb, int s2, bool on, int q,
+                                             bool xs_on) {
 #pragma unroll
   for (int t = 0; t < 16; t++) {
     const int m = t / 4, n = t % 4;
@@ -740,20 +746,15 @@ __device__ __forceinline__ void packed_kstep(v16f (&acc)[4][4], const u32x4 (&fa
     if (t % 4 == 0 && KS < 3)
       fb_next[t / 4] =
           *reinterpret_cast<const u32x4*>(lx + (t / 4) * 32 * kRowB + (((KS + 1) ^ xterm) * 16));
-    if (KS < 2) {
-      if (t % 2 == 1) {  // weight fragment (row block 2 KS + t / 8, k step (t / 2) % 4)
-        const int mb = 2 * KS + t / 8, i = (t / 2) % 4;
-        fa_next[mb][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            on ? c.rwc : c.rnone, c.va[mb], (uint32_t)((ns * 4 + i) * kPackBlockB), 0);
-      }
-      if (t % 4 == 2) packed_load_x<EDGE>(c, lds, nbuf, KS * 4 + t / 4, kb0, on);
-      if (t == 0 || t == 4) {
-        const int mb = 2 * KS + t / 4;
-        sw_next[mb] = __builtin_amdgcn_raw_buffer_load_b32(on ? c.rws : c.rnone, c.vs[mb],
-                                                           (uint32_t)(ns * kPackScaleB), 0);
-      }
-      if (KS == 1 && t == 8 && NX > 8) packed_load_xs(c, lds, q, xs_on);
+    if (n == 3) {
+      fa[m][KS] = __builtin_amdgcn_raw_buffer_load_b128(
+          on ? c.rwc : c.rnone, c.va[m], (uint32_t)((s2 * 4 + KS) * kPackBlockB), 0);
+      if (KS == 3)
+        sw[m] = __builtin_amdgcn_raw_buffer_load_b32(on ? c.rws : c.rnone, c.vs[m],
+                                                     (uint32_t)(s2 * kPackScaleB), 0);
     }
+    if (t == 1 || t == 9) packed_load_x<EDGE>(c, xb, KS * 2 + t / 8, s2 * kRowB, on);
+    if (KS == 1 && t == 8 && NX > 8) packed_load_xs(c, lds, q, xs_on);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -774,7 +775,7 @@ __device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int 
   c.rws = rsrc(p.ws, (uint32_t)nrb * (uint32_t)nst * kPackScaleB);
   c.rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
   c.rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
-  // a descriptor that reads nothing: the loads of the stage after the last go there (the loop
+  // a descriptor that reads nothing: the loads of stages after the last go there (the loop
   // body stays one basic block, so nothing can move across its barriers)
   c.rnone = rsrc(p.wc, 0u);
   c.t0 = t0;
@@ -811,23 +812,27 @@ __device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int 
   const int rx = (wt + rl) * kRowB;
   const int sx_off = (wt + rl) * kScaleRowB + 4 * h;
 
-  u32x4 fa[2][4][4];  // [stage parity][m][ks]: the weight fragments of a whole stage
+  u32x4 fa[2][4][4];  // [stage parity][m][ks]: the weight fragments of stages s and s + 1
   uint32_t sw[2][4];  // [stage parity][m]: their scale dwords
   u32x4 fb0[4], fb1[4];
   uint32_t sx[4];
 
-  // prologue: stage 0 (weights and their scales into registers, tokens into buffer 0) and
-  // token scale period 0
+  // prologue: stages 0 and 1 (weights and their scales into registers, tokens into buffers 0
+  // and 1) and token scale period 0
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
+  for (int st = 0; st < 2; st++) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      fa[0][m][i] = __builtin_amdgcn_raw_buffer_load_b128(c.rwc, c.va[m],
-                                                          (uint32_t)(i * kPackBlockB), 0);
-    sw[0][m] = __builtin_amdgcn_raw_buffer_load_b32(c.rws, c.vs[m], 0u, 0);
+    for (int m = 0; m < 4; m++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        fa[st][m][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            c.rwc, c.va[m], (uint32_t)((st * 4 + i) * kPackBlockB), 0);
+      sw[st][m] = __builtin_amdgcn_raw_buffer_load_b32(c.rws, c.vs[m],
+                                                       (uint32_t)(st * kPackScaleB), 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L.x[st], j, st * kRowB, true);
   }
-#pragma unroll
-  for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L, 0, j, 0, true);
   packed_load_xs(c, L, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -842,38 +847,41 @@ __device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int 
     for (int n = 0; n < 4; n++)
       fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
   };
-  // one stage: products from registers fa[P] / sw[P] and token buffer `buf`; the next stage
-  // (ns) into fa[P ^ 1] / sw[P ^ 1] and the other buffer
-  auto stage = [&](auto pc, auto nxc, int buf, int ns, bool on, int q, bool xs_on) {
+  // stage s: products from registers fa[P] / sw[P] and token buffer s % 3, while stage s + 2
+  // loads into the slots they free and buffer (s + 2) % 3. At its end, the loads issued before
+  // it (those of stage s + 1) are complete in this wave, and after the barrier in every wave.
+  auto stage = [&](auto pc, auto nxc, int s, int q, bool xs_on) {
     constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
-    const uint8_t* lx = L.x[buf] + rx;
-    const int kb0 = ns * kRowB;
+    const uint8_t* lx = L.x[s % 3] + rx;
+    uint8_t* xb = L.x[(s + 2) % 3];
+    const int s2 = s + 2;
+    const bool on = s2 < nst;
     __builtin_amdgcn_sched_barrier(0);
-    packed_kstep<EDGE, 0, NX>(acc, fa[P], fa[P ^ 1], fb0, fb1, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
-    packed_kstep<EDGE, 1, NX>(acc, fa[P], fa[P ^ 1], fb1, fb0, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
-    packed_kstep<EDGE, 2, NX>(acc, fa[P], fa[P ^ 1], fb0, fb1, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
-    packed_kstep<EDGE, 3, NX>(acc, fa[P], fa[P ^ 1], fb1, fb0, lx, xterm, sw[P], sw[P ^ 1], sx, c, L, buf ^ 1, ns, kb0, on, q, xs_on);
-    // this wave's loads (registers and LDS) are complete; after the barrier, everyone's
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    packed_kstep<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads + (NX > 8 ? 1 : 0)));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
   };
   stage_xs(0, 0);
   first_frags(0);
 
-  // two stages (one token scale period) per trip: stage 2 q (registers [0], buffer 0) and
-  // stage 2 q + 1 (registers [1], buffer 1); token scales of period q + 1 load during 2 q
+  // two stages (one token scale period) per trip: stage 2 q (registers [0]) and stage 2 q + 1
+  // (registers [1]); token scales of period q + 1 load during 2 q
   for (int q = 0; q < nst / 2; q++) {
     const bool more = 2 * q + 2 < nst;
     const int par = q & 1;
-    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 0, 2 * q + 1, true,
-          q + 1, more);
+    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 2 * q, q + 1, more);
     stage_xs(par, 1);
-    first_frags(1);
-    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 1, 2 * q + 2, more,
-          q + 1, false);
+    first_frags((2 * q + 1) % 3);
+    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 2 * q + 1, q + 1,
+          false);
     stage_xs(par ^ 1, 0);
-    first_frags(0);
+    first_frags((2 * q + 2) % 3);
   }
   store_tile<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
 }
