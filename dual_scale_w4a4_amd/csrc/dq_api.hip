@@ -89,7 +89,7 @@ struct Plan {
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
          off_gs = 0;
-  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, off_ymax = 0, total = 0;
+  size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, off_ymax = 0, off_epart = 0, total = 0;
 };
 
 bool shape_ok(int64_t rows, int64_t cols, int group) {
@@ -149,6 +149,10 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   if (fmt == DQ_FMT_NVFP4) {  // per-pass tensor scale: the row pass's row maxima of |y|
     p.off_ymax = o;
     o = align_up(o + sizeof(float) * (size_t)p.g_nct * m);
+  }
+  if (fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4) {  // single sweep: the first pass's W^2 partials
+    p.off_epart = o;
+    o = align_up(o + sizeof(double) * (size_t)p.f_nct * m);
   }
   p.total = o;
   return p;
@@ -278,8 +282,13 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   DQ_TRY(launch_vec(va, s));
   VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(vb, s));
-  RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
-  DQ_TRY(launch_rowstat(io.bf16, rs, s));
+  // E_i = sum_j W_ij^2 and the finite check: in their own sweep of W, or, on the single-sweep
+  // path with at least one iteration, inside the first iteration's pass
+  const bool stat_in_pass = fast && io.T > 0;
+  if (!stat_in_pass) {
+    RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
+    DQ_TRY(launch_rowstat(io.bf16, rs, s));
+  }
   if (nv) {
     ScaleArgs sa{amax, p.m, nullptr, io.init ? io.init->g0 : 0.0f, gs, io.tensor_scale, status};
     DQ_TRY(launch_tensor_scale(sa, s));
@@ -380,16 +389,21 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
 
   for (int t = 0; t < io.T; t++) {
     if (fast) {
+      double* epart = stat_in_pass && t == 0 ? at<double>(ws, p.off_epart) : nullptr;
+      fu.epart = epart;
       tm.before(DQ_K_FUSED);
       DQ_TRY(launch_fused(p.fmt, false, fu, s));
       tm.after();
+      fu.epart = nullptr;
       fa.nct = p.f_nct;
       fa.nrc = p.f_nrc;
       fa.gauge_check = 0;
       fa.row_ra = 1;
       fa.envelope = 1;
       fa.col_terms = 8 + (int)((p.f_rpc + 31) / 32);  // 8 rows per batch, then the batches
+      fa.epart = epart;
       if ((st = finalize(true, true, true)) != DQ_OK) return st;
+      fa.epart = nullptr;
     } else if (fused) {
       tm.before(DQ_K_FUSED);
       DQ_TRY(launch_sweep(p.fmt, io.bf16, kModeRow | kModeCol | kModeGauge, sw, s));

@@ -54,6 +54,7 @@ struct FusedArgs {
   int step_rows;    // rows per load step: 2 or 4
   double2* rowpart;  // [nct][m] (sum_j W t, sum_j (W - t)^2) with t = S b: R = ra * t
   double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
+  double* epart;     // first pass (or null): [nct][m] partial sums of W^2 over each tile's columns
   // final pass only: packed codes, E8M0 inner scales, the outer row scales
   uint8_t* codes;
   uint8_t* scales;
@@ -100,7 +101,8 @@ struct FinArgs {
   int nblk_rows;
   const double2* rowpart;
   int nct;
-  const double* E;
+  double* E;
+  const double* epart;  // if set: E_i = sum over the nct tiles of epart, stored into E first
   float* a;
   float* ra;
   int update_a;
@@ -178,7 +180,7 @@ hipError_t launch_act_gscale(bool bf16, const ActArgs& a, hipStream_t s);  // am
 int act_tile_cols();
 int act_amax_blocks();
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
-hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);  // a.epart: first pass
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,
                               hipStream_t s);
 

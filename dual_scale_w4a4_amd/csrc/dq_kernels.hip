@@ -213,13 +213,15 @@ struct FusedLane {
 // nonzero one (bit patterns, gmin offset by one so that a zero group never counts).
 // EMIT: the final pass; instead of the sums for the updates it stores the packed codes and
 // the E8M0 inner-scale bytes of the row (abits = bits of a_i) and keeps only the row error.
-template <int FMT, int LPG, int NH, bool PARTIAL, bool EMIT>
+template <int FMT, int LPG, int NH, bool PARTIAL, bool EMIT, bool STAT>
 __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L, float& nacc,
-                                          float& eacc, uint32_t& gmax, uint32_t& gmin,
-                                          const uint32_t (&amask)[NH], uint32_t* codes_row,
-                                          uint8_t* scales_row, uint32_t abits) {
+                                          float& eacc, double& wsq, uint32_t& gmax,
+                                          uint32_t& gmin, const uint32_t (&amask)[NH],
+                                          uint32_t* codes_row, uint8_t* scales_row,
+                                          uint32_t abits) {
   nacc = 0.0f;
   eacc = 0.0f;
+  wsq = 0.0;
 #pragma unroll
   for (int h = 0; h < NH; h++) {
     uint32_t u[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
@@ -238,6 +240,7 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
     for (int k = 0; k < 8; k++) {
       y[k] = w[k] * L.rb[8 * h + k];
       mx = fmaxf(mx, fabsf(y[k]));
+      if (STAT) wsq = fma((double)w[k], (double)w[k], wsq);  // W^2 is exact in fp64
     }
     const uint32_t mb = group_max_bits<LPG>(f2u(mx));
     gmax = max(gmax, mb);
@@ -297,11 +300,16 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
 
 // The pass. NH: 512-column halves per lane (the tile is 512 * NH columns); S: rows per load
 // step (loads run one step ahead of the rows being computed).
-template <int FMT, int G, bool PARTIAL, bool EMIT, int NH, int S>
+template <int FMT, int G, bool PARTIAL, bool EMIT, int NH, int S, bool STAT>
 __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   constexpr int LPG = G / kEpl;  // lanes per group
   constexpr int kCols = kTileCols * NH;
   __shared__ float2 smem[kWaves * (kCols > kFusedBatch * kWave ? kCols : kFusedBatch * kWave)];
+  // STAT (the first pass): each row's sum of W^2 over the tile's columns, for E_i, which the
+  // pass's finalize forms; lane partials in fp64 (every square and sum of squares of bf16
+  // values is exact or nearly so there, and never overflows), transposed and added like N
+  // and e
+  __shared__ double smem_e[STAT ? kWaves * kFusedBatch * kWave : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -353,9 +361,11 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     }
   };
   float2* R = smem + wave * (kFusedBatch * kWave);  // this wave's [8 rows][64 lanes] partials
+  double* RE = smem_e + (STAT ? wave * (kFusedBatch * kWave) : 0);
   // one row, skipped (uniformly) when it lies past the chunk; its lane partials go to LDS
   auto row_step = [&](const uint4 (&v)[NH], int64_t i, int r) {
     float n_out = 0.0f, e_out = 0.0f;
+    double q_out = 0.0;
     if (i < r_end) {
       uint32_t* codes_row = nullptr;
       uint8_t* scales_row = nullptr;
@@ -365,10 +375,11 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         scales_row = p.scales + i * (p.n / G) + col[0] / G;
         abits = f2u(p.a[i]);
       }
-      fused_row<FMT, LPG, NH, PARTIAL, EMIT>(v, L, n_out, e_out, gmax, gmin, amask, codes_row,
-                                             scales_row, abits);
+      fused_row<FMT, LPG, NH, PARTIAL, EMIT, STAT>(v, L, n_out, e_out, q_out, gmax, gmin, amask,
+                                                   codes_row, scales_row, abits);
     }
     R[r * kWave + lane] = make_float2(n_out, e_out);
+    if (STAT) RE[r * kWave + lane] = q_out;
   };
 
   // a batch is kFusedBatch / S load steps; buffers alternate so that each step's loads
@@ -418,6 +429,14 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     Er = sum8_dpp(Er);
     const int64_t i = row0 + (lane >> 3);
     if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, Er);
+    if (STAT) {
+      const double* srce = RE + (lane >> 3) * kWave + (lane & 7) * 8;
+      double Q = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) Q += srce[k];
+      Q = sum8_dpp(Q);
+      if ((lane & 7) == 0 && i < r_end) p.epart[(int64_t)ct * p.m + i] = Q;
+    }
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -641,6 +660,12 @@ __device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
     double err = 0.0;
     int flags = 0;
     if (i < p.m) {
+      if (p.epart) {  // E_i from the first pass's tile partials, in tile order
+        double e2 = 0.0;
+        for (int k = 0; k < p.nct; k++) e2 += p.epart[(int64_t)k * p.m + i];
+        p.E[i] = e2;
+        if (!(e2 <= DBL_MAX)) flags |= kStNonFinite;  // W^2 never overflows fp64: iff W is
+      }
       const double2 nd = sum_parts(p.rowpart + i, p.m, 0, 1, p.nct);
       double N = nd.x, D = nd.y;
       double rel_err = 0.0;  // error bound of N / D (single-sweep sums only)
@@ -782,36 +807,43 @@ hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, bool PARTIAL, bool EMIT, int NH, int S>
+template <int FMT, bool PARTIAL, bool EMIT, int NH, int S, bool STAT>
 static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
   switch (a.G) {
-    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT, NH, S>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, bool EMIT, int NH, int S>
+template <int FMT, bool EMIT, int NH, int S, bool STAT>
 static hipError_t fused_shape(const FusedArgs& a, dim3 grid, hipStream_t s) {
   // masking only when some tile extends past the last column
-  return a.n % (kTileCols * NH) != 0 ? fused_group<FMT, true, EMIT, NH, S>(a, grid, s)
-                                     : fused_group<FMT, false, EMIT, NH, S>(a, grid, s);
+  return a.n % (kTileCols * NH) != 0 ? fused_group<FMT, true, EMIT, NH, S, STAT>(a, grid, s)
+                                     : fused_group<FMT, false, EMIT, NH, S, STAT>(a, grid, s);
 }
 
-template <int FMT, bool EMIT>
+template <int FMT, bool EMIT, bool STAT>
 static hipError_t fused_variant(const FusedArgs& a, dim3 grid, hipStream_t s) {
-  if (a.halves == 1) return a.step_rows == 4 ? fused_shape<FMT, EMIT, 1, 4>(a, grid, s)
-                                             : fused_shape<FMT, EMIT, 1, 2>(a, grid, s);
-  return a.step_rows == 4 ? fused_shape<FMT, EMIT, 2, 4>(a, grid, s)
-                          : fused_shape<FMT, EMIT, 2, 2>(a, grid, s);
+  if (a.halves == 1) return a.step_rows == 4 ? fused_shape<FMT, EMIT, 1, 4, STAT>(a, grid, s)
+                                             : fused_shape<FMT, EMIT, 1, 2, STAT>(a, grid, s);
+  return a.step_rows == 4 ? fused_shape<FMT, EMIT, 2, 4, STAT>(a, grid, s)
+                          : fused_shape<FMT, EMIT, 2, 2, STAT>(a, grid, s);
+}
+
+template <int FMT>
+static hipError_t fused_fmt(bool emit, const FusedArgs& a, dim3 grid, hipStream_t s) {
+  if (emit) return fused_variant<FMT, true, false>(a, grid, s);
+  return a.epart ? fused_variant<FMT, false, true>(a, grid, s)
+                 : fused_variant<FMT, false, false>(a, grid, s);
 }
 
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.nct * a.nrc));
-  if (fmt == kMxFp4) return emit ? fused_variant<kMxFp4, true>(a, grid, s) : fused_variant<kMxFp4, false>(a, grid, s);
-  if (fmt == kMxInt4) return emit ? fused_variant<kMxInt4, true>(a, grid, s) : fused_variant<kMxInt4, false>(a, grid, s);
+  if (fmt == kMxFp4) return fused_fmt<kMxFp4>(emit, a, grid, s);
+  if (fmt == kMxInt4) return fused_fmt<kMxInt4>(emit, a, grid, s);
   return hipErrorInvalidValue;
 }
 
