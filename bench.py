@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": (57413.0 + 57509.0) / 2, "fetch_scale": 2.0,
+    "fetch_kib": (57417.1 + 57513.0) / 2, "fetch_scale": 2.0,
     "write_kib": (7552.0 + 7616.0) / 2, "write_scale": 1.0,
-    "sources_sha256": "1cfc4f371147b2d5f8a28d840cab8b68bc3b784b5d744cf0306fbc0f5e5790ae",
+    "sources_sha256": "8659b6f393c8313df15e092f18f5cf92d2fda74e9d9e4b5d94f17ee1924e08a7",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -64,9 +64,9 @@ ACT_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_act.hip", "dual_scale_w4a4_amd/csrc/
 # rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the two dispatches of
 # a step), scaled as above; valid only for the sources they were taken on.
 ACT_COUNTERS = {
-    "fetch_kib": 32921.7 + 114950.3, "fetch_scale": 2.0,
-    "write_kib": 17864.5 + 62526.7, "write_scale": 1.0,
-    "sources_sha256": "41ce3b95aa762c995bf302a84f1e21c59099ecf6f5eb35059aa94da4c6d7e9ee",
+    "fetch_kib": 32922.6 + 114951.7, "fetch_scale": 2.0,
+    "write_kib": 17864.9 + 62528.0, "write_scale": 1.0,
+    "sources_sha256": "1b3045fae26a6310414671bdfd2b9cdec7d390524dbbf8d8d4f4cb9ea7e7de07",
 }
 
 

@@ -102,6 +102,9 @@ bool shape_ok(int64_t rows, int64_t cols, int group) {
 
 bool fmt_ok(int fmt) { return fmt >= 0 && fmt <= 3; }
 
+// the bf16 single-sweep kernel's shapes: row and column indices within 32 bits
+bool fast_shape_ok(const Plan& p) { return p.m < INT32_MAX && p.n < INT32_MAX; }
+
 Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   Plan p;
   p.m = m;
@@ -276,7 +279,9 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   float* b0s = at<float>(ws, p.off_b0);
   const float* a_src = again ? a0s : (io.init ? io.init->a0 : nullptr);
   const float* b_src = again ? b0s : (io.init ? io.init->b0 : nullptr);
-  const bool fast = fused && io.bf16;  // the single-sweep kernel for bf16 weights
+  // the single-sweep kernel for bf16 weights (32-bit row and column indices; larger matrices
+  // take the general single-sweep kernel)
+  const bool fast = fused && io.bf16 && fast_shape_ok(p);
   const bool pass_g = nv && io.init && (io.init->flags & DQ_SOLVE_PER_PASS_G);
   VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(va, s));
@@ -808,7 +813,7 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
     if (st != DQ_OK) return st;
     tm.collect();
     if (timing) timing->used_fused = fused ? 1 : 0;
-    if (timing && fused && wt == DQ_BF16 && T > 0 && flags == 0) {
+    if (timing && fused && wt == DQ_BF16 && fast_shape_ok(p) && T > 0 && flags == 0) {
       st = time_isolated(p, ws.ptr, W, a, b, timing, stream);
       if (st != DQ_OK) return st;
     }

@@ -350,9 +350,11 @@ __device__ __forceinline__ float group_max_dpp(float v) {
   return v;
 }
 
+// (the old value 0 is the identity of the unsigned max the result feeds, which lets the
+// compiler fold the permutation into that max)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
 // max over aligned groups of LANES lanes of non-negative float bit patterns (for those the

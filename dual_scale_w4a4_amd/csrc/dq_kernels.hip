@@ -251,7 +251,9 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
     float S[8];
     uint32_t packed = 0;  // the 8 codes as nibbles, column 2k low (EMIT)
     if (FMT == kMxFp4) {
-      uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], c, 0);
+      // the four conversions write all four bytes, so the first one's other bytes may hold
+      // anything (a register that is free anyway saves clearing one)
+      uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u[0], y[0], y[1], c, 0);
       pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[2], y[3], c, 1);
       pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[4], y[5], c, 2);
       pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, y[6], y[7], c, 3);
@@ -315,16 +317,21 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int ct = blockIdx.x % p.nct;
   const int rc = blockIdx.x / p.nct;
-  const int64_t r_begin = (int64_t)rc * p.rpc;
-  const int64_t r_end = r_begin + p.rpc < p.m ? r_begin + p.rpc : p.m;
-  int64_t col[NH], lcol[NH];
+  // row and column indices fit 32 bits on this path (the host sends larger matrices to the
+  // general single-sweep kernel), which keeps the row bookkeeping in scalar registers
+  const int m = (int)p.m, n = (int)p.n;
+  const int r_begin = rc * (int)p.rpc;
+  const int r_end = r_begin + (int)p.rpc < m ? r_begin + (int)p.rpc : m;
+  int col[NH], lcol[NH];
+  uint32_t loff[NH];  // byte offset of the lane's 8 columns within a row
   bool act[NH];
   uint32_t amask[NH];
 #pragma unroll
   for (int h = 0; h < NH; h++) {
-    col[h] = (int64_t)ct * kCols + h * kTileCols + lane * kEpl;
-    act[h] = col[h] < p.n;
+    col[h] = ct * kCols + h * kTileCols + lane * kEpl;
+    act[h] = col[h] < n;
     lcol[h] = act[h] ? col[h] : 0;  // in-bounds address
+    loff[h] = (uint32_t)lcol[h] * 2u;
     amask[h] = act[h] ? 0xFFFFFFFFu : 0u;
   }
 
@@ -346,24 +353,30 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   uint32_t gmax = 0u, gmin = 0xFFFFFFFFu;
 
   // this wave's rows: batches of 8 consecutive rows, 32 rows apart across the workgroup
-  const int64_t first = r_begin + (int64_t)wave * kFusedBatch;
-  const int64_t nbatch =
+  const int first = r_begin + wave * kFusedBatch;
+  const int nbatch =
       first < r_end ? (r_end - first + kWaves * kFusedBatch - 1) / (kWaves * kFusedBatch) : 0;
   // loads of rows i .. i+S-1 from in-bounds addresses (rows past the chunk reload its first
-  // row and are skipped below; columns past n are masked in fused_row)
-  auto load = [&](int64_t i, uint4 (&buf)[S][NH]) {
+  // row and are skipped below; columns past n are masked in fused_row): a buffer descriptor
+  // per row, built in scalar registers, and the lane's 32-bit offset into it
+  auto load = [&](int i, uint4 (&buf)[S][NH]) {
 #pragma unroll
     for (int r = 0; r < S; r++) {
-      const int64_t row = i + r < r_end ? i + r : r_begin;
+      const int row = i + r < r_end ? i + r : r_begin;
+      const uint16_t* rowp = p.W + (int64_t)row * n;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(rowp), (short)0, n * 2, 0x00020000);
 #pragma unroll
-      for (int h = 0; h < NH; h++)
-        buf[r][h] = *reinterpret_cast<const uint4*>(p.W + row * p.n + lcol[h]);
+      for (int h = 0; h < NH; h++) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, loff[h], 0u, 0);
+        buf[r][h] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
     }
   };
   float2* R = smem + wave * (kFusedBatch * kWave);  // this wave's [8 rows][64 lanes] partials
   double* RE = smem_e + (STAT ? wave * (kFusedBatch * kWave) : 0);
   // one row, skipped (uniformly) when it lies past the chunk; its lane partials go to LDS
-  auto row_step = [&](const uint4 (&v)[NH], int64_t i, int r) {
+  auto row_step = [&](const uint4 (&v)[NH], int i, int r) {
     float n_out = 0.0f, e_out = 0.0f;
     double q_out = 0.0;
     if (i < r_end) {
@@ -371,8 +384,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
       uint8_t* scales_row = nullptr;
       uint32_t abits = 0u;
       if (EMIT) {
-        codes_row = reinterpret_cast<uint32_t*>(p.codes) + ((i * p.n + col[0]) >> 3);
-        scales_row = p.scales + i * (p.n / G) + col[0] / G;
+        codes_row = reinterpret_cast<uint32_t*>(p.codes) + (((int64_t)i * n + col[0]) >> 3);
+        scales_row = p.scales + (int64_t)i * (n / G) + col[0] / G;
         abits = f2u(p.a[i]);
       }
       fused_row<FMT, LPG, NH, PARTIAL, EMIT, STAT>(v, L, n_out, e_out, q_out, gmax, gmin, amask,
@@ -388,8 +401,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   static_assert(kSteps % 2 == 0, "an even number of steps per batch");
   uint4 bufA[S][NH], bufB[S][NH];
   if (nbatch > 0) load(first, bufA);
-  for (int64_t bt = 0; bt < nbatch; bt++) {
-    const int64_t row0 = first + bt * (kWaves * kFusedBatch);
+  for (int bt = 0; bt < nbatch; bt++) {
+    const int row0 = first + bt * (kWaves * kFusedBatch);
 #pragma unroll
     for (int st = 0; st < kSteps; st += 2) {
       load(row0 + (st + 1) * S, bufB);
@@ -427,15 +440,15 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     }
     N = sum8_dpp(N);
     Er = sum8_dpp(Er);
-    const int64_t i = row0 + (lane >> 3);
-    if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, Er);
+    const int i = row0 + (lane >> 3);
+    if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * m + i] = make_double2(N, Er);
     if (STAT) {
       const double* srce = RE + (lane >> 3) * kWave + (lane & 7) * 8;
       double Q = 0.0;
 #pragma unroll
       for (int k = 0; k < 8; k++) Q += srce[k];
       Q = sum8_dpp(Q);
-      if ((lane & 7) == 0 && i < r_end) p.epart[(int64_t)ct * p.m + i] = Q;
+      if ((lane & 7) == 0 && i < r_end) p.epart[(int64_t)ct * m + i] = Q;
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -456,8 +469,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         sp += (double)smem[v * kCols + c].x;
         sq += (double)smem[v * kCols + c].y;
       }
-      const int64_t j = (int64_t)ct * kCols + c;
-      if (j < p.n) p.colpart[(int64_t)rc * p.n + j] = make_double2(sp, sq);
+      const int j = ct * kCols + c;
+      if (j < n) p.colpart[(int64_t)rc * n + j] = make_double2(sp, sq);
     }
   }
   // range check: every nonzero group max in [2^-32, 2^32)
