@@ -178,6 +178,34 @@ def test_error_statuses(dq):
     assert np.array_equal(host(x["codes"]), host(y["codes"]))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_single_sweep_first_pass_row_statistics(dq, oracle_lib, fmt):
+    """On the single-sweep path for bf16 W (T >= 1) the first iteration's pass also forms
+    E_i = sum_j W_ij^2 and the finite check: a NaN or an infinity anywhere in W is reported
+    as non-finite, by the blocking call and in the asynchronous status word (bit 1); T = 0
+    solves (no iteration pass) keep the separate row-statistics sweep and match the oracle."""
+    import torch
+
+    W = rand_w(96, 1536, seed=31, dtype="bf16", outliers=3)  # bf16 bits
+    for bits, where in ((0x7F80, (5, 700)), (0x7FC1, (95, 1535)), (0xFF80, (0, 0))):
+        bad = W.copy()
+        bad[where] = bits  # +inf, a NaN, -inf
+        print(f"[solve] {fmt} bf16 with {bits:#06x} at {where}", flush=True)
+        Wd = to_device(bad, "bf16")
+        with pytest.raises(dq.DQError) as e:
+            dq.solve(Wd, fmt, 32, 4)
+        assert e.value.status == 3
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = dq.solve_outputs(Wd, fmt, 32, 4)
+        dq.solve_async(Wd, fmt, 32, 4, out, status)
+        torch.cuda.synchronize()
+        assert int(host(status)[0]) & 1
+    # T = 0: setup and emit only
+    ref = oracle_lib.solve(W, "bf16", fmt, 32, 0, diag=True)
+    gpu = dq.solve(to_device(W, "bf16"), fmt, 32, 0)
+    assert_parity(compare_solve(gpu, ref, fmt, 96, 1536), exact=True, name=f"{fmt} T=0")
+
+
 @pytest.mark.parametrize("fmt", ["int4_bf16", "nvfp4"])
 def test_subnormal_groups_on_the_two_sweep_pass(dq, oracle_lib, fmt):
     # bf16 weights with groups of subnormal values: their INT4 scale is a subnormal bf16
