@@ -41,6 +41,19 @@ COUNTERS = {
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
+# The vector-ALU roofline: 256 CUs x 4 SIMDs x 16 lanes issue one VALU lane-instruction each
+# per clock at 2.4 GHz (fp32 and fp64 adds, multiplies, fmas and conversions alike; packed
+# fp32 is not used), 39.3 * 10^12 lane-instructions/s. VALU lane-instructions per weight
+# element of each workload's dominant pass, from rocprofv3 --pmc SQ_INSTS_VALU runs (wave
+# instructions per dispatch x 64 / elements, over a step's matrices); valid only for the
+# kernel sources they were taken on.
+VALU_PEAK = 256 * 4 * 16 * 2.4e9
+VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
+VALU_COUNTERS = {
+    "per_elem": {3: 12.04, 4: 23.72, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
+    "sources_sha256": "51ad33efd2f5f4d0181407fc00590382c78526aa7bcba0c0bc8acaeaf4087f1e",
+}
+
 
 def _load(workload: int):
     import workloads
@@ -111,6 +124,17 @@ def to_device(w_np, dtype: str):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(w_np).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(w_np)).cuda()
+
+
+def valu_per_elem(workload: int, kind: str, used_fused: bool, per_pass_g: bool, batch: bool):
+    """VALU lane-instructions per element of the dominant pass, where counted on these
+    sources (the plain single-sweep pass of workload 3, the row pass of workloads 4 and 5)."""
+    c = VALU_COUNTERS
+    if per_pass_g or batch or sources_sha256(VALU_SOURCES) != c["sources_sha256"]:
+        return None
+    if kind == "fused" and not used_fused:
+        return None
+    return c["per_elem"].get(workload)
 
 
 def _dominant_kind(fmt: str) -> str:
@@ -315,6 +339,29 @@ def main() -> None:
     launch_bytes = bytes_total / max(n_kind, 1)
     achieved = bytes_total / (ms_kind * 1e-3) / 1e9
 
+    kernel_name = ("k_fused_mx" if kind == "fused" else
+                   ("k_pass (row mode)" if mats[0].dtype == "bf16" else "k_sweep (row mode)"))
+    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": counted_traffic(args.workload, kind == "fused" and used_fused),
+                "traffic_unit": "bytes per launch", "avg_launch_us": avg_launch_ms * 1e3,
+                "launches": n_kind, "bytes_per_launch": launch_bytes,
+                "timing": "isolated back-to-back launches" if iso[1] else "per-launch events",
+                "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}}
+    per_elem = valu_per_elem(args.workload, kind, used_fused, args.per_pass_g, args.batch)
+    if per_elem is not None:
+        valu = per_elem * (bytes_total / bytes_per_elem) / (ms_kind * 1e-3)
+        alu = {"lane_instructions_per_element": per_elem, "achieved": valu / 1e12,
+               "peak": VALU_PEAK / 1e12, "unit": "T VALU lane-instructions/s",
+               "frac": valu / VALU_PEAK}
+        if kind == "row":  # the two-sweep pass: its exact fp64 codes and sums bind the ALU
+            hbm = {k: roofline[k] for k in ("achieved", "peak", "unit", "frac")}
+            roofline.update(bound="alu", **{k: alu[k] for k in ("achieved", "peak", "unit", "frac")})
+            roofline["lane_instructions_per_element"] = per_elem
+            roofline["hbm"] = hbm
+        else:
+            roofline["valu"] = alu
+
     mse_final = [float(o["mse"][-1].item()) for o in outs]
     mse_first = [float(o["mse"][0].item()) for o in outs]
 
@@ -344,13 +391,7 @@ def main() -> None:
         "per_iteration": {"ms": t_iter * 1e3, "elems_per_s": elems / t_iter,
                           "GBps_one_read_of_W": iter_gbs, "frac_hbm_peak": iter_gbs / HBM_PEAK_GBS,
                           "ms_per_step_T1": t_step1 * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "k_fused_mx" if kind == "fused" else "k_pass (row mode)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counted_traffic(args.workload, kind == "fused" and used_fused),
-                     "traffic_unit": "bytes per launch", "avg_launch_us": avg_launch_ms * 1e3,
-                     "launches": n_kind, "bytes_per_launch": launch_bytes,
-                     "timing": "isolated back-to-back launches" if iso[1] else "per-launch events",
-                     "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}},
+        "roofline": roofline,
         "mse": {"first": mse_first, "final": mse_final,
                 "ratio_first_over_final": [a / b for a, b in zip(mse_first, mse_final)]},
         "cache": None if cw[2] == 0 else {
