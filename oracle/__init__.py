@@ -21,7 +21,9 @@ from typing import Dict, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdq_ref.so")
+# DQ_REF_LIB: load another build of the same source instead (the planted-mistake tests run
+# the pins against deliberately broken copies of dq_ref.c built in a scratch directory)
+LIB_PATH = os.environ.get("DQ_REF_LIB") or os.path.join(_HERE, "libdq_ref.so")
 
 FMT = {"int4_bf16": 0, "mxint4": 1, "mxfp4": 2, "nvfp4": 3}
 DTYPE = {"f32": 0, "bf16": 1}
@@ -29,11 +31,15 @@ STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_NONFINITE", 4: "E
           7: "ERR_INTERNAL"}
 
 
+GCC_FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+             "-fopenmp", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
 def build(verbose: bool = False) -> str:
     """Compile libdq_ref.so with gcc (plain C11, -O2, no FMA contraction, OpenMP)."""
-    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", "-Wno-unused-parameter",
-           os.path.join(_HERE, "dq_ref.c"), "-o", LIB_PATH + ".tmp", "-lm"]
+    if os.environ.get("DQ_REF_LIB"):
+        raise RuntimeError("DQ_REF_LIB names a prebuilt oracle library; not rebuilding it")
+    cmd = ["gcc", *GCC_FLAGS, os.path.join(_HERE, "dq_ref.c"), "-o", LIB_PATH + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -49,7 +55,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        if not os.path.exists(LIB_PATH) and not os.environ.get("DQ_REF_LIB"):
             build()
         L = ctypes.CDLL(LIB_PATH)
         P, I, I64, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double

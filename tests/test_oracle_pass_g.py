@@ -73,9 +73,18 @@ def test_power_of_two_equivariance(oracle_lib):
 
 def test_differs_from_the_frozen_scale_once_the_tile_moves(oracle_lib):
     # with g frozen at the initial tile the final g is the initial one; per pass it follows
-    # the final tile (and the two solves are different readings of the same method)
-    W = rand_w(40, 8 * G, seed=45, outliers=8)
+    # the final tile (and the two solves are different readings of the same method). Row 0
+    # holds the tile max: one value of 6 units per group and the rest at 4.5 units, which Q
+    # rounds down to 4, so the row's least-squares scale is about 1.11 and a_0 becomes 1.125;
+    # the tile max then shrinks, and so does the per-pass g.
+    W = rand_w(40, 8 * G, seed=45, outliers=0)
+    u = np.float32(np.abs(W).max() * 4)
+    W[0, :] = np.float32(0.75) * u
+    W[0, ::G] = u
     frozen = oracle_lib.solve(W, "f32", "nvfp4", G, 6)
     pp = oracle_lib.solve_pass_g(W, "f32", G, 6)
     assert frozen["g"] == _final_g(W, np.ones(40, np.float32), np.ones(8 * G, np.float32))
+    assert pp["a"][0] == np.float32(1.125)
     assert np.float32(pp["g"]) == _final_g(W, pp["a"], pp["b"])
+    assert np.float32(pp["g"]) < np.float32(frozen["g"])
+    assert not np.array_equal(pp["codes"], frozen["codes"])

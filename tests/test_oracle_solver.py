@@ -121,6 +121,44 @@ def test_quantizer_with_scales_matches_brute_force(oracle_lib, fmt):
         _check_q_brute(oracle_lib, W, fmt, group, a, b, 1.7e-5)  # a given tensor scale
 
 
+def test_scaled_tile_rounds_the_column_scale_first(oracle_lib):
+    """Reading 5 fixes the order of the two fp32 roundings of the scaled tile: X =
+    fl32(fl32(W * fl32(1/b)) * fl32(1/a)). At the top of the fp32 range the order decides
+    whether a value overflows: with W = 2^127, 1/b = 2 and 1/a = 1/4 the column scale first
+    gives fl32(2^128) = inf (a range error), the row scale first would give 2^126."""
+    from oracle import OracleError
+
+    for fmt in ("int4_bf16", "nvfp4"):  # outer scales that may be any bf16 / E4M3 value
+        group = GROUP[fmt]
+        W = np.zeros((1, group), np.float32)
+        W[0, 0] = np.float32(2.0 ** 127)
+        a = np.array([4.0], np.float32)
+        b = np.ones(group, np.float32)
+        b[0] = 0.5
+        with pytest.raises(OracleError) as e:
+            oracle_lib.quantize(W, "f32", fmt, group, a, b, 1.0 if fmt == "nvfp4" else 0.0)
+        assert e.value.status == 4  # DQR_ERR_RANGE
+        # the same magnitudes with the scales swapped stay finite in this order
+        out = oracle_lib.quantize(W, "f32", fmt, group, np.array([0.5], np.float32),
+                                  np.where(b == 0.5, np.float32(4.0), b), 1.0 if fmt == "nvfp4" else 0.0)
+        X = fb.scaled_tile(W, np.array([0.5], np.float32), np.where(b == 0.5, np.float32(4.0), b))
+        assert np.isfinite(X).all()
+        if fmt == "int4_bf16":  # (NVFP4 with g = 1 saturates its scale at this size)
+            check_q_output(out, X, fmt, group, 0.0, samples=group)
+
+
+def test_int4_scale_floor_for_the_smallest_groups(oracle_lib):
+    """Reading 1: INT4_BF16's s = max(bf16(fl32(m/7)), 2^-133). A group whose max is the
+    smallest fp32 subnormal has m/7 below half the smallest bf16 subnormal, so bf16 rounding
+    gives 0 and the floor gives s = 2^-133 (bits 0x0001); its values quantize to 0."""
+    W = np.zeros((2, 16), np.float32)
+    W[0, 3] = np.float32(2.0 ** -149)
+    W[1, 5] = -np.float32(2.0 ** -140)
+    out = oracle_lib.quantize(W, "f32", "int4_bf16", 16)
+    assert out["scales"].tolist() == [[0x0001], [0x0001]]  # both below 7 * 2^-134
+    assert not out["codes"].any()
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_zero_slices_take_scale_one(oracle_lib):
