@@ -220,7 +220,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f (&acc)[
         __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + ich;
         const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
         if (vec) {
-          *reinterpret_cast<bf16x4*>(yp) = hv;
+          __builtin_nontemporal_store(hv, reinterpret_cast<bf16x4*>(yp));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; e++)
@@ -229,7 +229,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const v16f (&acc)[
       } else {
         float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + ich;
         if (vec) {
-          *reinterpret_cast<f32x4*>(yp) = y;
+          __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(yp));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; e++)
