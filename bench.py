@@ -77,9 +77,9 @@ ACT_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_act.hip", "dual_scale_w4a4_amd/csrc/
 # rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the two dispatches of
 # a step), scaled as above; valid only for the sources they were taken on.
 ACT_COUNTERS = {
-    "fetch_kib": 32922.6 + 114951.7, "fetch_scale": 2.0,
-    "write_kib": 17864.9 + 62528.0, "write_scale": 1.0,
-    "sources_sha256": "1b3045fae26a6310414671bdfd2b9cdec7d390524dbbf8d8d4f4cb9ea7e7de07",
+    "fetch_kib": 32899.3 + 114919.3, "fetch_scale": 2.0,
+    "write_kib": 17408.0 + 60928.0, "write_scale": 1.0,
+    "sources_sha256": "3b3d55ce01ba88e5768f1918e1d05fbe3ab51306a9af5369e44c9771e4fa9730",
 }
 
 

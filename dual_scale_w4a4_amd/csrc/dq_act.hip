@@ -23,6 +23,8 @@
 #include "dq_device.h"
 #include "dq_internal.h"
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 namespace dq {
 
 constexpr int kActEpl = 16;                  // consecutive channels per lane
@@ -167,13 +169,15 @@ __global__ __launch_bounds__(kBlock) void k_act(ActArgs p) {
       const uint32_t lo = act_pack8<FMT>(x, gq, r, clamp);
       const uint32_t hi = act_pack8<FMT>(x + 8, gq, r, clamp);
       if (!PARTIAL || act) {
-        *reinterpret_cast<uint2*>(p.codes + ((i * p.n + lcol) >> 1)) = make_uint2(lo, hi);
+        // nontemporal: the codes and scales are written once and not read back here
+        const u32x2 cw = {lo, hi};
+        __builtin_nontemporal_store(cw, reinterpret_cast<u32x2*>(p.codes + ((i * p.n + lcol) >> 1)));
         if ((lane % LPG) == 0) {
           const int64_t si = i * (p.n / G) + lcol / G;
           if (FMT == kInt4Bf16)
-            static_cast<uint16_t*>(p.scales)[si] = (uint16_t)gq.scode;
+            __builtin_nontemporal_store((uint16_t)gq.scode, static_cast<uint16_t*>(p.scales) + si);
           else
-            static_cast<uint8_t*>(p.scales)[si] = (uint8_t)gq.scode;
+            __builtin_nontemporal_store((uint8_t)gq.scode, static_cast<uint8_t*>(p.scales) + si);
         }
       }
     }
