@@ -179,10 +179,12 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
 // log2(ra), so c = a_i * d_ig = 2^(floor(log2 max|y|) - 2) and the codes are those of y / c.
 // Consequently the re-quantization after the row update reproduces the same codes and the
 // same S = a d q (daiwk notes, "核心公式": row update, re-quantize, column update), and one
-// read of W gives both closed-form updates:
-//   row i:    N'_i = sum_j W_ij t_ij  with t = S b = a d q b, the reconstruction (R = ra_i t)
-//             e_i  = sum_j (W_ij - t_ij)^2, the row's reconstruction error; the finalize
-//                    recovers D'_i = sum_j t_ij^2 = e_i - E_i + 2 N'_i
+// read of W gives both closed-form updates. With t = S b = a d q b, the reconstruction
+// (R = ra_i t), and the residual r = W - t:
+//   row i:    M_i = sum_j W_ij r_ij  and  e_i = sum_j r_ij^2, the row's reconstruction error;
+//             with E_i = sum_j W_ij^2 the finalize forms N'_i = sum_j W_ij t_ij = E_i - M_i
+//             and D'_i = sum_j t_ij^2 = E_i - 2 M_i + e_i (M and e are small next to E, so
+//             their fp32 errors shrink in N' and D')
 //   column j: P_j = sum_i W_ij S_ij,   Q_j = sum_i S_ij^2
 // This holds while every value stays in fp32's normal range with exact products, which is
 // guaranteed when every nonzero group max |y| lies in [2^-32, 2^32) and every a, b in
@@ -193,9 +195,10 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs p) {
 // for power-of-two c; the matching decode returns S = code * c directly.
 //
 // Layout: a lane owns 16 columns of a 1024-column tile (two 512-column halves, each one
-// 128-bit load per row, contiguous across the wave). Products and W - t are exact in fp32;
-// per-lane sums run over 16 columns (rows) or over the chunk's rows (columns) in fp32; every
-// sum above that is fp64 in a fixed order: a row's 64 lane partials are transposed through LDS
+// 128-bit load per row, contiguous across the wave). Products and r = W - t are exact in
+// fp32 (r is one fused multiply-add, W - S b); row sums run in fp32 over at most 16 columns
+// (a lane's 16, or two neighbouring lanes' 8) and column sums over the chunk's rows; every
+// sum above that is fp64 in a fixed order: a row's lane partials are transposed through LDS
 // in batches of 8 rows and added by 8 lanes per row, and the 4 waves' column partials are
 // added through LDS at the end.
 constexpr int kFusedBatch = 8;  // rows per wave between row reductions
@@ -213,13 +216,14 @@ struct FusedLane {
 // nonzero one (bit patterns, gmin offset by one so that a zero group never counts).
 // EMIT: the final pass; instead of the sums for the updates it stores the packed codes and
 // the E8M0 inner-scale bytes of the row (abits = bits of a_i) and keeps only the row error.
+// first: the batch's first row, which starts the batch column sums Pb / Qb.
 template <int FMT, int LPG, int NH, bool PARTIAL, bool EMIT, bool STAT>
-__device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L, float& nacc,
+__device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L, float& macc,
                                           float& eacc, double& wsq, uint32_t& gmax,
                                           uint32_t& gmin, const uint32_t (&amask)[NH],
                                           uint32_t* codes_row, uint8_t* scales_row,
-                                          uint32_t abits) {
-  nacc = 0.0f;
+                                          uint32_t abits, bool first) {
+  macc = 0.0f;
   eacc = 0.0f;
   wsq = 0.0;
 #pragma unroll
@@ -288,13 +292,14 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       const int e = 8 * h + k;
-      const float t = S[k] * L.bb[e];  // the reconstruction a d q b of W_ij, exact
-      const float df = w[k] - t;       // exact: both have at most 8 significant bits
+      // the residual W_ij - t_ij with t = S b = a d q b, exact: S b is exact and both have at
+      // most 8 significant bits, so the fused multiply-add rounds nothing
+      const float df = fmaf(-S[k], L.bb[e], w[k]);
       eacc = fmaf(df, df, eacc);
       if (!EMIT) {
-        nacc = fmaf(w[k], t, nacc);
-        L.Pb[e] = fmaf(w[k], S[k], L.Pb[e]);
-        L.Qb[e] = fmaf(S[k], S[k], L.Qb[e]);
+        macc = fmaf(w[k], df, macc);
+        L.Pb[e] = first ? w[k] * S[k] : fmaf(w[k], S[k], L.Pb[e]);
+        L.Qb[e] = first ? S[k] * S[k] : fmaf(S[k], S[k], L.Qb[e]);
       }
     }
   }
@@ -379,6 +384,12 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   auto row_step = [&](const uint4 (&v)[NH], int i, int r) {
     float n_out = 0.0f, e_out = 0.0f;
     double q_out = 0.0;
+    // a batch's first row always lies inside the chunk (nbatch counts batches that start
+    // before r_end); were it skipped, the batch column sums would still restart at zero
+    if (r == 0 && !EMIT && !(i < r_end)) {
+#pragma unroll
+      for (int e = 0; e < 8 * NH; e++) L.Pb[e] = L.Qb[e] = 0.0f;
+    }
     if (i < r_end) {
       uint32_t* codes_row = nullptr;
       uint8_t* scales_row = nullptr;
@@ -389,7 +400,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         abits = f2u(p.a[i]);
       }
       fused_row<FMT, LPG, NH, PARTIAL, EMIT, STAT>(v, L, n_out, e_out, q_out, gmax, gmin, amask,
-                                                   codes_row, scales_row, abits);
+                                                   codes_row, scales_row, abits, r == 0);
     }
     R[r * kWave + lane] = make_float2(n_out, e_out);
     if (STAT) RE[r * kWave + lane] = q_out;
@@ -418,25 +429,40 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (!EMIT) {
+    if (!EMIT) {  // the next batch's first row restarts Pb / Qb
 #pragma unroll
       for (int e = 0; e < 8 * NH; e++) {
         L.P[e] += L.Pb[e];
         L.Q[e] += L.Qb[e];
-        L.Pb[e] = L.Qb[e] = 0.0f;
       }
     }
 
-    // 8 rows done: 8 lanes per row add 8 lane partials each in fp64 (transposed through
-    // LDS), then across the 8 lanes in a fixed order
+    // 8 rows done: 8 lanes per row add 8 lane partials each (transposed through LDS), then
+    // across the 8 lanes in a fixed order. With 8 columns per lane, neighbouring lanes'
+    // partials are first added in fp32 (a 16-column sum, inside the same error bound as a
+    // lane's 16 columns); every addition above is fp64.
     __builtin_amdgcn_wave_barrier();
     const float2* src = R + (lane >> 3) * kWave + (lane & 7) * 8;
-    double N = 0.0, Er = 0.0;
+    float2 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const float2 v = src[k];
-      N += (double)v.x;
-      Er += (double)v.y;
+    for (int k = 0; k < 8; k++) v[k] = src[k];
+    double N, Er;
+    if (NH == 1) {
+      N = (double)(v[0].x + v[1].x);
+      Er = (double)(v[0].y + v[1].y);
+#pragma unroll
+      for (int k = 2; k < 8; k += 2) {
+        N += (double)(v[k].x + v[k + 1].x);
+        Er += (double)(v[k].y + v[k + 1].y);
+      }
+    } else {
+      N = (double)v[0].x;
+      Er = (double)v[0].y;
+#pragma unroll
+      for (int k = 1; k < 8; k++) {
+        N += (double)v[k].x;
+        Er += (double)v[k].y;
+      }
     }
     N = sum8_dpp(N);
     Er = sum8_dpp(Er);
@@ -684,14 +710,27 @@ __device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
       double rel_err = 0.0;  // error bound of N / D (single-sweep sums only)
       const double ai = (double)p.a[i];
       if (p.row_ra) {
-        // single-sweep sums: (N', e) with R = ra_i t; D' = e - E + 2 N' (all terms >= 0)
-        const double e = D, Np = N;
+        // single-sweep sums: M = sum W r and e = sum r^2 with the residual r = W - t and
+        // R = ra_i t; N' = sum W t = E - M and D' = sum t^2 = E - 2 M + e
+        const double M = N, e = D, Ei = p.E[i];
         err = e;
-        const double Dp = fmax(e - p.E[i] + 2.0 * Np, 0.0);
+        const double Np = Ei - M;
+        const double Dp = Ei - 2.0 * M + e;
+        // Inside the envelope a row with a nonzero code has D' >= 2^-114 (its largest |W| is
+        // at least 2^-56 and t there at least half of it); D' below 2^-200 means every code
+        // of the row is 0 (W zero, or so small that y = W rb underflowed): D = 0, a = 1.
+        const bool zero_row = !(Dp >= 0x1p-200);
         const double r = (double)p.ra[i];
-        N = Np * r;
-        D = Np > 0.0 ? Dp * r * r : 0.0;  // N' = 0 exactly when every code is 0
-        rel_err = kRowSumErr * (1.0 + (e + p.E[i] + 2.0 * Np) / fmax(Dp, 1e-300));
+        N = zero_row ? 0.0 : Np * r;
+        D = zero_row ? 0.0 : Dp * r * r;
+        // error bounds: E's fp64 sums (no chain longer than n/64 + 64 additions), the fp32
+        // lane sums (sum |W r| <= sqrt(E e) by Cauchy-Schwarz, sum r^2 = e) and the two fp64
+        // operations here
+        const double eE = ((double)p.n * (1.0 / 64.0) + 64.0) * 0x1p-53 * Ei;
+        const double cs = sqrt(Ei * e) * (1.0 + 0x1p-20);
+        const double dN = eE + kRowSumErr * cs + 0x1p-50 * (Ei + fabs(M));
+        const double dD = eE + kRowSumErr * (2.0 * cs + e) + 0x1p-50 * (Ei + 2.0 * fabs(M) + e);
+        rel_err = zero_row ? 0.0 : dN / Np + dD / Dp;
       } else {
         err = fmax(p.E[i] - 2.0 * ai * N + ai * ai * D, 0.0);
       }

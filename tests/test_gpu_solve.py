@@ -118,6 +118,33 @@ def test_single_sweep_falls_back_outside_its_range(dq, oracle_lib):
     assert_parity(compare_solve(gpu, ref, "mxfp4", 64, 512), exact=True, name="extreme")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_single_sweep_row_whose_scaled_values_underflow(dq, oracle_lib, fmt):
+    # Row 7 holds bf16 subnormals of at most 3 * 2^-133, so while b >= 2^20 (it starts at
+    # 2^22 and moves at most two steps in these iterations) every y = fl32(W rb) of that
+    # row rounds to 0 and all its codes are 0 (scale 1 for the slice), although its sum of
+    # squares is not 0. The other rows' group maxima stay inside the single-sweep range, so
+    # the fast path must keep the solve (no fallback) and give that row a = 1 from 4.
+    rows, cols, T = 64, 512, 4
+    Wb = rand_w(rows, cols, seed=23, dtype="bf16")
+    rng = np.random.default_rng(24)
+    Wb[7] = (rng.integers(1, 4, cols) | (rng.integers(0, 2, cols) << 15)).astype(np.uint16)
+    a0 = np.ones(rows, np.float32)
+    a0[7] = 4.0
+    b0 = np.full(cols, 2.0 ** 22, np.float32)
+    print(f"[solve] underflow row {fmt}", flush=True)
+    gpu = dq.solve(to_device(Wb, "bf16"), fmt, 32, T, a0=a0, b0=b0, timing=True)
+    assert gpu["used_fused"]
+    two = dq.solve(to_device(Wb, "bf16"), fmt, 32, T, a0=a0, b0=b0, two_sweep=True)
+    for k in ("a", "b", "codes", "scales"):
+        assert np.array_equal(host(gpu[k]), host(two[k])), k
+    ref = oracle_lib.solve(Wb, "bf16", fmt, 32, T, a0=a0, b0=b0, diag=True)
+    exact = float(ref["margin"].min()) > 1e-9
+    assert_parity(compare_solve(gpu, ref, fmt, rows, cols), exact=exact, name=fmt)
+    assert host(gpu["a"])[7] == 1.0
+    assert not np.any(fb.unpack_codes(host(gpu["codes"]), fmt)[7])
+
+
 def test_zero_slices(dq, oracle_lib):
     for fmt in ("int4_bf16", "mxfp4", "nvfp4"):
         group = 16
