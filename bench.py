@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": (57417.1 + 57513.0) / 2, "fetch_scale": 2.0,
+    "fetch_kib": (57413.0 + 57509.0) / 2, "fetch_scale": 2.0,
     "write_kib": (7552.0 + 7616.0) / 2, "write_scale": 1.0,
-    "sources_sha256": "8659b6f393c8313df15e092f18f5cf92d2fda74e9d9e4b5d94f17ee1924e08a7",
+    "sources_sha256": "ac1304af39ab6801b1df7d3f0e454241789aec59f48459827cdb84c60000989e",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -50,8 +50,8 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {3: 12.04, 4: 23.72, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
-    "sources_sha256": "51ad33efd2f5f4d0181407fc00590382c78526aa7bcba0c0bc8acaeaf4087f1e",
+    "per_elem": {3: 10.93, 4: 23.72, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
+    "sources_sha256": "df0607b88a74c11dc4da9132c59ac23f14678360e59d6855c7bf116743ef8b0a",
 }
 
 
