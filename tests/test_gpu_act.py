@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import workloads
+import fmt_brute as fb
 from cases import adversarial_w
 from parity import host, to_device
 
@@ -70,6 +71,52 @@ def test_act_nvfp4_given_tensor_scale(dq, oracle_lib):
     X = workloads.activations(50, 2048, seed=5)
     b = workloads.act_column_scales(2048, seed=5)
     _check(dq, oracle_lib, X, "bf16", "nvfp4", 16, b, g=0.0071, name="given-g")
+
+
+def _nvfp4_tie_rows(g, rows, cols, seed):
+    """Rows whose 16-element groups each fix an E4M3 scale s (their first element is the one
+    of fl32(s * fl32(6 g)) and its neighbours with u = s exactly) and put the other elements
+    on E2M1 decision points times d = fl32(s g), or one fp32 step either side, with random
+    signs."""
+    rng = np.random.default_rng(seed)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    svals = fb.E4M3_POS_VALS[(fb.E4M3_POS_VALS >= 2.0 ** -6) & (fb.E4M3_POS_VALS <= 448.0)]
+    g = np.float32(g)
+    sixg = np.float32(6.0 * np.float64(g))
+    X = np.zeros((rows, cols), np.float32)
+    for i in range(rows):
+        for k in range(cols // 16):
+            mx = None
+            while mx is None:  # some s are no fl32(mx / fl32(6 g)): draw another
+                s = np.float32(rng.choice(svals))
+                mx0 = np.float32(np.float64(s) * np.float64(sixg))
+                cands = [mx0, np.nextafter(mx0, np.float32(np.inf)), np.nextafter(mx0, np.float32(0))]
+                ok = [c for c in cands if np.float32(np.float64(c) / np.float64(sixg)) == s]
+                mx = ok[0] if ok else None
+            d = np.float32(np.float64(s) * np.float64(g))
+            base = (mids[rng.integers(0, 7, 15)] * np.float64(d)).astype(np.float32)
+            step = rng.integers(-1, 2, 15)
+            near = np.where(step > 0, np.nextafter(base, np.float32(np.inf)),
+                            np.where(step < 0, np.nextafter(base, np.float32(0)), base))
+            sign = np.where(rng.integers(0, 2, 15) == 1, -1, 1).astype(np.float32)
+            X[i, 16 * k] = mx
+            X[i, 16 * k + 1:16 * k + 16] = sign * near
+    return X
+
+
+def test_act_nvfp4_ties_at_non_power_of_two_scales(dq, oracle_lib):
+    # With g = 3/256 the decision points times d are fp32 values (exact ties); with g =
+    # 0.0071 they are not, and the elements lie within an ulp of a tie on either side. Row 5
+    # is scaled up so that its scale saturates at 448 (quotients beyond 8, clamped before
+    # the fp32 quotient), and the last call has d below 2^-100, which takes the double
+    # quotient.
+    for g in (3.0 / 256.0, 0.0071):
+        X = _nvfp4_tie_rows(g, 24, 512, seed=int(g * 1e4))
+        X[5] *= np.float32(64.0)
+        _check(dq, oracle_lib, X, "f32", "nvfp4", 16, None, g=g, name=f"nv-ties g={g}")
+    g = float(np.float32(1.3 * 2.0 ** -110))
+    X = _nvfp4_tie_rows(g, 8, 256, seed=3)
+    _check(dq, oracle_lib, X, "f32", "nvfp4", 16, None, g=g, name="nv-ties tiny g")
 
 
 def test_act_group_scales_outside_the_conversion_range(dq, oracle_lib):
