@@ -74,60 +74,6 @@ __device__ __forceinline__ void act_unpack(const ActLoad<BF>& L, float (&w)[kAct
   }
 }
 
-// ------------------------------------------------------------------ NVFP4 in fp32 only
-// The group scale: NVFP4 takes u = fl32(mx / fl32(6 g)). With r6 = 1 / fl32(6 g) correctly
-// rounded in fp64, fl32(mx * r6) is that value: mx * r6 lies within 2^-52 (relative) of the
-// quotient, and a quotient of two fp32 values is an fp32 value or lies at least 2^-47
-// (relative) from every midpoint between fp32 values, so both round to the same fp32 value.
-// The rest of the rule is the one group_scale applies.
-__device__ __forceinline__ GroupQ nv_group_scale(float mx, float g, double r6) {
-  GroupQ r;
-  float s = 1.0f;
-  if (mx > 0.0f) s = fmaxf(e4m3_rne_sat((float)((double)mx * r6)), 0x1p-9f);
-  r.d = s * g;
-  r.scode = e4m3_bits(s);
-  r.rd = __builtin_amdgcn_rcpf(r.d);  // within one ulp of 1 / d
-  r.sc = 1.0f;
-  r.ds = r.d;
-  r.hds = 0.5f * r.d;
-  return r;
-}
-
-// The code of x / d rounded onto E2M1, in fp32: t = |x| rd and one correction give t1 within
-// one ulp of |x| / d (the correction's own error is below 2^-45 relative, as rd is within one
-// ulp), and t1 equals |x| / d where that is an fp32 value. The residual |x| - t1 d is then
-// exact, so its sign says on which side of t1 the quotient lies, and z below is the quotient
-// rounded to odd (t1 itself when exact, else the odd one of the two fp32 values around it).
-// E2M1's decision points (1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5) are even fp32 values, so z lies on
-// the same side of each as |x| / d and equals one only at a tie: rounding z onto E2M1 (the
-// hardware conversion with scale 1) gives the code of |x| / d. |x| is first clamped to 8 d:
-// every quotient of 5 or more takes the saturated code 6, and below 8 nothing overflows and
-// the residuals stay exact. Valid for 2^-100 <= d <= 2^100; the caller checks that.
-__device__ __forceinline__ float nv_odd_quotient(float x, float d, float rd, float d8) {
-  const float ax = fminf(fabsf(x), d8);
-  const float t = ax * rd;
-  const float t1 = fmaf(fmaf(-t, d, ax), rd, t);
-  const uint32_t rb = f2u(fmaf(-t1, d, ax));  // +0 when exact
-  const uint32_t z = (f2u(t1) - (rb >> 31)) | min(rb << 1, 1u);
-  return u2f(z | (f2u(x) & 0x80000000u));
-}
-
-// 8 NVFP4 codes as nibbles (column 2k low) through nv_odd_quotient
-__device__ __forceinline__ uint32_t nv_pack8_fast(const float* x, float d, float rd) {
-  const float d8 = 8.0f * d;
-  uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      0u, nv_odd_quotient(x[0], d, rd, d8), nv_odd_quotient(x[1], d, rd, d8), 1.0f, 0);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[2], d, rd, d8), nv_odd_quotient(x[3], d, rd, d8), 1.0f, 1);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[4], d, rd, d8), nv_odd_quotient(x[5], d, rd, d8), 1.0f, 2);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[6], d, rd, d8), nv_odd_quotient(x[7], d, rd, d8), 1.0f, 3);
-  const uint32_t mag = pk & 0x77777777u;  // keep the sign only where the magnitude is
-  const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;  // nonzero (no -0 code)
-  return mag | (pk & nz);
-}
-
 // 8 codes as nibbles (column 2k low) from 8 scaled values
 template <int FMT>
 __device__ __forceinline__ uint32_t act_pack8(const float* x, const GroupQ& gq, double r,

@@ -1,6 +1,7 @@
 // Host-side build of the HIP library's codec header, so that its rounding, projection and
 // per-group quantizer functions can be checked exhaustively on the CPU (tests/test_device_codecs.py).
 // No kernel is launched from here.
+#include <float.h>
 #include <stdint.h>
 
 #include "../dual_scale_w4a4_amd/csrc/dq_device.h"
@@ -160,6 +161,56 @@ extern "C" int64_t h_code64_mismatches(int fmt, const float* d, int64_t nd) {
         }
       }
     }
+  }
+  return bad;
+}
+
+// nv_odd_quotient followed by rounding onto E2M1 (e2m1_mag, as the hardware conversion with
+// scale 1 rounds), against the code of the exact quotient, at and 1..5 fp32 steps around every
+// E2M1 decision point, at quotients 0, 6, 7.99, 8, 9, 100 and 10^6, and at |x| = 10^38 and the
+// largest float (whose product with 1 / d overflows for small d), all with both signs, with
+// the reciprocal at, and one ulp either side of, the correctly rounded 1 / d (the device
+// takes v_rcp_f32, within one ulp); for divisors in [2^-100, 2^100]. Returns the mismatch
+// count.
+extern "C" int64_t h_nv_odd_mismatches(const float* d, int64_t nd) {
+  static const double pts[14] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                                 0.0,  6.0,  7.99, 8.0,  9.0, 100.0, 1e6};
+  int64_t bad = 0;
+  for (int64_t t = 0; t < nd; t++) {
+    const float dv = d[t];
+    const float rd0 = (float)(1.0 / (double)dv);
+    const float rds[3] = {rd0, nextafterf(rd0, INFINITY), nextafterf(rd0, 0.0f)};
+    for (int b = 0; b < 28; b++) {
+      const double h = (b < 14 ? 1.0 : -1.0) * pts[b % 14];
+      const float x0 = (float)(h * (double)dv);
+      float xs[11];
+      xs[0] = x0;
+      float up = x0, dn = x0;
+      for (int k = 1; k <= 5; k++) {
+        up = nextafterf(up, INFINITY);
+        dn = nextafterf(dn, -INFINITY);
+        xs[2 * k - 1] = up;
+        xs[2 * k] = dn;
+      }
+      for (int ix = 0; ix < 11; ix++) {
+        const float x = xs[ix];
+        const double qd = (double)x / (double)dv;
+        const double ref = qd < 0.0 ? -ref_e2m1(-qd) : ref_e2m1(qd);
+        for (int r = 0; r < 3; r++) {
+          const float z = dq::nv_odd_quotient(x, dv, rds[r], 8.0f * dv);
+          const float m = dq::e2m1_mag(fabsf(z));
+          const double got = z < 0.0f ? -(double)m : (double)m;
+          if (got != ref) bad++;
+        }
+      }
+    }
+    const float big[4] = {1e38f, -1e38f, FLT_MAX, -FLT_MAX};
+    for (int k = 0; k < 4; k++)
+      for (int r = 0; r < 3; r++) {
+        const float z = dq::nv_odd_quotient(big[k], dv, rds[r], 8.0f * dv);
+        const float m = dq::e2m1_mag(fabsf(z));
+        if ((z < 0.0f ? -(double)m : (double)m) != (big[k] < 0.0f ? -6.0 : 6.0)) bad++;
+      }
   }
   return bad;
 }

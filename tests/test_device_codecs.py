@@ -163,6 +163,22 @@ def test_double_quotient_codes_at_boundaries(H):
     assert H.h_code64_mismatches(3, _p(d), ctypes.c_int64(d.size)) == 0
 
 
+def test_nvfp4_odd_quotient_codes_at_boundaries(H):
+    # the fp32 NVFP4 codes of the activation quantizer and the two-sweep pass: divisors
+    # fl32(s g) for every positive E4M3 value s and tensor scales g across the range, plus
+    # random fp32 divisors, all within [2^-100, 2^100] where that path is taken
+    H.h_nv_odd_mismatches.restype = ctypes.c_int64
+    rng = np.random.default_rng(11)
+    s = fb.E4M3_POS_VALS[fb.E4M3_POS_VALS > 0]
+    g = np.concatenate([np.exp(rng.uniform(-60, 60, 40)), [2.0 ** -90, 1.0, 1.0 / 3.0, 0.0071]])
+    d = (s[None, :].astype(np.float32) * g[:, None].astype(np.float32)).reshape(-1)
+    r = (rng.uniform(1, 2, 3000) * 2.0 ** rng.integers(-100, 100, 3000)).astype(np.float32)
+    d = np.concatenate([d, r])
+    d = d[(d >= 2.0 ** -100) & (d <= 2.0 ** 100)].astype(np.float32)
+    assert d.size > 8000
+    assert H.h_nv_odd_mismatches(_p(d), ctypes.c_int64(d.size)) == 0
+
+
 @pytest.mark.parametrize("fmt,fid", [("int4_bf16", 0), ("nvfp4", 3)])
 @pytest.mark.parametrize("group", [16, 32, 64])
 def test_double_quotient_group_quantizer_matches_oracle(H, oracle_lib, fmt, fid, group):
