@@ -16,7 +16,7 @@
 // next batch, issued before the current rows are computed.
 //
 // Codes come from the snapped double quotient (code64): exact, and already in fp64 for the
-// sums. Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact
+// sums. NVFP4's group scale takes u = fl32(mx / fl32(6 g)) as fl32(mx r6) (nv_group_scale). Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact
 // product in fp64 and is accumulated in fp64 in a fixed order; a row's 64 lane partials are
 // transposed through LDS every 8 rows and added by 8 lanes per row, and the four waves'
 // column partials are added through LDS at the end. No floating-point atomics.
@@ -36,7 +36,8 @@ constexpr int kPassCols = kWave * kPassEpl;  // 1024 columns per tile
 template <int FMT, int LPG, int MODE, bool PARTIAL>
 __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[kPassEpl],
                                          const double (&bbd)[kPassEpl], float ra, float ai,
-                                         float g, float sixg, uint32_t amask, double& nacc,
+                                         float g, float sixg, double r6, uint32_t amask,
+                                         double& nacc,
                                          double& dacc, double (&P)[kPassEpl],
                                          double (&Q)[kPassEpl], int& flags, uint32_t* code_word,
                                          void* scale_ptr, float& ymax) {
@@ -69,7 +70,7 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
     flags |= kStRange;
     gm = 0.0f;
   }
-  const GroupQ gq = group_scale<FMT>(gm, g, sixg);
+  const GroupQ gq = FMT == kNvFp4 ? nv_group_scale(gm, g, r6) : group_scale<FMT>(gm, g, sixg);
   const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
   double q[E];  // the codes as values
   if (FMT == kInt4Bf16 && __any(int4_needs_clamp(gq.d))) {  // rare: a subnormal scale
@@ -157,9 +158,11 @@ __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
     }
   }
   float g = 1.0f, sixg = 6.0f;
+  double r6 = 0.0;  // 1 / fl32(6 g), correctly rounded
   if (FMT == kNvFp4) {
     g = p.gs[0];
     sixg = p.gs[1];
+    r6 = 1.0 / (double)sixg;
   }
   double P[E], Q[E];
 #pragma unroll
@@ -208,8 +211,8 @@ __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
         scale_ptr = FMT == kInt4Bf16 ? (void*)(static_cast<uint16_t*>(p.scales) + si)
                                      : (void*)(static_cast<uint8_t*>(p.scales) + si);
       }
-      pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, amask, nacc, dacc, P, Q,
-                                        flags, code_word, scale_ptr, ym);
+      pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, r6, amask, nacc, dacc, P,
+                                        Q, flags, code_word, scale_ptr, ym);
     }
     if (ROW) R[r * kWave + lane] = make_double2(nacc, dacc);
     if (YMAX) Ry[r * kWave + lane] = ym;
