@@ -172,8 +172,13 @@ __global__ __launch_bounds__(kBlock) void k_act(ActArgs p) {
         // fp32 codes unless a group of the wave has a divisor outside [2^-100, 2^100]: those
         // rows take the double quotient
         if (__all(gq.d >= 0x1p-100f && gq.d <= 0x1p100f)) {
-          lo = nv_pack8_fast(x, gq.d, gq.rd);
-          hi = nv_pack8_fast(x + 8, gq.d, gq.rd);
+          if (__any(!(gm < 7.0f * gq.d))) {  // some scale saturated at 448
+            lo = nv_pack8_fast<true>(x, gq.d, gq.rd);
+            hi = nv_pack8_fast<true>(x + 8, gq.d, gq.rd);
+          } else {
+            lo = nv_pack8_fast<false>(x, gq.d, gq.rd);
+            hi = nv_pack8_fast<false>(x + 8, gq.d, gq.rd);
+          }
         } else {
           const double r = recip64(gq.d);
           lo = act_pack8<FMT>(x, gq, r, false);

@@ -330,9 +330,11 @@ __device__ __forceinline__ GroupQ nv_group_scale(float mx, float g, double r6) {
 // the same side of each as |x| / d and equals one only at a tie: rounding z onto E2M1 (the
 // hardware conversion with scale 1) gives the code of |x| / d. |x| is first clamped to 8 d:
 // every quotient of 5 or more takes the saturated code 6, and below 8 nothing overflows and
-// the residuals stay exact. Valid for 2^-100 <= d <= 2^100; the caller checks that.
+// the residuals stay exact. Valid for 2^-100 <= d <= 2^100; the caller checks that. CLAMP =
+// false leaves the clamp out where the caller knows every |x| < 7 d.
+template <bool CLAMP = true>
 DQ_HD float nv_odd_quotient(float x, float d, float rd, float d8) {
-  const float ax = fminf(fabsf(x), d8);
+  const float ax = CLAMP ? fminf(fabsf(x), d8) : fabsf(x);
   const float t = ax * rd;
   const float t1 = fmaf(fmaf(-t, d, ax), rd, t);
   const uint32_t rb = f2u(fmaf(-t1, d, ax));  // +0 when exact
@@ -340,17 +342,16 @@ DQ_HD float nv_odd_quotient(float x, float d, float rd, float d8) {
   return u2f(z | (f2u(x) & 0x80000000u));
 }
 
-// 8 NVFP4 codes as nibbles (column 2k low) through nv_odd_quotient
+// 8 NVFP4 codes as nibbles (column 2k low) through nv_odd_quotient. CLAMP = false when no
+// quotient of the wave's groups can reach 8 (every group max below 7 d).
+template <bool CLAMP>
 __device__ __forceinline__ uint32_t nv_pack8_fast(const float* x, float d, float rd) {
   const float d8 = 8.0f * d;
-  uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      0u, nv_odd_quotient(x[0], d, rd, d8), nv_odd_quotient(x[1], d, rd, d8), 1.0f, 0);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[2], d, rd, d8), nv_odd_quotient(x[3], d, rd, d8), 1.0f, 1);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[4], d, rd, d8), nv_odd_quotient(x[5], d, rd, d8), 1.0f, 2);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-      pk, nv_odd_quotient(x[6], d, rd, d8), nv_odd_quotient(x[7], d, rd, d8), 1.0f, 3);
+  auto z = [&](int k) { return nv_odd_quotient<CLAMP>(x[k], d, rd, d8); };
+  uint32_t pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, z(0), z(1), 1.0f, 0);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, z(2), z(3), 1.0f, 1);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, z(4), z(5), 1.0f, 2);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, z(6), z(7), 1.0f, 3);
   const uint32_t mag = pk & 0x77777777u;  // keep the sign only where the magnitude is
   const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;  // nonzero (no -0 code)
   return mag | (pk & nz);
