@@ -37,7 +37,7 @@ COUNTERS = {
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
     "fetch_kib": (57413.0 + 57509.0) / 2, "fetch_scale": 2.0,
     "write_kib": (7552.0 + 7616.0) / 2, "write_scale": 1.0,
-    "sources_sha256": "ac1304af39ab6801b1df7d3f0e454241789aec59f48459827cdb84c60000989e",
+    "sources_sha256": "d6a7f238efcce94b6f041b3f80df7725342e1c0cee080794f2dd0ae6735bf5b4",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -50,8 +50,8 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {3: 10.93, 4: 23.72, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
-    "sources_sha256": "df0607b88a74c11dc4da9132c59ac23f14678360e59d6855c7bf116743ef8b0a",
+    "per_elem": {3: 10.93, 4: 23.23, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
+    "sources_sha256": "e17378c3e8c58da280ac36cfefda4645cab441c184451454064194070c414053",
 }
 
 
@@ -77,9 +77,9 @@ ACT_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_act.hip", "dual_scale_w4a4_amd/csrc/
 # rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the two dispatches of
 # a step), scaled as above; valid only for the sources they were taken on.
 ACT_COUNTERS = {
-    "fetch_kib": 32899.3 + 114919.3, "fetch_scale": 2.0,
+    "fetch_kib": 32899.6 + 114917.6, "fetch_scale": 2.0,
     "write_kib": 17408.0 + 60928.0, "write_scale": 1.0,
-    "sources_sha256": "3b3d55ce01ba88e5768f1918e1d05fbe3ab51306a9af5369e44c9771e4fa9730",
+    "sources_sha256": "9d59bf2a41301e8bdd982078477c37dc1173e20c2ef0fdaf49ca9d4bb64b4288",
 }
 
 
