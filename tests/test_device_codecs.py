@@ -163,6 +163,30 @@ def test_double_quotient_codes_at_boundaries(H):
     assert H.h_code64_mismatches(3, _p(d), ctypes.c_int64(d.size)) == 0
 
 
+def test_nvfp4_scale_quotient_by_fp64_reciprocal():
+    # NVFP4's u = fl32(mx / fl32(6 g)) is taken on the GPU as fl32(mx * r6) with
+    # r6 = 1 / fl32(6 g) correctly rounded in fp64 (both fp64 operations are IEEE there, as
+    # here): equal for random values over the whole range, for mx next to multiples of
+    # fl32(6 g) by an E4M3 value (the quotients that matter most) and for subnormal mx
+    rng = np.random.default_rng(13)
+    six = np.float32(6.0)
+    g = np.concatenate([np.exp(rng.uniform(-80, 80, 300)), [1.0, 1.0 / 3.0, 0.0071, 2.0 ** -126]])
+    sixg = (six * g.astype(np.float32)).astype(np.float32)
+    sixg = sixg[np.isfinite(sixg) & (sixg > 0)]
+    s = fb.E4M3_POS_VALS[fb.E4M3_POS_VALS > 0]
+    for sg in sixg:
+        r6 = 1.0 / np.float64(sg)
+        mx = np.concatenate([
+            (s * np.float64(sg)).astype(np.float32),
+            (rng.uniform(0, 1, 400) * 2.0 ** rng.integers(-149, 128, 400)).astype(np.float32)])
+        mx = np.concatenate([mx, np.nextafter(mx, np.float32(np.inf)), np.nextafter(mx, np.float32(0))])
+        mx = mx[np.isfinite(mx) & (mx > 0)]
+        with np.errstate(over="ignore", under="ignore"):
+            want = (mx.astype(np.float64) / np.float64(sg)).astype(np.float32)
+            got = (mx.astype(np.float64) * r6).astype(np.float32)
+        assert np.array_equal(want, got), (sg, mx[want != got][:4])
+
+
 def test_nvfp4_odd_quotient_codes_at_boundaries(H):
     # the fp32 NVFP4 codes of the activation quantizer and the two-sweep pass: divisors
     # fl32(s g) for every positive E4M3 value s and tensor scales g across the range, plus
