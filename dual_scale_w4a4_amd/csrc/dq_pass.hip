@@ -16,7 +16,9 @@
 // next batch, issued before the current rows are computed.
 //
 // Codes come from the snapped double quotient (code64): exact, and already in fp64 for the
-// sums. NVFP4's group scale takes u = fl32(mx / fl32(6 g)) as fl32(mx r6) (nv_group_scale). Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact
+// sums (NVFP4's final pass takes the fp32 codes of nv_pack8_fast, exact as well, and decodes
+// them for its row error). NVFP4's group scale takes u = fl32(mx / fl32(6 g)) as fl32(mx r6)
+// (nv_group_scale). Sums: every term (W * q * b, (q * b)^2, W * a * d * q, (a * d * q)^2) is an exact
 // product in fp64 and is accumulated in fp64 in a fixed order; a row's 64 lane partials are
 // transposed through LDS every 8 rows and added by 8 lanes per row, and the four waves'
 // column partials are added through LDS at the end. No floating-point atomics.
@@ -71,14 +73,43 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
     gm = 0.0f;
   }
   const GroupQ gq = FMT == kNvFp4 ? nv_group_scale(gm, g, r6) : group_scale<FMT>(gm, g, sixg);
-  const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
   double q[E];  // the codes as values
-  if (FMT == kInt4Bf16 && __any(int4_needs_clamp(gq.d))) {  // rare: a subnormal scale
+  uint32_t pk[2] = {0u, 0u};  // the codes packed as stored (EMIT)
+  // NVFP4's final pass takes the fp32 codes, which come packed (the nibble packing of the
+  // double-quotient codes costs the pass more than their sums); the iteration passes keep
+  // the double quotient, with which the row pass stays at three waves per SIMD
+  constexpr bool kFast = FMT == kNvFp4 && EMIT;
+  if (kFast && __all(gq.d >= 0x1p-100f && gq.d <= 0x1p100f)) {
+    if (__any(!(gm < 7.0f * gq.d))) {  // some scale saturated at 448
+      pk[0] = nv_pack8_fast<true>(x, gq.d, gq.rd);
+      pk[1] = nv_pack8_fast<true>(x + 8, gq.d, gq.rd);
+    } else {
+      pk[0] = nv_pack8_fast<false>(x, gq.d, gq.rd);
+      pk[1] = nv_pack8_fast<false>(x + 8, gq.d, gq.rd);
+    }
 #pragma unroll
-    for (int k = 0; k < E; k++) q[k] = int4_clamp(code64<FMT>(x[k], r, gq));
+    for (int h = 0; h < 2; h++) {
+      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
+      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
+      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
+      const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+      const float qv[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+#pragma unroll
+      for (int k = 0; k < 8; k++) q[8 * h + k] = (double)qv[k];
+    }
   } else {
+    const double r = (FMT == kInt4Bf16 || FMT == kNvFp4) ? recip64(gq.d) : 0.0;
+    if (FMT == kInt4Bf16 && __any(int4_needs_clamp(gq.d))) {  // rare: a subnormal scale
 #pragma unroll
-    for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);
+      for (int k = 0; k < E; k++) q[k] = int4_clamp(code64<FMT>(x[k], r, gq));
+    } else {
+#pragma unroll
+      for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);
+    }
+    if (EMIT) {
+#pragma unroll
+      for (int k = 0; k < E; k++) pk[k / 8] |= nibble_of<FMT>((float)q[k]) << (4 * (k % 8));
+    }
   }
 
   if (ROW) {
@@ -103,10 +134,7 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
     }
   }
   if (EMIT && (!PARTIAL || amask != 0u)) {
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int k = 0; k < E; k++) packed[k / 8] |= nibble_of<FMT>((float)q[k]) << (4 * (k % 8));
-    *reinterpret_cast<uint2*>(code_word) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2*>(code_word) = make_uint2(pk[0], pk[1]);
     if ((__lane_id() % LPG) == 0) {
       if (FMT == kInt4Bf16)
         *static_cast<uint16_t*>(scale_ptr) = (uint16_t)gq.scode;
