@@ -51,7 +51,7 @@ VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
     "per_elem": {3: 10.93, 4: 23.23, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
-    "sources_sha256": "e17378c3e8c58da280ac36cfefda4645cab441c184451454064194070c414053",
+    "sources_sha256": "cd5fb6762e52924449db7ced8d2876f30714dc997ebdbda3c398adffd168bdea",
 }
 
 
