@@ -341,12 +341,18 @@ __global__ __launch_bounds__(kBlock) void k_pass_multi(PassMulti m) {
   pass_block<FMT, G, MODE, PARTIAL, S>(m.a[k], (int)blockIdx.x - m.start[k]);
 }
 
+// Rows per load step: INT4's row pass loads one row ahead instead of two, which keeps it at
+// 168 VGPRs (three waves per SIMD instead of two)
+template <int FMT, int MODE>
+constexpr int pass_step_rows() { return FMT == kInt4Bf16 && MODE == kModeRow ? 1 : 2; }
+
 template <int FMT, int G, int MODE>
 static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int S = pass_step_rows<FMT, MODE>();
   if (a.n % kPassCols != 0)
-    hipLaunchKernelGGL((k_pass<FMT, G, MODE, true, 2>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_pass<FMT, G, MODE, true, S>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((k_pass<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_pass<FMT, G, MODE, false, S>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -355,10 +361,11 @@ static hipError_t pass_multi_partial(const PassMulti& m, hipStream_t s) {
   bool partial = false;
   for (int k = 0; k < m.n; k++) partial |= m.a[k].n % kPassCols != 0;
   const dim3 grid((unsigned)m.start[m.n]);
+  constexpr int S = pass_step_rows<FMT, MODE>();
   if (partial)
-    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, true, 2>), grid, dim3(kBlock), 0, s, m);
+    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, true, S>), grid, dim3(kBlock), 0, s, m);
   else
-    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, false, 2>), grid, dim3(kBlock), 0, s, m);
+    hipLaunchKernelGGL((k_pass_multi<FMT, G, MODE, false, S>), grid, dim3(kBlock), 0, s, m);
   return hipGetLastError();
 }
 
