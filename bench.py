@@ -50,8 +50,8 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {3: 10.93, 4: 23.23, 5: 14.23},  # single-sweep pass / NVFP4 / INT4 row pass
-    "sources_sha256": "cd5fb6762e52924449db7ced8d2876f30714dc997ebdbda3c398adffd168bdea",
+    "per_elem": {3: 10.93, 4: 23.23, 5: 14.24},  # single-sweep pass / NVFP4 / INT4 row pass
+    "sources_sha256": "34db35e17cdb045c3e02cb4954360c51e33a453d81ebfa58a96e130e39c45fe4",
 }
 
 
