@@ -282,11 +282,13 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
       }
     }
     if (EMIT && (!PARTIAL || amask[h] != 0u)) {  // store inside the matrix only
-      codes_row[h * (kTileCols / 8)] = packed;  // this lane's 8 columns of half h
+      // nontemporal: the codes and scales are written once and not read back by the solve
+      __builtin_nontemporal_store(packed, codes_row + h * (kTileCols / 8));  // 8 columns of half h
       if ((__lane_id() % LPG) == 0) {
         // E8M0 byte e + 127 with e = floor(log2(mx * ra_i)) - 2 = E(mx) - 129 - log2 a_i
         const uint32_t ey = (mb >> 23) & 0xFFu;
-        scales_row[h * (kTileCols / (8 * LPG))] = (uint8_t)(mb == 0u ? 127u : ey + 125u - (abits >> 23));
+        __builtin_nontemporal_store((uint8_t)(mb == 0u ? 127u : ey + 125u - (abits >> 23)),
+                                    scales_row + h * (kTileCols / (8 * LPG)));
       }
     }
 #pragma unroll
