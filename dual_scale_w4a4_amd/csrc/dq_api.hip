@@ -29,13 +29,14 @@ constexpr int kTileCols = 512;
 constexpr int kTargetBlocks = 512;  // two 4-wave workgroups per CU on 256 CUs
 
 // Single-sweep launch shape: 512-column halves per lane, rows per load step and the
-// workgroup target (measured best on MI355X for the 8B MLP shapes: one half, two rows,
-// about three 4-wave workgroups per CU). DQ_FUSED_SHAPE="halves,step_rows,target"
+// workgroup target (measured best on MI355X for the 8B MLP shapes: one half, two rows, about
+// two 4-wave workgroups per CU, so that two matrices solved at once on two streams share the
+// GPU; a matrix alone runs its pass as fast with three). DQ_FUSED_SHAPE="halves,step_rows,target"
 // overrides it (launch-shape tuning only).
 struct FusedShape {
   int halves = 1;
   int step_rows = 2;
-  int target = 768;
+  int target = 512;
 };
 FusedShape fused_shape() {
   FusedShape f;
