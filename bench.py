@@ -36,7 +36,7 @@ COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
     "fetch_kib": (57413.0 + 57509.0) / 2, "fetch_scale": 2.0,
-    "write_kib": (7552.0 + 7616.0) / 2, "write_scale": 1.0,
+    "write_kib": (5888.0 + 6048.0) / 2, "write_scale": 1.0,
     "sources_sha256": "4f80704e523f9c8a945f6d6796a939aa33210cd4d5575e35eedba11b8f965a36",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
@@ -50,7 +50,7 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {3: 10.93, 4: 23.23, 5: 14.24},  # single-sweep pass / NVFP4 / INT4 row pass
+    "per_elem": {3: 10.82, 4: 23.23, 5: 14.24},  # single-sweep pass / NVFP4 / INT4 row pass
     "sources_sha256": "749e5f4bf357464208872bf7f895c417650caf6e2a913d0af9e9f5824d40a326",
 }
 

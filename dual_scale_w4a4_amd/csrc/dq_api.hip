@@ -84,6 +84,10 @@ struct Plan {
   int64_t rpc = 0;
   int f_nct = 0, f_nrc = 0;  // single-sweep MX pass: 512 * halves columns, rows in multiples of 32
   int64_t f_rpc = 0;
+  // its final (emit) pass, which writes no column partials, in smaller row chunks: about three
+  // workgroups per CU, where its code and scale stores run faster than with two
+  int f_nrc_emit = 0;
+  int64_t f_rpc_emit = 0;
   FusedShape f_shape;
   int g_nct = 0, g_nrc = 0;  // two-sweep pass for bf16 weights: 512 columns, rows in 32s
   int64_t g_rpc = 0;
@@ -127,6 +131,10 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.f_rpc = (m + f_want - 1) / f_want;
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup
   p.f_nrc = (int)((m + p.f_rpc - 1) / p.f_rpc);
+  int64_t e_want = (p.f_shape.target * 3 / 2 + p.f_nct - 1) / p.f_nct;
+  if (e_want < 1) e_want = 1;
+  p.f_rpc_emit = ((m + e_want - 1) / e_want + 31) / 32 * 32;
+  p.f_nrc_emit = (int)((m + p.f_rpc_emit - 1) / p.f_rpc_emit);
   p.g_nct = (int)((n + dq::pass_tile_cols() - 1) / dq::pass_tile_cols());
   int64_t g_want = (pass_target() + p.g_nct - 1) / p.g_nct;
   if (g_want < 1) g_want = 1;
@@ -460,7 +468,10 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   if (pass_g && io.T > 0 && (st = pass_scale()) != DQ_OK) return st;
   tm.before(DQ_K_EMIT);
   if (fast) {
-    DQ_TRY(launch_fused(p.fmt, true, fu, s));
+    FusedArgs fe = fu;  // the emit pass's own row chunks (its row errors are per column tile)
+    fe.nrc = p.f_nrc_emit;
+    fe.rpc = p.f_rpc_emit;
+    DQ_TRY(launch_fused(p.fmt, true, fe, s));
     fa.nct = p.f_nct;
     fa.row_ra = 1;
   } else if (io.bf16) {
