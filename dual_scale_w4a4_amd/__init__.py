@@ -43,7 +43,14 @@ class _Timing(ctypes.Structure):
 
 class _Init(ctypes.Structure):
     _fields_ = [("a0", ctypes.c_void_p), ("b0", ctypes.c_void_p), ("g0", ctypes.c_float),
-                ("flags", ctypes.c_uint), ("timing", ctypes.POINTER(_Timing))]
+                ("flags", ctypes.c_uint)]
+
+
+class _Shape(ctypes.Structure):
+    """dq_launch_shape (include/dq_bench.h): 0 keeps a field's default."""
+    _fields_ = [("fused_halves", ctypes.c_int), ("fused_step_rows", ctypes.c_int),
+                ("fused_target", ctypes.c_int), ("pass_target", ctypes.c_int),
+                ("sweep_target", ctypes.c_int)]
 
 
 _lib = None
@@ -63,6 +70,12 @@ def lib() -> ctypes.CDLL:
         L.dq_solve.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P, P, P, P, P,
                                P, SZ, P]
         L.dq_solve.restype = I
+        L.dq_solve_timed.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P, P, P,
+                                     P, P, P, SZ, ctypes.POINTER(_Shape), ctypes.POINTER(_Timing),
+                                     P]
+        L.dq_solve_timed.restype = I
+        L.dq_bench_workspace_bytes.argtypes = [I64, I64, I, I, ctypes.POINTER(_Shape)]
+        L.dq_bench_workspace_bytes.restype = SZ
         L.dq_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, SZ, P]
         L.dq_quantize.restype = I
         L.dq_act_workspace_bytes.argtypes = [I64, I64, I, I]
@@ -143,12 +156,16 @@ def _vec(v, n, device):
 
 def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
           two_sweep: bool = False, workspace=None, timing: bool = False,
-          stream=None, flush=None, per_pass_g: bool = False) -> Dict[str, object]:
+          stream=None, flush=None, per_pass_g: bool = False, shape=None) -> Dict[str, object]:
     """dq_solve on W (rows x cols, CUDA float32 / bfloat16). Returns a dict of device
     tensors codes (rows x cols/2 u8), scales (rows x cols/group; int16 holding bf16 bits for
-    int4_bf16, else u8), a, b (float32), mse (T+1 float64), g (float32[1]) and, when
-    ``timing``, per-kernel-kind milliseconds and launch counts (``flush``: a device buffer
-    read in full before each cold re-run of the single-sweep pass)."""
+    int4_bf16, else u8), a, b (float32), mse (T+1 float64), g (float32[1]).
+
+    ``timing`` or ``shape`` (a dict of dq_launch_shape fields) go through the measurement
+    entry point dq_solve_timed (include/dq_bench.h), which adds per-kernel-kind milliseconds
+    and launch counts, whether the single-sweep path was used, and the isolated and cold /
+    warm re-runs of its pass (``flush``: a device buffer read in full before each cold
+    re-run)."""
     torch = _torch()
     dt = _check_w(W)
     rows, cols = W.shape
@@ -160,19 +177,23 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
     g = torch.zeros(1, dtype=torch.float32, device=dev)
     a0 = _vec(a0, rows, dev)
     b0 = _vec(b0, cols, dev)
-    tm = _Timing() if timing else None
-    if tm is not None and flush is not None:
-        tm.flush = flush.data_ptr()
-        tm.flush_bytes = flush.numel() * flush.element_size() // 16 * 16
     flags = (SOLVE_TWO_SWEEP if two_sweep else 0) | (SOLVE_PER_PASS_G if per_pass_g else 0)
-    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags,
-                 ctypes.pointer(tm) if tm is not None else None)
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
-    st = lib().dq_solve(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T,
-                        ctypes.byref(init), codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
-                        a.data_ptr(), b.data_ptr(), mse.data_ptr(), ws_ptr, ws_bytes,
-                        _stream(stream))
+    args = (W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T, ctypes.byref(init),
+            codes.data_ptr(), scales.data_ptr(), g.data_ptr(), a.data_ptr(), b.data_ptr(),
+            mse.data_ptr(), ws_ptr, ws_bytes)
+    tm = None
+    if timing or shape is not None:
+        tm = _Timing()
+        if flush is not None:
+            tm.flush = flush.data_ptr()
+            tm.flush_bytes = flush.numel() * flush.element_size() // 16 * 16
+        sh = _Shape(**(shape or {}))
+        st = lib().dq_solve_timed(*args, ctypes.byref(sh), ctypes.byref(tm), _stream(stream))
+    else:
+        st = lib().dq_solve(*args, _stream(stream))
     if st != 0:
         raise DQError(st, "dq_solve")
     out = {"codes": codes, "scales": scales, "a": a, "b": b, "mse": mse, "g": g}
@@ -182,6 +203,13 @@ def solve(W, fmt: str, group: int, T: int, a0=None, b0=None, g0: float = 0.0,
         out["isolated"] = (tm.isolated_ms, tm.isolated_launches)
         out["cold_warm"] = (tm.cold_ms, tm.warm_ms, tm.per_launch)
     return out
+
+
+def bench_workspace_bytes(rows: int, cols: int, fmt: str, group: int, shape=None) -> int:
+    """dq_bench_workspace_bytes: the workspace of a solve in a given launch shape."""
+    sh = _Shape(**(shape or {}))
+    return int(lib().dq_bench_workspace_bytes(int(rows), int(cols), FMT[fmt], int(group),
+                                              ctypes.byref(sh)))
 
 
 def solve_outputs(W, fmt: str, group: int, T: int) -> Dict[str, object]:
@@ -209,7 +237,7 @@ def solve_async(W, fmt: str, group: int, T: int, out, status, a0=None, b0=None, 
     a0 = _vec(a0, rows, W.device)
     b0 = _vec(b0, cols, W.device)
     flags = (SOLVE_TWO_SWEEP if two_sweep else 0) | (SOLVE_PER_PASS_G if per_pass_g else 0)
-    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags, None)
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     st = lib().dq_solve_async(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T,

@@ -21,58 +21,44 @@
 #include <vector>
 
 #include "../../include/dq.h"
+#include "../../include/dq_bench.h"
 #include "dq_internal.h"
 
 namespace {
 
 constexpr int kTileCols = 512;
-constexpr int kTargetBlocks = 512;  // two 4-wave workgroups per CU on 256 CUs
 
-// Single-sweep launch shape: 512-column halves per lane, rows per load step and the
-// workgroup target (measured best on MI355X for the 8B MLP shapes: one half, two rows, about
-// two 4-wave workgroups per CU, so that two matrices solved at once on two streams share the
-// GPU; a matrix alone runs its pass as fast with three). DQ_FUSED_SHAPE="halves,step_rows,target"
-// overrides it (launch-shape tuning only).
-struct FusedShape {
+// Launch shape of the iteration passes. The defaults were measured best on MI355X for the
+// 8B MLP shapes. Single-sweep MX pass: one 512-column half per lane, two rows per load step
+// and about two 4-wave workgroups per CU, so that two matrices solved at once on two streams
+// share the GPU (a matrix alone runs its pass as fast with three). Two-sweep pass for bf16
+// weights: 768 workgroups (a sweep of 768-3072 moved it by under 10%). General sweep for
+// fp32 weights: 512. The product entry points always take these defaults; only the
+// measurement entry point (dq_solve_timed) takes another shape, so the fixed summation order
+// and the workspace size of a solve never depend on the environment.
+struct LaunchShape {
   int halves = 1;
   int step_rows = 2;
   int target = 512;
+  int pass_target = 768;
+  int sweep_target = 512;
 };
-FusedShape fused_shape() {
-  FusedShape f;
-  const char* env = getenv("DQ_FUSED_SHAPE");
-  if (env) {
-    int h = 0, r = 0, t = 0;
-    if (sscanf(env, "%d,%d,%d", &h, &r, &t) == 3 && (h == 1 || h == 2) && (r == 2 || r == 4) &&
-        t >= 1 && t <= 65536) {
-      f.halves = h;
-      f.step_rows = r;
-      f.target = t;
-    }
-  }
-  return f;
-}
 
-// Workgroup target of the two-sweep pass for bf16 weights; DQ_PASS_TARGET overrides it
-// (launch-shape tuning only, like the others below).
-int pass_target() {
-  const char* env = getenv("DQ_PASS_TARGET");
-  if (env) {
-    int v = atoi(env);
-    if (v >= 1 && v <= 65536) return v;
+// a caller's shape (fields <= 0 keep the default); false if a field is out of range
+bool launch_shape(const dq_launch_shape* in, LaunchShape* out) {
+  LaunchShape f;
+  if (in) {
+    if (in->fused_halves > 0) f.halves = in->fused_halves;
+    if (in->fused_step_rows > 0) f.step_rows = in->fused_step_rows;
+    if (in->fused_target > 0) f.target = in->fused_target;
+    if (in->pass_target > 0) f.pass_target = in->pass_target;
+    if (in->sweep_target > 0) f.sweep_target = in->sweep_target;
   }
-  return 768;
-}
-
-// Workgroup target for the sweeps; DQ_TARGET_WGS overrides it (launch-shape tuning only:
-// results do not depend on it beyond the fixed summation order it implies).
-int target_blocks() {
-  const char* env = getenv("DQ_TARGET_WGS");
-  if (env) {
-    int v = atoi(env);
-    if (v >= 1 && v <= 65536) return v;
-  }
-  return kTargetBlocks;
+  if ((f.halves != 1 && f.halves != 2) || (f.step_rows != 2 && f.step_rows != 4) ||
+      f.target > 65536 || f.pass_target > 65536 || f.sweep_target > 65536)
+    return false;
+  *out = f;
+  return true;
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -88,7 +74,7 @@ struct Plan {
   // workgroups per CU, where its code and scale stores run faster than with two
   int f_nrc_emit = 0;
   int64_t f_rpc_emit = 0;
-  FusedShape f_shape;
+  LaunchShape f_shape;
   int g_nct = 0, g_nrc = 0;  // two-sweep pass for bf16 weights: 512 columns, rows in 32s
   int64_t g_rpc = 0;
   int nblk_rows = 0, nblk_cols = 0;
@@ -110,20 +96,20 @@ bool fmt_ok(int fmt) { return fmt >= 0 && fmt <= 3; }
 // the bf16 single-sweep kernel's shapes: row and column indices within 32 bits
 bool fast_shape_ok(const Plan& p) { return p.m < INT32_MAX && p.n < INT32_MAX; }
 
-Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
+Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = LaunchShape{}) {
   Plan p;
   p.m = m;
   p.n = n;
   p.G = G;
   p.fmt = fmt;
-  const int target = target_blocks();
+  const int target = shape.sweep_target;
   p.nct = (int)((n + kTileCols - 1) / kTileCols);
   int64_t want = (target + p.nct - 1) / p.nct;
   int64_t max_rc = (m + 3) / 4;  // at least one row per wave
   p.nrc = (int)(want < 1 ? 1 : (want > max_rc ? max_rc : want));
   p.rpc = (m + p.nrc - 1) / p.nrc;
   p.nrc = (int)((m + p.rpc - 1) / p.rpc);  // drop empty trailing chunks
-  p.f_shape = fused_shape();
+  p.f_shape = shape;
   const int64_t f_cols = (int64_t)kTileCols * p.f_shape.halves;
   p.f_nct = (int)((n + f_cols - 1) / f_cols);
   int64_t f_want = (p.f_shape.target + p.f_nct - 1) / p.f_nct;
@@ -136,7 +122,7 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G) {
   p.f_rpc_emit = ((m + e_want - 1) / e_want + 31) / 32 * 32;
   p.f_nrc_emit = (int)((m + p.f_rpc_emit - 1) / p.f_rpc_emit);
   p.g_nct = (int)((n + dq::pass_tile_cols() - 1) / dq::pass_tile_cols());
-  int64_t g_want = (pass_target() + p.g_nct - 1) / p.g_nct;
+  int64_t g_want = (shape.pass_target + p.g_nct - 1) / p.g_nct;
   if (g_want < 1) g_want = 1;
   p.g_rpc = (m + g_want - 1) / g_want;
   p.g_rpc = (p.g_rpc + 31) / 32 * 32;
@@ -598,7 +584,10 @@ struct BatchMat {
 
   dq_status emit(hipStream_t s) {
     using namespace dq;
-    if (pass_g && io.T > 0) DQ_TRY(pass_scale(s));
+    if (pass_g && io.T > 0) {
+      const dq_status st = pass_scale(s);
+      if (st != DQ_OK) return st;
+    }
     DQ_TRY(launch_pass(p.fmt, kModeEmit | kModeRow, sp, s));
     fa.ymax = nullptr;
     fa.amax_out = nullptr;
@@ -619,7 +608,10 @@ dq_status batch_iteration(BatchMat* mats, int n, int t, hipStream_t s) {
     const int cnt = n - k0 < kMaxMulti ? n - k0 : kMaxMulti;
     BatchMat* b = mats + k0;
     if (pass_g && t > 0)
-      for (int k = 0; k < cnt; k++) DQ_TRY(b[k].pass_scale(s));
+      for (int k = 0; k < cnt; k++) {
+        const dq_status st = b[k].pass_scale(s);
+        if (st != DQ_OK) return st;
+      }
     PassMulti pm{};
     pm.n = cnt;
     for (int k = 0; k < cnt; k++) {
@@ -784,22 +776,38 @@ dq_status get_workspace(const Plan& p, void* workspace, size_t bytes, hipStream_
   return DQ_OK;
 }
 
-}  // namespace
+// a, b: the outputs the passes read back (b in 128-bit loads)
+bool scale_outputs_ok(const float* a, const float* b) {
+  return a && b && ((uintptr_t)a & 3u) == 0 && ((uintptr_t)b & 15u) == 0;
+}
 
-extern "C" {
-
-dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
-                   int group, int T, const dq_init* init, uint8_t* codes, void* inner_scales,
-                   float* tensor_scale, float* a, float* b, double* mse, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+dq_status check_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                      int group, int T, const dq_init* init, const uint8_t* codes,
+                      const void* inner_scales, const float* tensor_scale, const float* a,
+                      const float* b, const double* mse) {
   dq_status st = check_common(W, wt, rows, cols, fmt, group, codes, inner_scales);
   if (st != DQ_OK) return st;
-  if (T < 0 || !a || !b || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale)) return DQ_ERR_ARG;
+  if (T < 0 || !scale_outputs_ok(a, b) || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale))
+    return DQ_ERR_ARG;
   if (init && (init->g0 != init->g0 || (init->g0 > 0.0f && init->g0 > 3.4028234663852886e38f)))
     return DQ_ERR_ARG;
   if (init && fmt == DQ_FMT_NVFP4 && (init->flags & DQ_SOLVE_PER_PASS_G) && init->g0 > 0.0f)
     return DQ_ERR_ARG;
-  const Plan p = make_plan(rows, cols, fmt, group);
+  return DQ_OK;
+}
+
+// The blocking solve of dq_solve / dq_solve_timed: enqueue, wait, read the device status,
+// and redo the solve on the two-sweep path if the MX single-sweep identity was not
+// guaranteed somewhere.
+dq_status solve_blocking(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                         int group, int T, const dq_init* init, uint8_t* codes,
+                         void* inner_scales, float* tensor_scale, float* a, float* b,
+                         double* mse, void* workspace, size_t workspace_bytes,
+                         const LaunchShape& shape, dq_timing* timing, hipStream_t stream) {
+  dq_status st = check_solve(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                             tensor_scale, a, b, mse);
+  if (st != DQ_OK) return st;
+  const Plan p = make_plan(rows, cols, fmt, group, shape);
   WsGuard ws;
   st = get_workspace(p, workspace, workspace_bytes, stream, ws);
   if (st != DQ_OK) return st;
@@ -807,7 +815,6 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
   SolveIo io{W, wt == DQ_BF16, init, codes, inner_scales, tensor_scale, a, b, mse, T};
   const bool mx = fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4;
   bool fused = mx && !(init && (init->flags & DQ_SOLVE_TWO_SWEEP));
-  dq_timing* timing = init ? init->timing : nullptr;
 
   int flags = 0;
   const void* flush = timing ? timing->flush : nullptr;
@@ -838,20 +845,46 @@ dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_fo
   return map_status(flags & ~dq::kStGauge);
 }
 
+}  // namespace
+
+extern "C" {
+
+dq_status dq_solve(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                   int group, int T, const dq_init* init, uint8_t* codes, void* inner_scales,
+                   float* tensor_scale, float* a, float* b, double* mse, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return solve_blocking(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                        tensor_scale, a, b, mse, workspace, workspace_bytes, LaunchShape{},
+                        nullptr, stream);
+}
+
+size_t dq_bench_workspace_bytes(int64_t rows, int64_t cols, dq_format fmt, int group,
+                                const dq_launch_shape* shape) {
+  LaunchShape sh;
+  if (!fmt_ok(fmt) || !shape_ok(rows, cols, group) || !launch_shape(shape, &sh)) return 0;
+  return make_plan(rows, cols, fmt, group, sh).total;
+}
+
+dq_status dq_solve_timed(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
+                         int group, int T, const dq_init* init, uint8_t* codes,
+                         void* inner_scales, float* tensor_scale, float* a, float* b,
+                         double* mse, void* workspace, size_t workspace_bytes,
+                         const dq_launch_shape* shape, dq_timing* timing, hipStream_t stream) {
+  LaunchShape sh;
+  if (!launch_shape(shape, &sh)) return DQ_ERR_ARG;
+  return solve_blocking(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                        tensor_scale, a, b, mse, workspace, workspace_bytes, sh, timing, stream);
+}
+
 dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
                          int group, int T, const dq_init* init, uint8_t* codes,
                          void* inner_scales, float* tensor_scale, float* a, float* b,
                          double* mse, int* status, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  dq_status st = check_common(W, wt, rows, cols, fmt, group, codes, inner_scales);
+  dq_status st = check_solve(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                             tensor_scale, a, b, mse);
   if (st != DQ_OK) return st;
-  if (T < 0 || !a || !b || !mse || (fmt == DQ_FMT_NVFP4 && !tensor_scale)) return DQ_ERR_ARG;
   if (!status || ((uintptr_t)status & 3u) != 0) return DQ_ERR_ARG;
-  if (init && init->timing) return DQ_ERR_ARG;  // timing needs the host to wait
-  if (init && (init->g0 != init->g0 || (init->g0 > 0.0f && init->g0 > 3.4028234663852886e38f)))
-    return DQ_ERR_ARG;
-  if (init && fmt == DQ_FMT_NVFP4 && (init->flags & DQ_SOLVE_PER_PASS_G) && init->g0 > 0.0f)
-    return DQ_ERR_ARG;
   const Plan p = make_plan(rows, cols, fmt, group);
   WsGuard ws;  // an owned workspace is freed stream-ordered, after the solve's kernels
   st = get_workspace(p, workspace, workspace_bytes, stream, ws);
@@ -1038,7 +1071,8 @@ dq_status dq_solve_batch(int n, const dq_batch_item* items, dq_dtype wt, dq_form
     const dq_batch_item& it = items[k];
     dq_status st = check_common(it.W, wt, it.rows, it.cols, fmt, group, it.codes, it.inner_scales);
     if (st != DQ_OK) return st;
-    if (!it.a || !it.b || !it.mse || (fmt == DQ_FMT_NVFP4 && !it.tensor_scale)) return DQ_ERR_ARG;
+    if (!scale_outputs_ok(it.a, it.b) || !it.mse || (fmt == DQ_FMT_NVFP4 && !it.tensor_scale))
+      return DQ_ERR_ARG;
     if (it.g0 != it.g0 || it.g0 > 3.4028234663852886e38f || (pass_g && it.g0 > 0.0f))
       return DQ_ERR_ARG;
   }
@@ -1067,7 +1101,7 @@ dq_status dq_solve_batch(int n, const dq_batch_item* items, dq_dtype wt, dq_form
     m.io = SolveIo{it.W, true, nullptr, it.codes, it.inner_scales, it.tensor_scale, it.a, it.b,
                    it.mse, T};
     m.pass_g = pass_g;
-    dq_init init{it.a0, it.b0, it.g0, flags, nullptr};
+    dq_init init{it.a0, it.b0, it.g0, flags};
     dq_status st = m.setup(&init, stream);
     if (st != DQ_OK) return st;
   }

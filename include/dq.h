@@ -77,44 +77,12 @@ typedef enum { DQ_F32 = 0, DQ_BF16 = 1 } dq_dtype;
  * pass's g, and init->g0 must then be <= 0. Costs one read of W per Q pass. */
 #define DQ_SOLVE_PER_PASS_G 2u
 
-/* Per-kernel timing, filled by dq_solve when dq_init.timing is not NULL (HIP events recorded
- * on `stream` around each launch; adds a little overhead). Index by dq_kernel_kind. */
-typedef enum {
-  DQ_K_SETUP = 0,  /* init vectors, row statistics, tensor scale */
-  DQ_K_FUSED = 1,  /* MX single-sweep pass: codes, row sums and column sums */
-  DQ_K_ROW = 2,    /* general row pass */
-  DQ_K_COL = 3,    /* general column pass */
-  DQ_K_FINAL = 4,  /* closed-form updates and projections */
-  DQ_K_EMIT = 5,   /* final codes and inner scales */
-  DQ_K_KINDS = 6
-} dq_kernel_kind;
-
-typedef struct {
-  double ms[DQ_K_KINDS];
-  int64_t launches[DQ_K_KINDS];
-  int used_fused; /* 1 if the MX single-sweep path produced the result */
-  /* single-sweep path only: after the solve, the pass is re-run isolated_launches times
-     back to back between one pair of events (results unchanged); this is its time */
-  double isolated_ms;
-  int isolated_launches;
-  /* in (kept by the call): an optional device buffer of flush_bytes bytes (a multiple of 16).
-     When given, the re-runs are also timed one launch at a time, cold_ms after a full read
-     of this buffer before each launch (evicting W from the caches when it is larger than
-     them) and warm_ms without it; per_launch re-runs each */
-  const void* flush;
-  size_t flush_bytes;
-  double cold_ms;
-  double warm_ms;
-  int per_launch;
-} dq_timing;
-
 typedef struct {
   const float* a0;   /* device, rows values > 0, or NULL for ones; projected onto the scale set */
   const float* b0;   /* device, cols values > 0, or NULL for ones; projected onto the scale set */
   float g0;          /* NVFP4: > 0 fixes the tensor scale; <= 0 computes it from the initial
                         scaled tile as fl32(max|X| / 2688), at least 2^-126 (1 if X == 0) */
   unsigned flags;    /* DQ_SOLVE_* */
-  dq_timing* timing; /* HOST pointer or NULL */
 } dq_init;
 
 /* Bytes of device workspace dq_solve / dq_quantize need for this shape (0 on invalid
@@ -130,6 +98,7 @@ size_t dq_workspace_bytes(int64_t rows, int64_t cols, dq_format fmt, int group);
  *  tensor_scale: out, 1 float: NVFP4's g; ignored (may be NULL) for other formats.
  *  a, b:         out, rows / cols floats: the final outer inverse scales, each exactly a value
  *                of the format's scale set (bf16 normal, 2^k with |k| <= 126, or E4M3FN >= 2^-9).
+ *                a is 4-byte and b 16-byte aligned (the passes read b in 128-bit loads).
  *  mse:          out, T+1 doubles: mse[t] = mean (W - D_a Qhat D_b)^2 of the synced state after
  *                t iterations; mse[0] is single-scale round-to-nearest quantization.
  *  workspace:    device scratch of at least dq_workspace_bytes(...) bytes, or NULL to let the
@@ -165,8 +134,7 @@ dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq
  *      unspecified and the solve must be redone with DQ_SOLVE_TWO_SWEEP, which dq_solve does
  *      by itself
  *  16  internal (never expected)
- * A nonzero status leaves the outputs unspecified. init->timing must be NULL. The workspace
- * may be NULL (then allocated and freed stream-ordered). Host-side argument checks return
+ * A nonzero status leaves the outputs unspecified. The workspace may be NULL (then allocated and freed stream-ordered). Host-side argument checks return
  * errors as dq_solve does, before anything is enqueued. */
 dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,
                          int group, int T, const dq_init* init, uint8_t* codes,
@@ -231,8 +199,8 @@ typedef struct {
   uint8_t* codes;        /* out, as for dq_solve */
   void* inner_scales;    /* out */
   float* tensor_scale;   /* out, NVFP4 */
-  float* a;              /* out, rows */
-  float* b;              /* out, cols */
+  float* a;              /* out, rows, 4-byte aligned */
+  float* b;              /* out, cols, 16-byte aligned */
   double* mse;           /* out, T+1 */
 } dq_batch_item;
 

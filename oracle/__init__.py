@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.dq_ref_solve.restype = I
         L.dq_ref_solve_diag.argtypes = [P, I, I64, I64, I, I, I, P, P, F, P, P, P, P, P, P, P, P]
         L.dq_ref_solve_diag.restype = I
-        for name in ("dq_ref_project",):
+        for name in ("dq_ref_project", "dq_ref_proj_margin"):
             getattr(L, name).argtypes = [I, D]
             getattr(L, name).restype = D
         for name in ("dq_ref_bf16_rne", "dq_ref_e4m3_rne_sat", "dq_ref_e2m1_round"):
@@ -212,6 +212,11 @@ def solve(W: np.ndarray, dtype: str, fmt: str, group: int, T: int, a0=None, b0=N
 
 def project(fmt: str, v: float) -> float:
     return float(lib().dq_ref_project(FMT[fmt], float(v)))
+
+
+def proj_margin(fmt: str, v: float) -> float:
+    """Relative distance from v to the nearest decision point of the projection."""
+    return float(lib().dq_ref_proj_margin(FMT[fmt], float(v)))
 
 
 def bf16_rne(v: float) -> float:

@@ -174,8 +174,10 @@ static void e4m3_table_init(void) {
   e4m3_table_ready = 1;
 }
 
-/* relative distance from v to the nearest decision boundary of Pi_F */
-static double proj_margin(int fmt, double v) {
+/* relative distance from v to the nearest decision boundary of Pi_F: |v - t| / v for the
+ * nearest midpoint t between two neighbouring values of the scale set (infinite where the
+ * set has a single value on each side, which never happens) */
+double dq_ref_proj_margin(int fmt, double v) {
   double p = dq_ref_project(fmt, v), prev = 0, next = 0;
   int has_prev = 1, has_next = 1;
   if (fmt == DQR_FMT_INT4_BF16) {
@@ -668,7 +670,7 @@ static int solve_core(const void* W, int wt, int64_t rows, int64_t cols, int fmt
       } else {
         if (!(N > 0.0)) internal = 1; /* every W*R term is >= 0 */
         a[i] = (float)dq_ref_project(fmt, N / D);
-        mrow[i] = proj_margin(fmt, N / D);
+        mrow[i] = dq_ref_proj_margin(fmt, N / D);
       }
     }
     if (internal) {
@@ -715,7 +717,7 @@ static int solve_core(const void* W, int wt, int64_t rows, int64_t cols, int fmt
           goto done;
         }
         b[j] = (float)dq_ref_project(fmt, Nc[j] / Dc[j]);
-        if (margin) mcol = fmin(mcol, proj_margin(fmt, Nc[j] / Dc[j]));
+        if (margin) mcol = fmin(mcol, dq_ref_proj_margin(fmt, Nc[j] / Dc[j]));
       }
     }
     if (margin) margin[2 * t + 1] = mcol;

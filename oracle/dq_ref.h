@@ -107,6 +107,7 @@ int dq_ref_solve_diag(const void* W, int wt, int64_t rows, int64_t cols, int fmt
 
 /* Scalar pieces, exposed so that tests can pin them against brute force. */
 double dq_ref_project(int fmt, double v);       /* Pi_F of an outer inverse-scale, v > 0 */
+double dq_ref_proj_margin(int fmt, double v);   /* relative distance of v to Pi_F's nearest decision point */
 double dq_ref_bf16_rne(double v);               /* nearest bf16, ties to even (v >= 0) */
 double dq_ref_e4m3_rne_sat(double v);           /* nearest E4M3FN, ties to even, <= 448 */
 double dq_ref_e2m1_round(double v);             /* nearest E2M1 value, ties to even index */

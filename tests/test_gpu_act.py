@@ -193,3 +193,99 @@ def test_act_async_matches_blocking_and_collects_status(dq):
     dq.quantize_act_async(Bd, "mxfp4", 32, out["codes"], out["scales"], status, b=bd)
     torch.cuda.synchronize()
     assert int(host(status)[0]) & 1
+
+
+def _projected_b(fmt, cols, seed):
+    """Column inverse scales drawn as the solver returns them: uniform(0.05, 4) values
+    projected onto the format's outer scale set (bf16 values for INT4_BF16, E4M3 values for
+    NVFP4), so that most products X * b are inexact in fp32."""
+    rng = np.random.default_rng(seed)
+    return np.array([fb.project(fmt, float(v)) for v in rng.uniform(0.05, 4.0, cols)],
+                    np.float32)
+
+
+def _inexact_products(X, b):
+    exact = X.astype(np.float64) * b[None, :].astype(np.float64)
+    return int(np.count_nonzero(exact != (X * b[None, :]).astype(np.float64)))
+
+
+@pytest.mark.parametrize("fmt,group", [("int4_bf16", 32), ("int4_bf16", 64), ("nvfp4", 16)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_with_the_solvers_scale_sets(dq, oracle_lib, fmt, group, dtype):
+    X = workloads.activations(67, 1088, seed=group + 3, dtype=dtype)
+    b = _projected_b(fmt, 1088, seed=group)
+    assert np.mean(np.log2(b) != np.round(np.log2(b))) > 0.5  # mostly not powers of two
+    if dtype == "f32":  # bf16 X times a bf16 or E4M3 b is exact in fp32 (<= 16 bits)
+        assert _inexact_products(X, b) > X.size // 4
+    _check(dq, oracle_lib, X, dtype, fmt, group, b, name="projected b")
+    if fmt == "nvfp4":
+        _check(dq, oracle_lib, X, dtype, fmt, group, b, g=0.0071, name="projected b, given g")
+
+
+@pytest.mark.parametrize("fmt,group", [("int4_bf16", 64), ("nvfp4", 16), ("mxfp4", 32)])
+def test_act_with_b_from_a_gpu_solve(dq, oracle_lib, fmt, group):
+    # the consumer chain: the solver's column scales of a weight with these input channels
+    W = workloads.config5_layer(2, scale_down=4, only=("up",))[0].W[:, :1024]
+    sol = dq.solve(to_device(np.ascontiguousarray(W), "bf16"), fmt, group, 6)
+    b = host(sol["b"])
+    X = workloads.activations(40, 1024, seed=11)
+    _check(dq, oracle_lib, X, "bf16", fmt, group, b, name=f"b of a {fmt} solve")
+
+
+def _tie_targets(fmt, group, rows, cols, rng, g=1.0):
+    """Scaled activations x with every group's scale fixed by its first element and the
+    other elements on the code grid's decision points times the divisor d, or one fp32 step
+    either side (INT4_BF16: d a bf16 value, x_max = 7 d, ties at (k + 1/2) d)."""
+    if fmt == "nvfp4":
+        return _nvfp4_tie_rows(g, rows, cols, seed=int(rng.integers(1 << 30)))
+    x = np.zeros((rows, cols), np.float32)
+    for i in range(rows):
+        for k in range(cols // group):
+            d = fb.bf16_decode(np.array([rng.integers(0x3A00, 0x3F00)], np.uint16))[0]
+            ks = rng.integers(-7, 7, group - 1) + 0.5
+            base = (ks * np.float64(d)).astype(np.float32)
+            step = rng.integers(-1, 2, group - 1)
+            near = np.where(step > 0, np.nextafter(base, np.float32(np.inf)),
+                            np.where(step < 0, np.nextafter(base, np.float32(-np.inf)), base))
+            x[i, k * group] = np.float32(7.0 * np.float64(d)) * np.float32(rng.choice([-1, 1]))
+            x[i, k * group + 1:(k + 1) * group] = near
+    return x
+
+
+def _unscale(x, b):
+    """fp32 X with fl32(X * b) == x where one exists, preferring an X whose exact product
+    is not x (so the tie comes out of a rounded product); else the nearest one."""
+    X0 = (x.astype(np.float64) / b[None, :].astype(np.float64)).astype(np.float32)
+    cands = [X0]
+    lo = hi = X0
+    for _ in range(3):
+        lo = np.nextafter(lo, np.float32(-np.inf))
+        hi = np.nextafter(hi, np.float32(np.inf))
+        cands += [lo, hi]
+    best = X0.copy()
+    score = np.full(x.shape, 3, np.int8)  # 0: tie from an inexact product, 1: exact one
+    bb = b[None, :].astype(np.float64)
+    for c in cands:
+        prod = c.astype(np.float64) * bb
+        hit = (prod.astype(np.float32) == x)
+        s = np.where(hit & (prod != x.astype(np.float64)), 0, np.where(hit, 1, 3)).astype(np.int8)
+        take = s < score
+        best = np.where(take, c, best)
+        score = np.minimum(score, s)
+    return best, score
+
+
+@pytest.mark.parametrize("fmt,group", [("int4_bf16", 32), ("int4_bf16", 64), ("nvfp4", 16)])
+def test_act_ties_after_an_inexact_product(dq, oracle_lib, fmt, group):
+    # x = fl32(X * b) lands on a code decision point (or one step beside it) although the
+    # exact product X * b does not: the quantizer must take the tie from the rounded product
+    rng = np.random.default_rng(group + 100)
+    cols = 512
+    b = _projected_b(fmt, cols, seed=group + 1)
+    for g in ((3.0 / 256.0, 0.0071) if fmt == "nvfp4" else (0.0,)):
+        x = _tie_targets(fmt, group, 24, cols, rng, g=g)
+        X, score = _unscale(x, b)
+        assert np.mean(score == 0) > 0.5, np.mean(score == 0)
+        got_x = (X * b[None, :]).astype(np.float32)
+        assert np.mean(got_x == x) > 0.8
+        _check(dq, oracle_lib, X, "f32", fmt, group, b, g=g, name=f"inexact ties g={g}")

@@ -1,18 +1,21 @@
 """CPU-side checks of the C ABI: the library loads, exports every entry point the header
 declares, and rejects invalid arguments on the host before touching the GPU."""
 import ctypes
+import json
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dq.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "dq_bench.h")
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(dq_[a-z_]+)\s*\(", src)))
 
@@ -36,14 +39,22 @@ def test_header_declares_the_boundary():
                      "dq_solve_async", "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
 
 
+def test_bench_header_declares_only_the_measurement_hooks():
+    assert _declared_functions(BENCH_HEADER) == ["dq_bench_workspace_bytes", "dq_solve_timed"]
+    # the solver's own header carries no timing or launch-shape types
+    src = open(HEADER).read()
+    assert "dq_timing" not in src and "launch_shape" not in src
+
+
 def test_library_exports_every_declared_symbol(dqlib):
     lib = dqlib.lib()
-    for name in _declared_functions():
+    declared = _declared_functions() + _declared_functions(BENCH_HEADER)
+    for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", dqlib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
-    assert set(_declared_functions()) <= exported
+    assert set(declared) <= exported
 
 
 def test_library_is_built_for_gfx950(dqlib):
@@ -68,7 +79,7 @@ def test_workspace_bytes_validates_shape(dqlib):
 def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     L = dqlib.lib()
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
-    init = dqlib._Init(None, None, 0.0, 0, None)
+    init = dqlib._Init(None, None, 0.0, 0)
     args = dict(W=fake, wt=1, rows=128, cols=256, fmt=2, group=32, T=4)
 
     def call(**kw):
@@ -90,8 +101,13 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert st == 5
     st = L.dq_quantize(fake, 1, 128, 256, 3, 32, None, None, None, fake, fake, None, 0, None)
     assert st == 1  # NVFP4 needs the tensor-scale pointer
+    # b is read in 128-bit loads, a as floats
+    for a_ptr, b_ptr in ((fake, ctypes.c_void_p(0x1004)), (ctypes.c_void_p(0x1002), fake)):
+        st = L.dq_solve(fake, 1, 128, 256, 2, 32, 4, ctypes.byref(init), fake, fake, fake, a_ptr,
+                        b_ptr, fake, None, 0, None)
+        assert st == 1
 
-    # the asynchronous solve checks the same, its status pointer, and refuses timing
+    # the asynchronous solve checks the same, and its status pointer
     def call_async(status=fake, init_=init, **kw):
         a = dict(args, **kw)
         return L.dq_solve_async(a["W"], a["wt"], a["rows"], a["cols"], a["fmt"], a["group"],
@@ -103,8 +119,37 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert call_async(fmt=9) == 2
     assert call_async(status=None) == 1
     assert call_async(status=ctypes.c_void_p(0x1002)) == 1
-    tm = dqlib._Timing()
-    assert call_async(init_=dqlib._Init(None, None, 0.0, 0, ctypes.pointer(tm))) == 1
+
+    # the measurement entry point: the same checks, and launch-shape fields in range
+    def call_timed(shape=None, **kw):
+        a = dict(args, **kw)
+        return L.dq_solve_timed(a["W"], a["wt"], a["rows"], a["cols"], a["fmt"], a["group"],
+                                a["T"], ctypes.byref(init), fake, fake, fake, fake, fake, fake,
+                                None, 0, ctypes.byref(shape) if shape else None, None, None)
+
+    assert call_timed(W=None) == 1
+    assert call_timed(fmt=9) == 2
+    assert call_timed(shape=dqlib._Shape(3, 0, 0, 0, 0)) == 1  # halves: 1 or 2
+    assert call_timed(shape=dqlib._Shape(0, 3, 0, 0, 0)) == 1  # step rows: 2 or 4
+    assert call_timed(shape=dqlib._Shape(0, 0, 70000, 0, 0)) == 1
+
+
+def test_workspace_size_does_not_depend_on_the_environment(dqlib):
+    # the launch shape of the product entry points is fixed: tuning variables in the
+    # environment (read by earlier versions) change neither the workspace nor the sums' order
+    shapes = [(14336, 4096, "mxfp4", 32), (4096, 14336, "int4_bf16", 64), (300, 1568, "nvfp4", 16),
+              (128, 256, "int4_bf16", 32)]
+    code = ("import sys, json; sys.path.insert(0, %r); import dual_scale_w4a4_amd as dq; "
+            "print(json.dumps([dq.workspace_bytes(*s) for s in %r]))" % (ROOT, shapes))
+    env = dict(os.environ, DQ_FUSED_SHAPE="2,4,2048", DQ_PASS_TARGET="3000", DQ_TARGET_WGS="64")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout
+    assert json.loads(out) == [dqlib.workspace_bytes(*s) for s in shapes]
+    # the measurement entry point's default shape is the product's; another one differs
+    for s in shapes:
+        assert dqlib.bench_workspace_bytes(*s) == dqlib.workspace_bytes(*s)
+    assert dqlib.bench_workspace_bytes(14336, 4096, "mxfp4", 32, {"fused_target": 2048}) != \
+        dqlib.workspace_bytes(14336, 4096, "mxfp4", 32)
 
 
 def test_act_arguments_are_rejected_on_the_host(dqlib):

@@ -15,7 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "dq_ref.c")
 PIN_FILES = ["tests/test_oracle_codecs.py", "tests/test_oracle_solver.py", "tests/test_golden.py",
-             "tests/test_oracle_act.py", "tests/test_oracle_gemm.py", "tests/test_oracle_pass_g.py"]
+             "tests/test_oracle_act.py", "tests/test_oracle_gemm.py", "tests/test_oracle_pass_g.py",
+             "tests/test_oracle_diag.py"]
 
 # (what the slip is, text in dq_ref.c that occurs exactly once, what it becomes)
 MUTANTS = [
@@ -80,6 +81,17 @@ MUTANTS = [
      "int ef = (e - 1) + 7;", "int ef = (e - 1) + 8;"),
     ("per-pass tensor scale never recomputed",
      "c->g = tensor_scale(c, ra, rb);", "c->g = c->g;"),
+    ("projection margin measured to the wrong upper neighbour of a bf16 value",
+     "next = p + ldexp(1.0, e - 7);", "next = p + ldexp(1.0, e - 8);"),
+    ("projection margin relative to the projected value instead of v",
+     "if (has_next) m = fmin(m, fabs(v - 0.5 * (p + next)) / v);",
+     "if (has_next) m = fmin(m, fabs(v - 0.5 * (p + next)) / p);"),
+    ("row-update change counts compare the wrong pair of passes",
+     "changes[4 * t + 0] = count_diff_i8(qA, qB, m * n);",
+     "changes[4 * t + 0] = count_diff_i8(qB, qB, m * n);"),
+    ("column-update scale changes counted on the codes' buffer",
+     "changes[4 * (t - 1) + 3] = count_diff_u16(sB, sA, m * c.ng);\n    }\n\n    /* 3",
+     "changes[4 * (t - 1) + 3] = count_diff_u16(sB, sB, m * c.ng);\n    }\n\n    /* 3"),
     ("all-zero column gets scale 2",
      "if (Dc[j] == 0.0) {\n        b[j] = 1.0f;", "if (Dc[j] == 0.0) {\n        b[j] = 2.0f;"),
 ]
