@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.dq_solve_async.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P, P, P, P,
                                      P, P, P, SZ, P]
         L.dq_solve_async.restype = I
+        L.dq_solve_async_noalloc.argtypes = [P, I, I64, I64, I, I, I, ctypes.POINTER(_Init), P, P,
+                                             P, P, P, P, P, P]
+        L.dq_solve_async_noalloc.restype = I
         L.dq_gemm_mx.argtypes = [P, P, I64, I64, P, P, P, I64, I, P, P]
         L.dq_gemm_mx.restype = I
         L.dq_gemm_pack_bytes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
@@ -247,6 +250,32 @@ def solve_async(W, fmt: str, group: int, T: int, out, status, a0=None, b0=None, 
                               ws_ptr, ws_bytes, _stream(stream))
     if st != 0:
         raise DQError(st, "dq_solve_async")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DQ_NOALLOC_SCRATCH_BYTES
+
+
+def solve_async_noalloc(W, fmt: str, group: int, T: int, out, status, a0=None, b0=None,
+                        g0: float = 0.0, two_sweep: bool = False, per_pass_g: bool = False,
+                        stream=None) -> None:
+    """dq_solve_async_noalloc into ``out`` (from solve_outputs): as solve_async, with the
+    library's per-device scratch as the workspace (no allocation on any path; calls on one GPU
+    must not overlap)."""
+    dt = _check_w(W)
+    rows, cols = W.shape
+    if out["mse"].numel() != T + 1:
+        raise ValueError("out was made for another T")
+    a0 = _vec(a0, rows, W.device)
+    b0 = _vec(b0, cols, W.device)
+    flags = (SOLVE_TWO_SWEEP if two_sweep else 0) | (SOLVE_PER_PASS_G if per_pass_g else 0)
+    init = _Init(_ptr(a0), _ptr(b0), float(g0), flags)
+    st = lib().dq_solve_async_noalloc(W.data_ptr(), DTYPE[dt], rows, cols, FMT[fmt], group, T,
+                                      ctypes.byref(init), out["codes"].data_ptr(),
+                                      out["scales"].data_ptr(), out["g"].data_ptr(),
+                                      out["a"].data_ptr(), out["b"].data_ptr(),
+                                      out["mse"].data_ptr(), status.data_ptr(), _stream(stream))
+    if st != 0:
+        raise DQError(st, "dq_solve_async_noalloc")
 
 
 def quantize(W, fmt: str, group: int, a=None, b=None, g: float = 0.0, workspace=None,

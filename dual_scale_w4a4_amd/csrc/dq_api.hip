@@ -18,6 +18,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/dq.h"
@@ -776,6 +777,36 @@ dq_status get_workspace(const Plan& p, void* workspace, size_t bytes, hipStream_
   return DQ_OK;
 }
 
+// The workspace of dq_solve_async_noalloc, for callers that cannot allocate: one per device
+// (each GPU the library runs on holds its own copy until the process ends). Host code never
+// passes the array's name to a kernel: it is a host-side stand-in, and the device address is
+// looked up per device with hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[DQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];  // the device address of `scratch` on each device, or null
+
+// The address of `scratch` on the current device, which `stream` must belong to; looked up on
+// the first call on each device (with that device current), then kept.
+dq_status scratch_address(hipStream_t stream, char** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur < 0 || cur >= kMaxDevices) return DQ_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return DQ_ERR_HIP;
+    if (sdev != cur) return DQ_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DQ_ERR_HIP;
+    g_scratch_ptr[cur] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[cur];
+  return DQ_OK;
+}
+
 // a, b: the outputs the passes read back (b in 128-bit loads)
 bool scale_outputs_ok(const float* a, const float* b) {
   return a && b && ((uintptr_t)a & 3u) == 0 && ((uintptr_t)b & 15u) == 0;
@@ -899,6 +930,26 @@ dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols,
                      status);
   DQ_TRY(hipGetLastError());
   return DQ_OK;
+}
+
+dq_status dq_solve_async_noalloc(const void* W, dq_dtype wt, int64_t rows, int64_t cols,
+                                 dq_format fmt, int group, int T, const dq_init* init,
+                                 uint8_t* codes, void* inner_scales, float* tensor_scale,
+                                 float* a, float* b, double* mse, int* status,
+                                 hipStream_t stream) {
+  dq_status st = check_solve(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                             tensor_scale, a, b, mse);
+  if (st != DQ_OK) return st;
+  if (!status || ((uintptr_t)status & 3u) != 0) return DQ_ERR_ARG;
+  if (dq_workspace_bytes(rows, cols, fmt, group) > (size_t)DQ_NOALLOC_SCRATCH_BYTES)
+    return DQ_ERR_WORKSPACE;
+  char* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != DQ_OK) return st;
+  // the same enqueue as dq_solve_async with a caller workspace: no allocation on any path
+  return dq_solve_async(W, wt, rows, cols, fmt, group, T, init, codes, inner_scales,
+                        tensor_scale, a, b, mse, status, ws, (size_t)DQ_NOALLOC_SCRATCH_BYTES,
+                        stream);
 }
 
 dq_status dq_quantize(const void* W, dq_dtype wt, int64_t rows, int64_t cols, dq_format fmt,

@@ -23,8 +23,9 @@
  *  - Work is enqueued on `stream`; the call then synchronizes `stream` so that errors found
  *    on the device (non-finite W, non-finite scaled values, invalid init values) can be
  *    returned. Outputs are unspecified when the call returns an error.
- *  - Calls keep no state between them: the library holds no global mutable data. Calls
- *    that share a workspace must not overlap.
+ *  - Calls keep no state between them: the library holds no global mutable data (except
+ *    dq_solve_async_noalloc's scratch, see there). Calls that share a workspace must not
+ *    overlap.
  *  - Results are deterministic: every reduction has a fixed order (no floating-point
  *    atomics), so the same inputs give bit-identical outputs.
  *
@@ -141,6 +142,24 @@ dq_status dq_solve_async(const void* W, dq_dtype wt, int64_t rows, int64_t cols,
                          void* inner_scales, float* tensor_scale, float* a, float* b,
                          double* mse, int* status, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* dq_solve_async for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. It takes no workspace and
+ * calls no allocating routine: its scratch is a device array inside the library of
+ * DQ_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the library's first use on that GPU
+ * until the process ends. Shapes whose dq_workspace_bytes exceeds it are rejected with
+ * DQ_ERR_WORKSPACE before anything is enqueued (64 MiB holds every matrix up to
+ * 28672 x 8192 in any format, and much larger ones). `stream` must belong to the current
+ * device (else DQ_ERR_ARG). Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (the solve needs none on entry): calls on one GPU must not overlap,
+ * so enqueue them on one stream or order their streams; overlapping calls race. Arguments,
+ * results and the status word are those of dq_solve_async. */
+#define DQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+dq_status dq_solve_async_noalloc(const void* W, dq_dtype wt, int64_t rows, int64_t cols,
+                                 dq_format fmt, int group, int T, const dq_init* init,
+                                 uint8_t* codes, void* inner_scales, float* tensor_scale,
+                                 float* a, float* b, double* mse, int* status,
+                                 hipStream_t stream);
 
 /* Bytes of device workspace dq_quantize_act needs (0 on invalid arguments); scratch only. */
 size_t dq_act_workspace_bytes(int64_t tokens, int64_t cols, dq_format fmt, int group);

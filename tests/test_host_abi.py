@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     assert names == ["dq_act_workspace_bytes", "dq_batch_workspace_bytes", "dq_gemm_mx",
                      "dq_gemm_mx_packed", "dq_gemm_pack_bytes", "dq_gemm_pack_weights",
                      "dq_quantize", "dq_quantize_act", "dq_quantize_act_async", "dq_solve",
-                     "dq_solve_async", "dq_solve_batch", "dq_status_str", "dq_workspace_bytes"]
+                     "dq_solve_async", "dq_solve_async_noalloc", "dq_solve_batch",
+                     "dq_status_str", "dq_workspace_bytes"]
 
 
 def test_bench_header_declares_only_the_measurement_hooks():
@@ -119,6 +120,20 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert call_async(fmt=9) == 2
     assert call_async(status=None) == 1
     assert call_async(status=ctypes.c_void_p(0x1002)) == 1
+
+    # the allocation-free solve: the same checks, then shapes beyond its scratch, all on the
+    # host before any HIP call
+    def call_noalloc(status=fake, **kw):
+        a = dict(args, **kw)
+        return L.dq_solve_async_noalloc(a["W"], a["wt"], a["rows"], a["cols"], a["fmt"],
+                                        a["group"], a["T"], ctypes.byref(init), fake, fake, fake,
+                                        fake, fake, fake, status, None)
+
+    assert call_noalloc(W=None) == 1
+    assert call_noalloc(cols=250) == 1
+    assert call_noalloc(status=None) == 1
+    assert dqlib.workspace_bytes(1 << 17, 16384, "nvfp4", 16) > dqlib.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(rows=1 << 17, cols=16384, fmt=3, group=16) == 5
 
     # the measurement entry point: the same checks, and launch-shape fields in range
     def call_timed(shape=None, **kw):
