@@ -83,6 +83,31 @@ ACT_COUNTERS = {
 }
 
 
+def _layer(args):
+    import workloads
+
+    layer, only = args
+    return workloads.config5_layer(layer, only=only)
+
+
+def load_layers(layers: int, only=None):
+    """The decoder layers 0..layers-1 of workload 5 (seeded, one stream per matrix), drawn by
+    a pool of host processes when there are several, with a progress line per layer."""
+    if layers <= 1:
+        return _layer((0, only))
+    from concurrent.futures import ProcessPoolExecutor
+
+    workers = max(1, min(16, os.cpu_count() or 1, layers))
+    out = [None] * layers
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        for L, ws in enumerate(ex.map(_layer, [(L, only) for L in range(layers)])):
+            out[L] = ws
+            print(f"[bench] layer {L} drawn ({time.perf_counter() - t0:.0f} s)", file=sys.stderr,
+                  flush=True)
+    return [w for ws in out for w in ws]
+
+
 def sources_sha256(files=KERNEL_SOURCES) -> str:
     import hashlib
 
@@ -128,17 +153,13 @@ def to_device(w_np, dtype: str):
 
 def valu_per_elem(workload: int, kind: str, used_fused: bool, per_pass_g: bool, batch: bool):
     """VALU lane-instructions per element of the dominant pass, where counted on these
-    sources (the plain single-sweep pass of workload 3, the row pass of workloads 4 and 5)."""
+    sources (keyed by workload and pass kind)."""
     c = VALU_COUNTERS
     if per_pass_g or batch or sources_sha256(VALU_SOURCES) != c["sources_sha256"]:
         return None
     if kind == "fused" and not used_fused:
         return None
-    return c["per_elem"].get(workload)
-
-
-def _dominant_kind(fmt: str) -> str:
-    return "fused" if fmt in ("mxint4", "mxfp4") else "row"
+    return c["per_elem"].get(f"{workload}/{kind}")
 
 
 def main() -> None:
@@ -160,6 +181,10 @@ def main() -> None:
                          "q,k,v,o,gate,up,down), e.g. the small k,v")
     ap.add_argument("--layers", type=int, default=1,
                     help="workload 5: decoder layers per step (layer-by-layer inputs 0..N-1)")
+    ap.add_argument("--streams", type=int, default=16,
+                    help="concurrent solves: matrix k goes on stream k mod N (at most one "
+                         "stream per matrix)")
+    ap.add_argument("--oracle-child", default="", help=argparse.SUPPRESS)
     ap.add_argument("--batch", action="store_true",
                     help="solve the step's matrices with one batch solve (shared launches) "
                          "instead of one solve per matrix")
@@ -175,6 +200,9 @@ def main() -> None:
                     help="only run plain 512 MiB device-to-device copies (the reference that "
                          "scales HBM byte counters)")
     args = ap.parse_args()
+    if args.oracle_child:
+        oracle_child(args.oracle_child)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the solver runs each matrix on a single device "
               "(sharding across GPUs is by matrix, with no communication); use --gpus 1",
@@ -205,23 +233,22 @@ def main() -> None:
 
     mats, desc = _load(args.workload)
     if args.workload == 5:
-        import workloads
-
         only = tuple(args.only.split(",")) if args.only else None
-        mats = [w for L in range(args.layers) for w in workloads.config5_layer(L, only=only)]
+        mats = load_layers(args.layers, only)
         desc = desc.replace("layer 0", f"layers 0..{args.layers - 1}" if args.layers > 1 else "layer 0")
         if args.only:
             desc += f", only {args.only}"
     dev_w = [to_device(w.W, w.dtype) for w in mats]
     work = [dq.workspace_bytes(w.rows, w.cols, w.fmt, w.group) for w in mats]
     wss = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in work]
-    streams = [torch.cuda.Stream() for _ in mats]  # default priority
+    n_streams = max(1, min(args.streams, len(mats)))
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]  # default priority
     torch.cuda.synchronize()
     pool = None
     if not args.sequential and len(mats) > 1:
         from concurrent.futures import ThreadPoolExecutor
 
-        pool = ThreadPoolExecutor(max_workers=len(mats))
+        pool = ThreadPoolExecutor(max_workers=n_streams)
 
     # read in full before each cold re-run of the dominant pass: twice the 256 MB
     # Infinity Cache, so that W is evicted from every cache level
@@ -264,14 +291,20 @@ def main() -> None:
             # and workspaces (the library keeps no global state)
             if pool is None or timing:
                 return [solve_one(k, T, timing, None) for k in range(len(mats))]
-            futs = [pool.submit(solve_one, k, T, False, streams[k]) for k in range(len(mats))]
-            return [f.result() for f in futs]
+            # one worker per stream, each solving its own matrices in order
+            def worker(j):
+                return [(k, solve_one(k, T, False, streams[j]))
+                        for k in range(j, len(mats), n_streams)]
+
+            done = dict(kv for f in [pool.submit(worker, j) for j in range(n_streams)]
+                        for kv in f.result())
+            return [done[k] for k in range(len(mats))]
         res = []
         for k, w in enumerate(mats):
             Tk = w.T if T is None else T
             o = outs_for(k, Tk)
             dq.solve_async(dev_w[k], w.fmt, w.group, Tk, o, status, workspace=wss[k],
-                           stream=None if args.sequential else streams[k],
+                           stream=None if args.sequential else streams[k % n_streams],
                            per_pass_g=args.per_pass_g and w.fmt == "nvfp4")
             res.append(o)
         return res
@@ -302,18 +335,18 @@ def main() -> None:
     t_step1, _ = timed_steps(T=1)
 
     # instrumented pass over the same steps: per-kernel HIP events on the solve's stream
-    kind = _dominant_kind(mats[0].fmt)
     bytes_per_elem = 2 if mats[0].dtype == "bf16" else 4
-    ms_all, used_fused = {}, True
+    per_kind, used_fused = {}, True  # kind -> [ms, launches, bytes read by those launches]
     iso = [0.0, 0, 0.0]  # ms, launches, bytes of the isolated back-to-back runs
     cw = [0.0, 0.0, 0, 0.0]  # cold ms, warm ms, launches, bytes of the one-at-a-time re-runs
     for _ in range(args.steps):
         for w, o in zip(mats, step(timing=True)):
             used_fused = used_fused and o["used_fused"]
             for k, (ms, n) in o["timing"].items():
-                acc = ms_all.setdefault(k, [0.0, 0])
+                acc = per_kind.setdefault(k, [0.0, 0, 0.0])
                 acc[0] += ms
                 acc[1] += n
+                acc[2] += n * w.rows * w.cols * bytes_per_elem  # each pass launch reads W once
             iso[0] += o["isolated"][0]
             iso[1] += o["isolated"][1]
             iso[2] += o["isolated"][1] * w.rows * w.cols * bytes_per_elem
@@ -322,10 +355,11 @@ def main() -> None:
             cw[1] += warm
             cw[2] += n1
             cw[3] += n1 * w.rows * w.cols * bytes_per_elem
-    ms_kind, n_kind = ms_all[kind]
-    # dominant kernel: each launch reads every weight of its matrix once, T launches per solve
-    bytes_total = args.steps * sum(w.rows * w.cols * bytes_per_elem * w.T for w in mats)
-    if iso[1] > 0:  # back-to-back launches between one event pair: no per-launch overhead
+    # the dominant kernel: the iteration pass with the most kernel time
+    kind = max((k for k in ("fused", "rowres", "row", "col") if per_kind.get(k, [0])[0] > 0),
+               key=lambda k: per_kind[k][0])
+    ms_kind, n_kind, bytes_total = per_kind[kind]
+    if kind == "fused" and iso[1] > 0:  # back-to-back launches between one event pair
         ms_kind, n_kind, bytes_total = iso
 
     elems = sum(w.rows * w.cols for w in mats)
@@ -339,22 +373,35 @@ def main() -> None:
     launch_bytes = bytes_total / max(n_kind, 1)
     achieved = bytes_total / (ms_kind * 1e-3) / 1e9
 
-    kernel_name = ("k_fused_mx" if kind == "fused" else
-                   ("k_pass (row mode)" if mats[0].dtype == "bf16" else "k_sweep (row mode)"))
+    kernel_name = {"fused": "k_fused_mx", "rowres": "k_rowres",
+                   "row": "k_pass (row mode)" if mats[0].dtype == "bf16" else "k_sweep (row mode)",
+                   "col": "k_pass (column mode)" if mats[0].dtype == "bf16" else "k_sweep (column mode)"}[kind]
     roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": counted_traffic(args.workload, kind == "fused" and used_fused),
                 "traffic_unit": "bytes per launch", "avg_launch_us": avg_launch_ms * 1e3,
                 "launches": n_kind, "bytes_per_launch": launch_bytes,
-                "timing": "isolated back-to-back launches" if iso[1] else "per-launch events",
-                "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ms_all.items()}}
+                "timing": "isolated back-to-back launches" if (kind == "fused" and iso[1])
+                          else "per-launch events, sequential instrumented solves",
+                "kernel_share": {k: v[0] / sum(x[0] for x in per_kind.values())
+                                 for k, v in per_kind.items() if v[0] > 0}}
+    if cw[2] > 0 and kind == "fused":
+        # `achieved` above times back-to-back launches, where a matrix that fits the 256 MB
+        # Infinity Cache is partly served from it; the cold figure reads W from HBM
+        cold_gbs = cw[3] / (cw[0] * 1e-3) / 1e9
+        roofline.update({
+            "source_of_W": "back-to-back launches: W (<= 256 MB) partly served from the "
+                           "Infinity Cache; achieved_cold / frac_cold: one launch after a "
+                           "full read of a 512 MiB buffer, W from HBM",
+            "achieved_cold": cold_gbs, "frac_cold": cold_gbs / HBM_PEAK_GBS,
+            "avg_launch_us_cold": cw[0] / cw[2] * 1e3})
     per_elem = valu_per_elem(args.workload, kind, used_fused, args.per_pass_g, args.batch)
     if per_elem is not None:
         valu = per_elem * (bytes_total / bytes_per_elem) / (ms_kind * 1e-3)
         alu = {"lane_instructions_per_element": per_elem, "achieved": valu / 1e12,
                "peak": VALU_PEAK / 1e12, "unit": "T VALU lane-instructions/s",
                "frac": valu / VALU_PEAK}
-        if kind == "row":  # the two-sweep pass: its exact fp64 codes and sums bind the ALU
+        if kind in ("row", "col", "rowres"):  # exact fp64 codes and sums bind the ALU
             hbm = {k: roofline[k] for k in ("achieved", "peak", "unit", "frac")}
             roofline.update(bound="alu", **{k: alu[k] for k in ("achieved", "peak", "unit", "frac")})
             roofline["lane_instructions_per_element"] = per_elem
@@ -624,9 +671,61 @@ def bench_gemm(args, dq) -> None:
     print(json.dumps(line), flush=True)
 
 
+def oracle_child(spec: str) -> None:
+    """Run in a child process pinned to one core: the oracle, single-threaded, on a sample
+    saved by the parent; prints its wall time as JSON."""
+    import numpy as np
+
+    import oracle
+
+    d = json.loads(spec)
+    sample = np.load(d["path"], allow_pickle=False)
+    threads = oracle.set_threads(1)
+    t0 = time.perf_counter()
+    if d["pass_g"]:
+        oracle.solve_pass_g(sample, d["dtype"], d["group"], d["T"])
+    else:
+        oracle.solve(sample, d["dtype"], d["fmt"], d["group"], d["T"])
+    dt = time.perf_counter() - t0
+    print(json.dumps({"seconds": dt, "threads": threads, "affinity": sorted(os.sched_getaffinity(0))}))
+
+
+def cpu_single_core(w, per_pass_g: bool):
+    """The oracle on one host core: a child process pinned to one core (taskset -c 0, else
+    sched_setaffinity in the child) on rows 0..R-1 of the matrix, R about 4M / cols."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+
+    rows = min(w.rows, max(16, (1024 * 4096) // w.cols))
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "sample.npy")
+        np.save(path, np.ascontiguousarray(w.W[:rows]))
+        spec = json.dumps({"path": path, "dtype": w.dtype, "fmt": w.fmt, "group": w.group,
+                           "T": w.T, "pass_g": bool(per_pass_g and w.fmt == "nvfp4")})
+        cmd = [sys.executable, os.path.abspath(__file__), "--oracle-child", spec]
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        if shutil.which("taskset"):
+            cmd, how = ["taskset", "-c", "0"] + cmd, "taskset -c 0"
+        else:
+            env["DQ_BENCH_PIN_CPU"] = "0"
+            how = "sched_setaffinity"
+        res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+        if res.returncode != 0:
+            return {"error": res.stderr[-500:]}
+        d = json.loads(res.stdout.strip().splitlines()[-1])
+    return {"value": rows * w.cols * w.T / d["seconds"], "unit": "weight-elements x iterations / s",
+            "cores": 1, "pinned": how, "affinity": d["affinity"], "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of {w.name} ({rows}x{w.cols}), {w.fmt}, T={w.T}",
+            "seconds": d["seconds"]}
+
+
 def cpu_baseline(w, dq, to_device, per_pass_g=False):
     """The oracle on a bounded row sample of the first matrix (same T), all host cores up to
-    16, and the GPU on the same sample checked against it."""
+    16, and the GPU on the same sample checked against it; beside it the oracle on one pinned
+    core, on a smaller sample."""
     import numpy as np
 
     import oracle
@@ -657,8 +756,11 @@ def cpu_baseline(w, dq, to_device, per_pass_g=False):
         "gpu_vs_oracle_on_sample": {"mse_final_rel": float(abs(mse_g[-1] - ref["mse"][-1]) / ref["mse"][-1]),
                                     "a_identical": a_eq, "b_identical": b_eq,
                                     "codes_identical": codes_eq},
+        "single_core": cpu_single_core(w, per_pass_g),
     }
 
 
 if __name__ == "__main__":
+    if os.environ.get("DQ_BENCH_PIN_CPU"):
+        os.sched_setaffinity(0, {int(os.environ["DQ_BENCH_PIN_CPU"])})
     main()

@@ -24,7 +24,7 @@ STATUS = {0: "DQ_OK", 1: "DQ_ERR_ARG", 2: "DQ_ERR_UNSUPPORTED", 3: "DQ_ERR_NONFI
           4: "DQ_ERR_RANGE", 5: "DQ_ERR_WORKSPACE", 6: "DQ_ERR_HIP", 7: "DQ_ERR_INTERNAL"}
 SOLVE_TWO_SWEEP = 1
 SOLVE_PER_PASS_G = 2
-KERNEL_KINDS = ("setup", "fused", "row", "col", "final", "emit")
+KERNEL_KINDS = ("setup", "fused", "row", "col", "final", "emit", "rowres")
 
 
 class DQError(RuntimeError):
@@ -34,7 +34,7 @@ class DQError(RuntimeError):
 
 
 class _Timing(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
+    _fields_ = [("ms", ctypes.c_double * 7), ("launches", ctypes.c_int64 * 7),
                 ("used_fused", ctypes.c_int), ("isolated_ms", ctypes.c_double),
                 ("isolated_launches", ctypes.c_int), ("flush", ctypes.c_void_p),
                 ("flush_bytes", ctypes.c_size_t), ("cold_ms", ctypes.c_double),
@@ -50,7 +50,8 @@ class _Shape(ctypes.Structure):
     """dq_launch_shape (include/dq_bench.h): 0 keeps a field's default."""
     _fields_ = [("fused_halves", ctypes.c_int), ("fused_step_rows", ctypes.c_int),
                 ("fused_target", ctypes.c_int), ("pass_target", ctypes.c_int),
-                ("sweep_target", ctypes.c_int)]
+                ("sweep_target", ctypes.c_int), ("row_resident", ctypes.c_int),
+                ("rowres_target", ctypes.c_int)]
 
 
 _lib = None

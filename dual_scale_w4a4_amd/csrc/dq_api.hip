@@ -30,8 +30,11 @@ namespace {
 constexpr int kTileCols = 512;
 
 // Launch shape of the iteration passes. The defaults were measured best on MI355X for the
-// 8B MLP shapes. Single-sweep MX pass: one 512-column half per lane, two rows per load step
-// and about two 4-wave workgroups per CU, so that two matrices solved at once on two streams
+// 8B shapes. Row-resident pass (INT4_BF16 / NVFP4 rows of up to 4096 columns): off, since the
+// two-sweep passes ran a whole decoder layer faster (the row-resident pass issues more
+// instructions per element); when on, 256 workgroups (one 8-wave workgroup per CU; 384 and
+// 512 were slower on the 14336-row matrices). Single-sweep MX pass: one 512-column half per
+// lane, two rows per load step and about two 4-wave workgroups per CU, so that two matrices solved at once on two streams
 // share the GPU (a matrix alone runs its pass as fast with three). Two-sweep pass for bf16
 // weights: 768 workgroups (a sweep of 768-3072 moved it by under 10%). General sweep for
 // fp32 weights: 512. The product entry points always take these defaults; only the
@@ -43,6 +46,8 @@ struct LaunchShape {
   int target = 512;
   int pass_target = 768;
   int sweep_target = 512;
+  bool row_resident = false;
+  int rowres_target = 256;
 };
 
 // a caller's shape (fields <= 0 keep the default); false if a field is out of range
@@ -54,9 +59,12 @@ bool launch_shape(const dq_launch_shape* in, LaunchShape* out) {
     if (in->fused_target > 0) f.target = in->fused_target;
     if (in->pass_target > 0) f.pass_target = in->pass_target;
     if (in->sweep_target > 0) f.sweep_target = in->sweep_target;
+    if (in->row_resident != 0) f.row_resident = in->row_resident > 0;
+    if (in->rowres_target > 0) f.rowres_target = in->rowres_target;
   }
   if ((f.halves != 1 && f.halves != 2) || (f.step_rows != 2 && f.step_rows != 4) ||
-      f.target > 65536 || f.pass_target > 65536 || f.sweep_target > 65536)
+      f.target > 65536 || f.pass_target > 65536 || f.sweep_target > 65536 ||
+      f.rowres_target > 65536)
     return false;
   *out = f;
   return true;
@@ -78,9 +86,13 @@ struct Plan {
   LaunchShape f_shape;
   int g_nct = 0, g_nrc = 0;  // two-sweep pass for bf16 weights: 512 columns, rows in 32s
   int64_t g_rpc = 0;
+  // row-resident pass (INT4_BF16 / NVFP4 rows it takes): workgroups, rows per workgroup
+  bool rr_ok = false;
+  int rr_nwg = 0;
+  int64_t rr_rpc = 0;
   int nblk_rows = 0, nblk_cols = 0;
   size_t off_status = 0, off_ra = 0, off_rb = 0, off_a0 = 0, off_b0 = 0, off_E = 0, off_amax = 0,
-         off_gs = 0;
+         off_gs = 0, off_rowerr = 0;
   size_t off_rowpart = 0, off_colpart = 0, off_msepart = 0, off_ymax = 0, off_epart = 0, total = 0;
 };
 
@@ -128,6 +140,12 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = 
   p.g_rpc = (m + g_want - 1) / g_want;
   p.g_rpc = (p.g_rpc + 31) / 32 * 32;
   p.g_nrc = (int)((m + p.g_rpc - 1) / p.g_rpc);
+  if (shape.row_resident && dq::rowres_shape_ok(fmt, n)) {
+    const int64_t B = dq::rowres_batch_rows(n);
+    p.rr_ok = true;
+    p.rr_rpc = ((m + shape.rowres_target - 1) / shape.rowres_target + B - 1) / B * B;
+    p.rr_nwg = (int)((m + p.rr_rpc - 1) / p.rr_rpc);
+  }
   p.nblk_rows = (int)((m + 255) / 256);
   p.nblk_cols = (int)((n + 31) / 32);  // finalize: 8 lanes per column
   size_t o = 0;
@@ -142,9 +160,14 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = 
   const size_t rc_parts = (size_t)(p.nct > p.f_nct ? p.nct : p.f_nct);
   size_t cc_parts = (size_t)(p.nrc > p.f_nrc ? p.nrc : p.f_nrc);
   if ((size_t)p.g_nrc > cc_parts) cc_parts = (size_t)p.g_nrc;
+  if ((size_t)p.rr_nwg > cc_parts) cc_parts = (size_t)p.rr_nwg;
   p.off_rowpart = o; o = align_up(o + 2 * sizeof(double) * rc_parts * m);
   p.off_colpart = o; o = align_up(o + 2 * sizeof(double) * cc_parts * n);
   p.off_msepart = o; o = align_up(o + 2 * sizeof(double) * p.nblk_rows);
+  if (p.rr_ok) {  // the row-resident pass's per-row errors
+    p.off_rowerr = o;
+    o = align_up(o + sizeof(double) * m);
+  }
   if (fmt == DQ_FMT_NVFP4) {  // per-pass tensor scale: the row pass's row maxima of |y|
     p.off_ymax = o;
     o = align_up(o + sizeof(float) * (size_t)p.g_nct * m);
@@ -366,6 +389,24 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.a = io.a;
   fu.status = status;
 
+  // the row-resident pass (bf16 weights, a tensor scale fixed for the solve, shapes it takes)
+  const bool rowres = io.bf16 && !pass_g && p.rr_ok;
+  RowResArgs rr{};
+  rr.W = static_cast<const uint16_t*>(io.W);
+  rr.m = p.m;
+  rr.n = p.n;
+  rr.G = p.G;
+  rr.a = io.a;
+  rr.ra = ra;
+  rr.rb = rb;
+  rr.b = io.b;
+  rr.gs = gs;
+  rr.E = E;
+  rr.rowerr = p.off_rowerr ? at<double>(ws, p.off_rowerr) : nullptr;
+  rr.colpart = colpart;
+  rr.rpc = p.rr_rpc;
+  rr.status = status;
+
   // mse[t]: a finalize that takes row sums writes per-block error sums into one of two
   // buffers; the next finalize (or the final collect) adds them up into mse[t]
   int produced = 0, pend_idx = -1;
@@ -413,6 +454,16 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       fa.nrc = p.nrc;
       fa.gauge_check = 1;
       if ((st = finalize(true, true, true)) != DQ_OK) return st;
+    } else if (io.bf16 && rowres) {
+      // one read of W: both Q evaluations, the row update and the column partials
+      tm.before(DQ_K_ROWRES);
+      DQ_TRY(launch_rowres(p.fmt, rr, p.rr_nwg, s));
+      tm.after();
+      fa.nct = 0;
+      fa.nrc = p.rr_nwg;
+      fa.rowerr = rr.rowerr;
+      if ((st = finalize(true, true, false)) != DQ_OK) return st;
+      fa.rowerr = nullptr;
     } else if (io.bf16) {
       if (pass_g && t > 0 && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_ROW);

@@ -62,6 +62,24 @@ struct FusedArgs {
   int* status;
 };
 
+// Row-resident iteration pass on bf16 weights (see k_rowres): both Q evaluations of an
+// iteration from one read of W, for formats whose row update changes the codes.
+struct RowResArgs {
+  const uint16_t* W;
+  int64_t m, n;
+  int G;
+  float* a;          // rows: in the current a, out the updated a'
+  float* ra;         // rows: in fl32(1 / a), out fl32(1 / a')
+  const float* rb;   // cols: fl32(1 / b)
+  const float* b;    // cols
+  const float* gs;   // NVFP4: gs[0] = g, gs[1] = fl32(6 g)
+  const double* E;   // rows: sum_j W_ij^2
+  double* rowerr;    // rows, out: E_i - 2 a_i N_i + a_i^2 D_i of the state before the update
+  double2* colpart;  // [workgroups][n] (P, Q) with S = D_a' Qhat'
+  int64_t rpc;       // rows per workgroup, a multiple of rowres_batch_rows(n)
+  int* status;
+};
+
 struct RowStatArgs {
   const void* W;
   int64_t m, n;
@@ -126,6 +144,9 @@ struct FinArgs {
   // the next pass's row maxima of |x| out
   const float* ymax;
   float* amax_out;
+  // rows: per-row errors already formed by the row-resident pass (then the rows' part only
+  // adds them up; rowpart is not read)
+  const double* rowerr;
 };
 
 // Several matrices per launch (a batch solve): workgroups [start[k], start[k+1]) belong to
@@ -180,6 +201,13 @@ hipError_t launch_act_gscale(bool bf16, const ActArgs& a, hipStream_t s);  // am
 int act_tile_cols();
 int act_amax_blocks();
 hipError_t launch_finalize(const FinArgs& a, hipStream_t s);
+// row-resident pass (dq_rowres.hip): nwg workgroups of rowres_lanes(n) threads, each owning
+// RowResArgs::rpc rows (a multiple of rowres_batch_rows(n)); for the shapes rowres_shape_ok
+// accepts (INT4_BF16 and NVFP4 rows of up to 4096 columns)
+hipError_t launch_rowres(int fmt, const RowResArgs& a, int nwg, hipStream_t s);
+bool rowres_shape_ok(int fmt, int64_t n);
+int rowres_lanes(int64_t n);
+int rowres_batch_rows(int64_t n);
 hipError_t launch_fused(int fmt, bool emit, const FusedArgs& a, hipStream_t s);  // a.epart: first pass
 hipError_t launch_mse_collect(const double* part, int count, double* out, double inv_mn,
                               hipStream_t s);

@@ -700,7 +700,9 @@ __device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
     const int64_t i = (int64_t)bid * 256 + tid;
     double err = 0.0;
     int flags = 0;
-    if (i < p.m) {
+    if (i < p.m && p.rowerr) {
+      err = p.rowerr[i];  // formed by the row-resident pass, which also updated a
+    } else if (i < p.m) {
       if (p.epart) {  // E_i from the first pass's tile partials, in tile order
         double e2 = 0.0;
         for (int k = 0; k < p.nct; k++) e2 += p.epart[(int64_t)k * p.m + i];

@@ -22,7 +22,8 @@ typedef enum {
   DQ_K_COL = 3,    /* general column pass */
   DQ_K_FINAL = 4,  /* closed-form updates and projections */
   DQ_K_EMIT = 5,   /* final codes and inner scales */
-  DQ_K_KINDS = 6
+  DQ_K_ROWRES = 6, /* row-resident pass: both Q evaluations of an iteration from one read */
+  DQ_K_KINDS = 7
 } dq_kernel_kind;
 
 typedef struct {
@@ -49,13 +50,20 @@ typedef struct {
  *  fused_step_rows:  single-sweep MX pass, rows per load step (2 or 4; default 2)
  *  fused_target:     single-sweep MX pass, target workgroup count (default 512)
  *  pass_target:      two-sweep pass for bf16 weights, target workgroup count (default 768)
- *  sweep_target:     general sweep (fp32 weights), target workgroup count (default 512) */
+ *  sweep_target:     general sweep (fp32 weights), target workgroup count (default 512)
+ *  row_resident:     INT4_BF16 / NVFP4 on bf16 weights (tensor scale fixed for the solve), rows
+ *                    of up to 4096 columns: 1 takes the row-resident pass (one read of W per
+ *                    iteration), -1 or 0 the two-sweep passes (the default: they solve a
+ *                    whole decoder layer faster on MI355X)
+ *  rowres_target:    row-resident pass, target workgroup count (default 256) */
 typedef struct {
   int fused_halves;
   int fused_step_rows;
   int fused_target;
   int pass_target;
   int sweep_target;
+  int row_resident;
+  int rowres_target;
 } dq_launch_shape;
 
 /* dq_workspace_bytes for a solve in the given launch shape (NULL: the default one). */

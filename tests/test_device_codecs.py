@@ -23,12 +23,17 @@ SRC = [os.path.join(HERE, "codec_host.hip"),
 
 @pytest.fixture(scope="module")
 def H():
+    # DQ_CODEC_HOST_LIB: load another build of codec_host.hip instead (for example one built
+    # with the host sanitizers)
+    if os.environ.get("DQ_CODEC_HOST_LIB"):
+        return ctypes.CDLL(os.environ["DQ_CODEC_HOST_LIB"])
     os.makedirs(BUILD, exist_ok=True)
     if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(s) for s in SRC):
+        tmp = f"{LIB}.tmp{os.getpid()}"  # parallel test workers may build at once
         subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O2", "-std=c++17",
-                        "-fPIC", "-shared", "-ffp-contract=off", SRC[0], "-o", LIB + ".tmp"],
+                        "-fPIC", "-shared", "-ffp-contract=off", SRC[0], "-o", tmp],
                        check=True, capture_output=True)
-        os.replace(LIB + ".tmp", LIB)
+        os.replace(tmp, LIB)
     return ctypes.CDLL(LIB)
 
 

@@ -35,11 +35,11 @@ def par_oracle(oracle_lib):
     oracle_lib.set_threads(1)
 
 
-def _run_pair(dq, oracle, w, T=None, exact_if_margin=1e-9):
+def _run_pair(dq, oracle, w, T=None, exact_if_margin=1e-9, shape=None):
     T = w.T if T is None else T
-    print(f"[solve] {w.name} {w.fmt} G={w.group} T={T}", flush=True)
+    print(f"[solve] {w.name} {w.fmt} G={w.group} T={T} {shape or ''}", flush=True)
     ref = oracle.solve(w.W, w.dtype, w.fmt, w.group, T, diag=True)
-    gpu = dq.solve(to_device(w.W, w.dtype), w.fmt, w.group, T)
+    gpu = dq.solve(to_device(w.W, w.dtype), w.fmt, w.group, T, shape=shape)
     res = compare_solve(gpu, ref, w.fmt, w.rows, w.cols)
     exact = T == 0 or float(ref["margin"].min()) > exact_if_margin
     assert_parity(res, exact=exact, name=w.name)
@@ -233,17 +233,49 @@ def test_single_sweep_first_pass_row_statistics(dq, oracle_lib, fmt):
     assert_parity(compare_solve(gpu, ref, fmt, 96, 1536), exact=True, name=f"{fmt} T=0")
 
 
+@pytest.mark.parametrize("row_resident", [1, -1])
 @pytest.mark.parametrize("fmt", ["int4_bf16", "nvfp4"])
-def test_subnormal_groups_on_the_two_sweep_pass(dq, oracle_lib, fmt):
+def test_subnormal_groups_on_the_bf16_passes(dq, oracle_lib, fmt, row_resident):
     # bf16 weights with groups of subnormal values: their INT4 scale is a subnormal bf16
-    # value, where the codes need the clamp to [-8, 7]
+    # value, where the codes need the clamp to [-8, 7]; on the row-resident pass and on the
+    # two-sweep passes
     group = 16 if fmt == "nvfp4" else 32
     W32 = rand_w(48, 1088, seed=17)
     W32[5, :32] = (np.linspace(-1, 1, 32) * 2.2e-39).astype(np.float32)
     W32[11, 64:96] = (np.linspace(-1, 1, 32) * 5e-40).astype(np.float32)
     Wb = workloads.fp32_to_bf16_bits(W32)
     w = workloads.Workload("subnormal", Wb, "bf16", fmt, group, 4)
-    _run_pair(dq, oracle_lib, w)
+    _run_pair(dq, oracle_lib, w, shape={"row_resident": row_resident})
+
+
+ROW_RESIDENT_CASES = [
+    # (rows, cols, format, group, T): ragged row counts (not a multiple of the 8-row batch or
+    # of the rows per workgroup), column counts below, at and between whole 512-column waves,
+    # every group size, and the widest rows the pass takes
+    (203, 1088, "int4_bf16", 32, 7), (77, 2080, "nvfp4", 16, 6), (40, 3072, "int4_bf16", 16, 5),
+    (300, 4096, "int4_bf16", 64, 6), (129, 4096, "nvfp4", 16, 5), (1, 512, "int4_bf16", 64, 4),
+    (517, 16, "nvfp4", 16, 5), (64, 96, "int4_bf16", 32, 5),
+]
+
+
+@pytest.mark.parametrize("rows,cols,fmt,group,T", ROW_RESIDENT_CASES)
+def test_row_resident_pass_equals_two_sweep_and_oracle(dq, oracle_lib, rows, cols, fmt, group, T):
+    # the row-resident pass does both Q evaluations of an iteration from one read of each row:
+    # the same codes and the same exact products as the two-sweep passes, summed in another
+    # fixed fp64 order
+    Wb = rand_w(rows, cols, seed=rows + cols, dtype="bf16", outliers=max(1, cols // 200))
+    W = to_device(Wb, "bf16")
+    rr = dq.solve(W, fmt, group, T, shape={"row_resident": 1}, timing=True)
+    assert rr["timing"]["rowres"][1] == T  # one launch per iteration
+    two = dq.solve(W, fmt, group, T, shape={"row_resident": -1}, timing=True)
+    assert two["timing"]["rowres"][1] == 0
+    for k in ("a", "b", "codes", "scales", "g"):
+        assert np.array_equal(host(rr[k]), host(two[k])), k
+    mr, mt = host(rr["mse"]), host(two["mse"])
+    assert np.all(np.abs(mr - mt) <= 1e-12 * mt), (mr, mt)
+    ref = oracle_lib.solve(Wb, "bf16", fmt, group, T, diag=True)
+    res = compare_solve(rr, ref, fmt, rows, cols)
+    assert_parity(res, exact=float(ref["margin"].min()) > 1e-9, name=f"{rows}x{cols} {fmt}")
 
 
 @pytest.mark.parametrize("shape,T,dtype", [((520, 1104), 20, "bf16"), ((96, 512), 6, "f32"),
