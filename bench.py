@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": (57413.0 + 57509.0) / 2, "fetch_scale": 2.0,
-    "write_kib": (5888.0 + 6048.0) / 2, "write_scale": 1.0,
-    "sources_sha256": "4f80704e523f9c8a945f6d6796a939aa33210cd4d5575e35eedba11b8f965a36",
+    "fetch_kib": 57457.0, "fetch_scale": 2.0,  # average over both matrices' launches
+    "write_kib": 5968.0, "write_scale": 1.0,
+    "sources_sha256": "7144f6e193e3d9fbcd014cdfa327f018ac9317c3716ac415dae73f4a217709a9",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -50,8 +50,9 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {3: 10.82, 4: 23.23, 5: 14.24},  # single-sweep pass / NVFP4 / INT4 row pass
-    "sources_sha256": "749e5f4bf357464208872bf7f895c417650caf6e2a913d0af9e9f5824d40a326",
+    "per_elem": {"3/fused": 10.82, "4/row": 23.23, "4/col": 22.95, "5/row": 14.24,
+                 "5/col": 14.09},  # workload / pass kind
+    "sources_sha256": "96e05f7c7c6ab948ec3ebb9fc993068d97a860a584d417e79d168844b01185aa",
 }
 
 
