@@ -897,10 +897,251 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed(GemmArgs p) {
     gemm_tile_packed<BF16, VECY, true>(p, i0, t0, lds);
 }
 
+// ------------------------------------------------- packed weights, 4 x 1 wave layout
+// The same tile and stage pipeline with the waves stacked along the weight rows: wave w owns
+// rows 64 w .. 64 w + 63 (two 32-row blocks) and all 256 tokens (eight blocks), 2 x 8
+// products per k step. Each weight fragment then enters the CU once (the 2 x 2 layout loads
+// every one twice, for the two waves that share its rows); each wave reads all eight token
+// fragments of a k step from LDS instead of four. Per stage a lane issues 8 fragment loads,
+// 2 scale loads and 8 token loads.
+constexpr int kStageLoads41 = 8 + 2 + 8;
+
+template <bool EDGE, int KS, int NX>
+__device__ __forceinline__ void packed_kstep41(v16f (&acc)[2][8], u32x4 (&fa)[2][4],
+                                               const u32x4 (&fb)[8], u32x4 (&fb_next)[8],
+                                               const uint8_t* lx, int xterm, uint32_t (&sw)[2],
+                                               const uint32_t (&sx)[8], const PackedCtx& c,
+                                               PackedLds& lds, uint8_t* xb, int s2, bool on,
+                                               int q, bool xs_on) {
+#pragma unroll
+  for (int t = 0; t < 16; t++) {
+    const int m = t / 8, n = t % 8;
+    mfma_sel<KS>(acc[m][n], fa[m][KS], fb[n], sw[m], sx[n]);
+    if (t % 2 == 0 && KS < 3)
+      fb_next[t / 2] =
+          *reinterpret_cast<const u32x4*>(lx + (t / 2) * 32 * kRowB + (((KS + 1) ^ xterm) * 16));
+    if (n == 7) {
+      fa[m][KS] = __builtin_amdgcn_raw_buffer_load_b128(
+          on ? c.rwc : c.rnone, c.va[m], (uint32_t)((s2 * 4 + KS) * kPackBlockB), 0);
+      if (KS == 3)
+        sw[m] = __builtin_amdgcn_raw_buffer_load_b32(on ? c.rws : c.rnone, c.vs[m],
+                                                     (uint32_t)(s2 * kPackScaleB), 0);
+    }
+    if (t == 1 || t == 9) packed_load_x<EDGE>(c, xb, KS * 2 + t / 8, s2 * kRowB, on);
+    if (KS == 1 && t == 8 && NX > 8) packed_load_xs(c, lds, q, xs_on);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The epilogue of the 4 x 1 layout: the wave's 64 x 256 results through LDS, 32 tokens at a
+// time (rows of 64 fp32 channels, padded by 16 bytes); a lane reads back 4 channels of one row,
+// 16 lanes to a row, and each store instruction writes four rows of 128 (bf16) or 256 bytes.
+constexpr int kRowStage41 = 64 * 4 + 16;
+static_assert(4 * 32 * kRowStage41 <= (int)sizeof(PackedLds), "epilogue staging does not fit");
+
+template <bool BF16, bool VECY, bool EDGE>
+__device__ __forceinline__ void store_tile41(const GemmArgs& p, const v16f (&acc)[2][8], int i0,
+                                             int t0, uint8_t* stage) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rl = lane & 31, h = lane >> 5;
+  const int wi = wave * 64;
+  uint8_t* region = stage + wave * 32 * kRowStage41;
+  const int ich = i0 + wi + (lane & 15) * 4;  // the 4 channels this lane stores
+  f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (p.a) {
+    if (!EDGE || ich + 3 < p.out) {
+      av = *reinterpret_cast<const f32x4*>(p.a + ich);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; e++) av[e] = ich + e < p.out ? p.a[ich + e] : 1.0f;
+    }
+  }
+  __syncthreads();  // every wave is done with the main loop's LDS
+
+#pragma unroll
+  for (int n = 0; n < 8; n++) {
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const f32x4 y = {acc[m][n][g * 4], acc[m][n][g * 4 + 1], acc[m][n][g * 4 + 2],
+                         acc[m][n][g * 4 + 3]};
+        *reinterpret_cast<f32x4*>(region + rl * kRowStage41 + (m * 32 + g * 8 + h * 4) * 4) = y;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const int row = (lane >> 4) + 4 * r;
+      f32x4 y = *reinterpret_cast<const f32x4*>(region + row * kRowStage41 + (lane & 15) * 16);
+      const int t = t0 + n * 32 + row;
+      if (EDGE && t >= p.tokens) continue;
+#pragma unroll
+      for (int e = 0; e < 4; e++) y[e] *= av[e];
+      const bool vec = VECY && (!EDGE || ich + 3 < p.out);
+      if (BF16) {
+        __bf16* yp = static_cast<__bf16*>(p.y) + (int64_t)t * p.ldy + ich;
+        const bf16x4 hv = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+        if (vec) {
+          __builtin_nontemporal_store(hv, reinterpret_cast<bf16x4*>(yp));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (ich + e < p.out) yp[e] = hv[e];
+        }
+      } else {
+        float* yp = static_cast<float*>(p.y) + (int64_t)t * p.ldy + ich;
+        if (vec) {
+          __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(yp));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (ich + e < p.out) yp[e] = y[e];
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next chunk's writes
+  }
+}
+
+template <bool BF16, bool VECY, bool EDGE>
+__device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, int t0,
+                                                   PackedLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave * 64;
+  const int ldb = p.K / 2, nkb = p.K / 32;
+  const int nst = p.K / kBK;  // even: K % 512 == 0
+  const int nrb = (p.out + 31) / 32;
+  const int rl = lane & 31, h = lane >> 5;
+
+  PackedCtx c;
+  c.rwc = rsrc(p.wc, (uint32_t)nrb * (uint32_t)nst * 4u * kPackBlockB);
+  c.rws = rsrc(p.ws, (uint32_t)nrb * (uint32_t)nst * kPackScaleB);
+  c.rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
+  c.rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
+  c.rnone = rsrc(p.wc, 0u);  // reads nothing: the loads of stages after the last
+  c.t0 = t0;
+  c.rows_x = EDGE ? p.tokens : INT32_MAX;
+  c.ldb = ldb;
+  c.nst = nst;
+  c.wave = wave;
+  c.lane = lane;
+#pragma unroll
+  for (int m = 0; m < 2; m++) {
+    const int rb = (i0 + wi) / 32 + m;
+    const bool in = !EDGE || rb < nrb;
+    c.va[m] = in ? (uint32_t)rb * (uint32_t)nst * 4u * kPackBlockB + (uint32_t)(lane * 16) : kOob;
+    c.vs[m] = in ? (uint32_t)rb * (uint32_t)nst * kPackScaleB + (uint32_t)(lane * 4) : kOob;
+  }
+  {
+    const int lr = lane >> 3;
+    const uint32_t bx = (uint32_t)(t0 + wave * 64 + lr) * (uint32_t)ldb;
+    c.vx[0] = bx + (uint32_t)(((lane & 7) ^ lr) * 16);
+    c.vx[1] = bx + (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
+    const int rx = t0 + wave * 64 + lane;
+    c.sbx = (EDGE && rx >= p.tokens) ? kOob : (uint32_t)rx * (uint32_t)nkb;
+  }
+
+  v16f acc[2][8];
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int n = 0; n < 8; n++) acc[m][n] = v16f{};
+
+  // token fragment reads: row 32 n + lane % 32 of the buffer, chunk 4 h + ks at its swizzled
+  // position (4 h + ks) ^ term = ks ^ (term ^ 4 h)
+  const int xterm = (rl & 7) ^ ((rl >> 3) & 1) ^ (4 * h);
+  const int rx = rl * kRowB;
+  const int sx_off = rl * kScaleRowB + 4 * h;
+
+  u32x4 fa[2][2][4];  // [stage parity][m][ks]
+  uint32_t sw[2][2];  // [stage parity][m]
+  u32x4 fb0[8], fb1[8];
+  uint32_t sx[8];
+
+#pragma unroll
+  for (int st = 0; st < 2; st++) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        fa[st][m][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            c.rwc, c.va[m], (uint32_t)((st * 4 + i) * kPackBlockB), 0);
+      sw[st][m] = __builtin_amdgcn_raw_buffer_load_b32(c.rws, c.vs[m],
+                                                       (uint32_t)(st * kPackScaleB), 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L.x[st], j, st * kRowB, true);
+  }
+  packed_load_xs(c, L, 0, true);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto stage_xs = [&](int par, int half) {
+    const uint8_t* bx = L.xs[par] + sx_off + half * 8;
+#pragma unroll
+    for (int n = 0; n < 8; n++) sx[n] = *reinterpret_cast<const uint32_t*>(bx + n * 32 * kScaleRowB);
+  };
+  auto first_frags = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < 8; n++)
+      fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
+  };
+  auto stage = [&](auto pc, auto nxc, int s, int q, bool xs_on) {
+    constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
+    const uint8_t* lx = L.x[s % 3] + rx;
+    uint8_t* xb = L.x[(s + 2) % 3];
+    const int s2 = s + 2;
+    const bool on = s2 < nst;
+    __builtin_amdgcn_sched_barrier(0);
+    packed_kstep41<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep41<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep41<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep41<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads41 + (NX > 8 ? 1 : 0)));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  stage_xs(0, 0);
+  first_frags(0);
+
+  for (int q = 0; q < nst / 2; q++) {
+    const bool more = 2 * q + 2 < nst;
+    const int par = q & 1;
+    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 2 * q, q + 1, more);
+    stage_xs(par, 1);
+    first_frags((2 * q + 1) % 3);
+    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 2 * q + 1, q + 1,
+          false);
+    stage_xs(par ^ 1, 0);
+    first_frags((2 * q + 2) % 3);
+  }
+  store_tile41<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
+}
+
+template <bool BF16, bool VECY>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed41(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) PackedLds lds;
+  int i0, t0;
+  tile_origin(p, i0, t0);
+  if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
+    gemm_tile_packed41<BF16, VECY, false>(p, i0, t0, lds);
+  else
+    gemm_tile_packed41<BF16, VECY, true>(p, i0, t0, lds);
+}
+
+// The packed product's wave layout: 4 x 1 (each weight fragment loaded once per CU) or 2 x 2.
+constexpr bool kPackedWaves41 = true;
+
 template <bool BF16, bool VECY>
 hipError_t launch_packed_t(const GemmArgs& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_mx_packed<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s,
-                     p);
+  if (kPackedWaves41)
+    hipLaunchKernelGGL((k_gemm_mx_packed41<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_mx_packed<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s,
+                       p);
   return hipGetLastError();
 }
 
