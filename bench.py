@@ -550,9 +550,9 @@ GEMM_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_gemm.hip",)
 # WRITE_SIZE runs (KiB per dispatch, summed over the two products), scaled as above; valid
 # only for the kernel source they were taken on.
 GEMM_COUNTERS = {
-    "fetch_kib": 183027.0 + 183971.0, "fetch_scale": 2.0,
-    "write_kib": 229485.7 + 65555.3, "write_scale": 1.0,
-    "sources_sha256": "52a17577db7241866f57150632c865b039c2281605311cb7c36f1fe96381af21",
+    "fetch_kib": 183034.5 + 183978.5, "fetch_scale": 2.0,
+    "write_kib": 229469.7 + 65554.5, "write_scale": 1.0,
+    "sources_sha256": "1f02704219bdd265397a027ff98cc063b8e93c0fa4b1e10d3ed55485f9fd48d2",
 }
 
 
@@ -627,6 +627,8 @@ def bench_gemm(args, dq) -> None:
                 "tflops": m["flops"] / (t * 1e-3) / 1e12,
                 "frac": m["flops"] / (t * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
     tf = flops / (ms * 1e-3) / 1e12
+    # what the matrix cores sustain on this instruction with nothing but register operands
+    attainable = dq.bench_fp4_mfma_rate(20000, stream=stream)
     line = {
         "metric": "W4A4 MXFP4 product TFLOP/s (dense-equivalent), % FP4 matrix-core peak",
         "value": tf, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -639,6 +641,10 @@ def bench_gemm(args, dq) -> None:
         "roofline": {"bound": "mfma", "kernel": "k_gemm_mx_packed", "achieved": tf,
                      "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / FP4_MFMA_PEAK_TFLOPS, "traffic": gemm_traffic(),
+                     "attainable": attainable, "frac_attainable": tf / attainable,
+                     "attainable_note": "the same instruction streamed on register operands "
+                                        "alone (dq_bench_fp4_mfma_rate): the chip's clock "
+                                        "drops under full matrix-core load",
                      "traffic_unit": "HBM bytes per step",
                      "timing": "back-to-back asynchronous calls between one pair of events"},
         "products": per,

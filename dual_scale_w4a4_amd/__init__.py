@@ -51,7 +51,7 @@ class _Shape(ctypes.Structure):
     _fields_ = [("fused_halves", ctypes.c_int), ("fused_step_rows", ctypes.c_int),
                 ("fused_target", ctypes.c_int), ("pass_target", ctypes.c_int),
                 ("sweep_target", ctypes.c_int), ("row_resident", ctypes.c_int),
-                ("rowres_target", ctypes.c_int)]
+                ("rowres_target", ctypes.c_int), ("fused_ahead", ctypes.c_int)]
 
 
 _lib = None
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.dq_solve_timed.restype = I
         L.dq_bench_workspace_bytes.argtypes = [I64, I64, I, I, ctypes.POINTER(_Shape)]
         L.dq_bench_workspace_bytes.restype = SZ
+        L.dq_bench_fp4_mfma_rate.argtypes = [I, P, ctypes.POINTER(ctypes.c_double)]
+        L.dq_bench_fp4_mfma_rate.restype = I
         L.dq_quantize.argtypes = [P, I, I64, I64, I, I, P, P, P, P, P, P, SZ, P]
         L.dq_quantize.restype = I
         L.dq_act_workspace_bytes.argtypes = [I64, I64, I, I]
@@ -214,6 +216,16 @@ def bench_workspace_bytes(rows: int, cols: int, fmt: str, group: int, shape=None
     sh = _Shape(**(shape or {}))
     return int(lib().dq_bench_workspace_bytes(int(rows), int(cols), FMT[fmt], int(group),
                                               ctypes.byref(sh)))
+
+
+def bench_fp4_mfma_rate(iters: int = 20000, stream=None) -> float:
+    """dq_bench_fp4_mfma_rate: the attainable dense-equivalent TFLOP/s of the scaled FP4 matrix
+    instruction (register operands only)."""
+    out = ctypes.c_double(0.0)
+    st = lib().dq_bench_fp4_mfma_rate(int(iters), _stream(stream), ctypes.byref(out))
+    if st != 0:
+        raise DQError(st, "dq_bench_fp4_mfma_rate")
+    return float(out.value)
 
 
 def solve_outputs(W, fmt: str, group: int, T: int) -> Dict[str, object]:

@@ -43,6 +43,7 @@ constexpr int kTileCols = 512;
 struct LaunchShape {
   int halves = 1;
   int step_rows = 2;
+  int ahead = 1;
   int target = 512;
   int pass_target = 768;
   int sweep_target = 512;
@@ -56,6 +57,7 @@ bool launch_shape(const dq_launch_shape* in, LaunchShape* out) {
   if (in) {
     if (in->fused_halves > 0) f.halves = in->fused_halves;
     if (in->fused_step_rows > 0) f.step_rows = in->fused_step_rows;
+    if (in->fused_ahead > 0) f.ahead = in->fused_ahead;
     if (in->fused_target > 0) f.target = in->fused_target;
     if (in->pass_target > 0) f.pass_target = in->pass_target;
     if (in->sweep_target > 0) f.sweep_target = in->sweep_target;
@@ -63,6 +65,7 @@ bool launch_shape(const dq_launch_shape* in, LaunchShape* out) {
     if (in->rowres_target > 0) f.rowres_target = in->rowres_target;
   }
   if ((f.halves != 1 && f.halves != 2) || (f.step_rows != 2 && f.step_rows != 4) ||
+      (f.ahead != 1 && f.ahead != 3) || (f.ahead == 3 && (f.halves != 1 || f.step_rows != 2)) ||
       f.target > 65536 || f.pass_target > 65536 || f.sweep_target > 65536 ||
       f.rowres_target > 65536)
     return false;
@@ -382,6 +385,7 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.rpc = p.f_rpc;
   fu.halves = p.f_shape.halves;
   fu.step_rows = p.f_shape.step_rows;
+  fu.ahead = p.f_shape.ahead;
   fu.rowpart = rowpart;
   fu.colpart = colpart;
   fu.codes = io.codes;
@@ -717,6 +721,7 @@ dq_status time_isolated(const Plan& p, char* ws, const void* W, float* a, const 
   fu.rpc = p.f_rpc;
   fu.halves = p.f_shape.halves;
   fu.step_rows = p.f_shape.step_rows;
+  fu.ahead = p.f_shape.ahead;
   fu.rowpart = at<double2>(ws, p.off_rowpart);
   fu.colpart = at<double2>(ws, p.off_colpart);
   fu.a = a;

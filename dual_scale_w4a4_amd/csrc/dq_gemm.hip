@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "../../include/dq.h"
+#include "../../include/dq_bench.h"
 
 namespace dqg {
 
@@ -720,11 +721,14 @@ __device__ __forceinline__ void mfma_sel(v16f& acc, const u32x4& fa, const u32x4
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, KS, (int)sa, KS, (int)sb);
 }
 
-// Loads one stage issues (each lane): 16 weight fragments, 4 weight scale dwords, 8 token
-// loads, and on a period's first stage the token scales.
-constexpr int kStageLoads = 16 + 4 + 8;
+// ------------------------------------------------- packed weights: the tile loop
+// The four waves stack along the weight rows: wave w owns rows 64 w .. 64 w + 63 (two 32-row
+// blocks m) and all 256 tokens (eight blocks n), 2 x 8 products per k step, so every weight
+// fragment enters the CU once. Loads one stage issues (each lane): 8 weight fragments, 2
+// weight scale dwords, 8 token loads, and on a period's first stage the token scales.
+constexpr int kStageLoads = 8 + 2 + 8;
 
-// k step KS of stage s: 16 products in the order (m, n). Between them: the next step's four
+// k step KS of stage s: 16 products in the order (m, n). Between them: the next step's eight
 // token fragments from LDS (KS < 3); after the last product of weight-row block m, that block's
 // fragment of this step is reloaded with stage s + 2's, since its register is free from then on
 // (and at KS 3 the block's scale dword as well); two of stage s + 2's eight token loads into
@@ -733,181 +737,7 @@ constexpr int kStageLoads = 16 + 4 + 8;
 // nothing (a load to LDS that reads nothing still writes its zero bytes, into a buffer no
 // longer read), and every stage issues the same number of them.
 template <bool EDGE, int KS, int NX>
-__device__ __forceinline__ void packed_kstep(v16f (&acc)[4][4], u32x4 (&fa)[4][4],
-                                             const u32x4 (&fb)[4], u32x4 (&fb_next)[4],
-                                             const uint8_t* lx, int xterm, uint32_t (&sw)[4],
-                                             const uint32_t (&sx)[4], const PackedCtx& c,
-                                             PackedLds& lds, uint8_t* xb, int s2, bool on, int q,
-                                             bool xs_on) {
-#pragma unroll
-  for (int t = 0; t < 16; t++) {
-    const int m = t / 4, n = t % 4;
-    mfma_sel<KS>(acc[m][n], fa[m][KS], fb[n], sw[m], sx[n]);
-    if (t % 4 == 0 && KS < 3)
-      fb_next[t / 4] =
-          *reinterpret_cast<const u32x4*>(lx + (t / 4) * 32 * kRowB + (((KS + 1) ^ xterm) * 16));
-    if (n == 3) {
-      fa[m][KS] = __builtin_amdgcn_raw_buffer_load_b128(
-          on ? c.rwc : c.rnone, c.va[m], (uint32_t)((s2 * 4 + KS) * kPackBlockB), 0);
-      if (KS == 3)
-        sw[m] = __builtin_amdgcn_raw_buffer_load_b32(on ? c.rws : c.rnone, c.vs[m],
-                                                     (uint32_t)(s2 * kPackScaleB), 0);
-    }
-    if (t == 1 || t == 9) packed_load_x<EDGE>(c, xb, KS * 2 + t / 8, s2 * kRowB, on);
-    if (KS == 1 && t == 8 && NX > 8) packed_load_xs(c, lds, q, xs_on);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-template <bool BF16, bool VECY, bool EDGE>
-__device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int t0,
-                                                 PackedLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wi = (wave >> 1) * 128, wt = (wave & 1) * 128;
-  const int ldb = p.K / 2, nkb = p.K / 32;
-  const int nst = p.K / kBK;  // even: K % 512 == 0
-  const int nrb = (p.out + 31) / 32;
-  const int rl = lane & 31, h = lane >> 5;
-
-  PackedCtx c;
-  c.rwc = rsrc(p.wc, (uint32_t)nrb * (uint32_t)nst * 4u * kPackBlockB);
-  c.rws = rsrc(p.ws, (uint32_t)nrb * (uint32_t)nst * kPackScaleB);
-  c.rxc = rsrc(p.xc, (uint32_t)p.tokens * (uint32_t)ldb);
-  c.rxs = rsrc(p.xs, (uint32_t)p.tokens * (uint32_t)nkb);
-  // a descriptor that reads nothing: the loads of stages after the last go there (the loop
-  // body stays one basic block, so nothing can move across its barriers)
-  c.rnone = rsrc(p.wc, 0u);
-  c.t0 = t0;
-  c.rows_x = EDGE ? p.tokens : INT32_MAX;
-  c.ldb = ldb;
-  c.nst = nst;
-  c.wave = wave;
-  c.lane = lane;
-#pragma unroll
-  for (int m = 0; m < 4; m++) {
-    const int rb = (i0 + wi) / 32 + m;
-    const bool in = !EDGE || rb < nrb;
-    c.va[m] = in ? (uint32_t)rb * (uint32_t)nst * 4u * kPackBlockB + (uint32_t)(lane * 16) : kOob;
-    c.vs[m] = in ? (uint32_t)rb * (uint32_t)nst * kPackScaleB + (uint32_t)(lane * 4) : kOob;
-  }
-  {
-    const int lr = lane >> 3;
-    const uint32_t bx = (uint32_t)(t0 + wave * 64 + lr) * (uint32_t)ldb;
-    c.vx[0] = bx + (uint32_t)(((lane & 7) ^ lr) * 16);
-    c.vx[1] = bx + (uint32_t)(((lane & 7) ^ lr ^ 1) * 16);
-    const int rx = t0 + wave * 64 + lane;
-    c.sbx = (EDGE && rx >= p.tokens) ? kOob : (uint32_t)rx * (uint32_t)nkb;
-  }
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; m++)
-#pragma unroll
-    for (int n = 0; n < 4; n++) acc[m][n] = v16f{};
-
-  // token fragment reads: row wt + 32 n + lane % 32 of the buffer, chunk 4 h + ks at its
-  // swizzled position (4 h + ks) ^ term = ks ^ (term ^ 4 h)
-  const int xterm = (rl & 7) ^ ((rl >> 3) & 1) ^ (4 * h);
-  const int rx = (wt + rl) * kRowB;
-  const int sx_off = (wt + rl) * kScaleRowB + 4 * h;
-
-  u32x4 fa[2][4][4];  // [stage parity][m][ks]: the weight fragments of stages s and s + 1
-  uint32_t sw[2][4];  // [stage parity][m]: their scale dwords
-  u32x4 fb0[4], fb1[4];
-  uint32_t sx[4];
-
-  // prologue: stages 0 and 1 (weights and their scales into registers, tokens into buffers 0
-  // and 1) and token scale period 0
-#pragma unroll
-  for (int st = 0; st < 2; st++) {
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        fa[st][m][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            c.rwc, c.va[m], (uint32_t)((st * 4 + i) * kPackBlockB), 0);
-      sw[st][m] = __builtin_amdgcn_raw_buffer_load_b32(c.rws, c.vs[m],
-                                                       (uint32_t)(st * kPackScaleB), 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L.x[st], j, st * kRowB, true);
-  }
-  packed_load_xs(c, L, 0, true);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  auto stage_xs = [&](int par, int half) {
-    const uint8_t* bx = L.xs[par] + sx_off + half * 8;
-#pragma unroll
-    for (int n = 0; n < 4; n++) sx[n] = *reinterpret_cast<const uint32_t*>(bx + n * 32 * kScaleRowB);
-  };
-  auto first_frags = [&](int buf) {
-#pragma unroll
-    for (int n = 0; n < 4; n++)
-      fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
-  };
-  // stage s: products from registers fa[P] / sw[P] and token buffer s % 3, while stage s + 2
-  // loads into the slots they free and buffer (s + 2) % 3. At its end, the loads issued before
-  // it (those of stage s + 1) are complete in this wave, and after the barrier in every wave.
-  auto stage = [&](auto pc, auto nxc, int s, int q, bool xs_on) {
-    constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
-    const uint8_t* lx = L.x[s % 3] + rx;
-    uint8_t* xb = L.x[(s + 2) % 3];
-    const int s2 = s + 2;
-    const bool on = s2 < nst;
-    __builtin_amdgcn_sched_barrier(0);
-    packed_kstep<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads + (NX > 8 ? 1 : 0)));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  stage_xs(0, 0);
-  first_frags(0);
-
-  // two stages (one token scale period) per trip: stage 2 q (registers [0]) and stage 2 q + 1
-  // (registers [1]); token scales of period q + 1 load during 2 q
-  for (int q = 0; q < nst / 2; q++) {
-    const bool more = 2 * q + 2 < nst;
-    const int par = q & 1;
-    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 2 * q, q + 1, more);
-    stage_xs(par, 1);
-    first_frags((2 * q + 1) % 3);
-    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 2 * q + 1, q + 1,
-          false);
-    stage_xs(par ^ 1, 0);
-    first_frags((2 * q + 2) % 3);
-  }
-  store_tile<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
-}
-
-template <bool BF16, bool VECY>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) PackedLds lds;
-  int i0, t0;
-  tile_origin(p, i0, t0);
-  if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
-    gemm_tile_packed<BF16, VECY, false>(p, i0, t0, lds);
-  else
-    gemm_tile_packed<BF16, VECY, true>(p, i0, t0, lds);
-}
-
-// ------------------------------------------------- packed weights, 4 x 1 wave layout
-// The same tile and stage pipeline with the waves stacked along the weight rows: wave w owns
-// rows 64 w .. 64 w + 63 (two 32-row blocks) and all 256 tokens (eight blocks), 2 x 8
-// products per k step. Each weight fragment then enters the CU once (the 2 x 2 layout loads
-// every one twice, for the two waves that share its rows); each wave reads all eight token
-// fragments of a k step from LDS instead of four. Per stage a lane issues 8 fragment loads,
-// 2 scale loads and 8 token loads.
-constexpr int kStageLoads41 = 8 + 2 + 8;
-
-template <bool EDGE, int KS, int NX>
-__device__ __forceinline__ void packed_kstep41(v16f (&acc)[2][8], u32x4 (&fa)[2][4],
+__device__ __forceinline__ void packed_kstep(v16f (&acc)[2][8], u32x4 (&fa)[2][4],
                                                const u32x4 (&fb)[8], u32x4 (&fb_next)[8],
                                                const uint8_t* lx, int xterm, uint32_t (&sw)[2],
                                                const uint32_t (&sx)[8], const PackedCtx& c,
@@ -933,18 +763,18 @@ __device__ __forceinline__ void packed_kstep41(v16f (&acc)[2][8], u32x4 (&fa)[2]
   }
 }
 
-// The epilogue of the 4 x 1 layout: the wave's 64 x 256 results through LDS, 32 tokens at a
-// time (rows of 64 fp32 channels, padded by 16 bytes); a lane reads back 4 channels of one row,
-// 16 lanes to a row, and each store instruction writes four rows of 128 (bf16) or 256 bytes.
-constexpr int kRowStage41 = 64 * 4 + 16;
-static_assert(4 * 32 * kRowStage41 <= (int)sizeof(PackedLds), "epilogue staging does not fit");
+// The packed kernel's epilogue: the wave's 64 x 256 results through LDS, 32 tokens at a time
+// (rows of 64 fp32 channels, padded by 16 bytes); a lane reads back 4 channels of one row, 16
+// lanes to a row, and each store instruction writes four rows of 128 (bf16) or 256 bytes.
+constexpr int kRowStageRows = 64 * 4 + 16;
+static_assert(4 * 32 * kRowStageRows <= (int)sizeof(PackedLds), "epilogue staging does not fit");
 
 template <bool BF16, bool VECY, bool EDGE>
-__device__ __forceinline__ void store_tile41(const GemmArgs& p, const v16f (&acc)[2][8], int i0,
+__device__ __forceinline__ void store_tile_rows(const GemmArgs& p, const v16f (&acc)[2][8], int i0,
                                              int t0, uint8_t* stage) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, rl = lane & 31, h = lane >> 5;
   const int wi = wave * 64;
-  uint8_t* region = stage + wave * 32 * kRowStage41;
+  uint8_t* region = stage + wave * 32 * kRowStageRows;
   const int ich = i0 + wi + (lane & 15) * 4;  // the 4 channels this lane stores
   f32x4 av = {1.0f, 1.0f, 1.0f, 1.0f};
   if (p.a) {
@@ -965,13 +795,13 @@ __device__ __forceinline__ void store_tile41(const GemmArgs& p, const v16f (&acc
       for (int g = 0; g < 4; g++) {
         const f32x4 y = {acc[m][n][g * 4], acc[m][n][g * 4 + 1], acc[m][n][g * 4 + 2],
                          acc[m][n][g * 4 + 3]};
-        *reinterpret_cast<f32x4*>(region + rl * kRowStage41 + (m * 32 + g * 8 + h * 4) * 4) = y;
+        *reinterpret_cast<f32x4*>(region + rl * kRowStageRows + (m * 32 + g * 8 + h * 4) * 4) = y;
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const int row = (lane >> 4) + 4 * r;
-      f32x4 y = *reinterpret_cast<const f32x4*>(region + row * kRowStage41 + (lane & 15) * 16);
+      f32x4 y = *reinterpret_cast<const f32x4*>(region + row * kRowStageRows + (lane & 15) * 16);
       const int t = t0 + n * 32 + row;
       if (EDGE && t >= p.tokens) continue;
 #pragma unroll
@@ -1003,7 +833,7 @@ __device__ __forceinline__ void store_tile41(const GemmArgs& p, const v16f (&acc
 }
 
 template <bool BF16, bool VECY, bool EDGE>
-__device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, int t0,
+__device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int t0,
                                                    PackedLds& L) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1053,11 +883,13 @@ __device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, in
   const int rx = rl * kRowB;
   const int sx_off = rl * kScaleRowB + 4 * h;
 
-  u32x4 fa[2][2][4];  // [stage parity][m][ks]
-  uint32_t sw[2][2];  // [stage parity][m]
+  u32x4 fa[2][2][4];  // [stage parity][m][ks]: the weight fragments of stages s and s + 1
+  uint32_t sw[2][2];  // [stage parity][m]: their scale dwords
   u32x4 fb0[8], fb1[8];
   uint32_t sx[8];
 
+  // prologue: stages 0 and 1 (weights and their scales into registers, tokens into buffers 0
+  // and 1) and token scale period 0
 #pragma unroll
   for (int st = 0; st < 2; st++) {
 #pragma unroll
@@ -1086,6 +918,9 @@ __device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, in
     for (int n = 0; n < 8; n++)
       fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
   };
+  // stage s: products from registers fa[P] / sw[P] and token buffer s % 3, while stage s + 2
+  // loads into the slots they free and buffer (s + 2) % 3. At its end, the loads issued before
+  // it (those of stage s + 1) are complete in this wave, and after the barrier in every wave.
   auto stage = [&](auto pc, auto nxc, int s, int q, bool xs_on) {
     constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
     const uint8_t* lx = L.x[s % 3] + rx;
@@ -1093,11 +928,11 @@ __device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, in
     const int s2 = s + 2;
     const bool on = s2 < nst;
     __builtin_amdgcn_sched_barrier(0);
-    packed_kstep41<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep41<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep41<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep41<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads41 + (NX > 8 ? 1 : 0)));
+    packed_kstep<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads + (NX > 8 ? 1 : 0)));
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1106,6 +941,8 @@ __device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, in
   stage_xs(0, 0);
   first_frags(0);
 
+  // two stages (one token scale period) per trip: stage 2 q (registers [0]) and stage 2 q + 1
+  // (registers [1]); token scales of period q + 1 load during 2 q
   for (int q = 0; q < nst / 2; q++) {
     const bool more = 2 * q + 2 < nst;
     const int par = q & 1;
@@ -1117,31 +954,24 @@ __device__ __forceinline__ void gemm_tile_packed41(const GemmArgs& p, int i0, in
     stage_xs(par ^ 1, 0);
     first_frags((2 * q + 2) % 3);
   }
-  store_tile41<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
+  store_tile_rows<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
 }
 
 template <bool BF16, bool VECY>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed41(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_packed(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) PackedLds lds;
   int i0, t0;
   tile_origin(p, i0, t0);
   if (i0 + kBM <= p.out && t0 + kBN <= p.tokens)
-    gemm_tile_packed41<BF16, VECY, false>(p, i0, t0, lds);
+    gemm_tile_packed<BF16, VECY, false>(p, i0, t0, lds);
   else
-    gemm_tile_packed41<BF16, VECY, true>(p, i0, t0, lds);
+    gemm_tile_packed<BF16, VECY, true>(p, i0, t0, lds);
 }
-
-// The packed product's wave layout: 4 x 1 (each weight fragment loaded once per CU) or 2 x 2.
-constexpr bool kPackedWaves41 = true;
 
 template <bool BF16, bool VECY>
 hipError_t launch_packed_t(const GemmArgs& p, hipStream_t s) {
-  if (kPackedWaves41)
-    hipLaunchKernelGGL((k_gemm_mx_packed41<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0,
-                       s, p);
-  else
-    hipLaunchKernelGGL((k_gemm_mx_packed<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s,
-                       p);
+  hipLaunchKernelGGL((k_gemm_mx_packed<BF16, VECY>), dim3(p.nti * p.ntt), dim3(kThreads), 0, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -1169,6 +999,34 @@ hipError_t launch(const GemmArgs& p, bool bf16, bool fullk, bool dma, bool vecy,
   }
   if (fullk) return vecy ? launch_t<false, true, true>(p, s) : launch_t<false, true, false>(p, s);
   return vecy ? launch_t<false, false, true>(p, s) : launch_t<false, false, false>(p, s);
+}
+
+// The matrix cores' attainable rate: a stream of the scaled FP4 instruction on register
+// operands only (eight independent accumulators per wave, nothing read or written in the loop),
+// for comparison with the product's own rate at the clock the chip holds under that load. The
+// sums are kept alive by a store that happens only if a lane's sum is exactly -1 (into a word
+// of this module's own memory).
+__device__ float g_mfma_sink[1];
+
+__global__ __launch_bounds__(kThreads) void k_mfma_rate(int iters) {
+  v16f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc[i] = v16f{};
+  const int t = threadIdx.x;
+  const v8i A = {t, t * 3, t * 5, t * 7, 0, 0, 0, 0};
+  const v8i B = {t * 11, t * 13, t * 17, t * 19, 0, 0, 0, 0};
+  const int unit = 0x7F7F7F7F;  // E8M0 2^0 in every byte
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[i], 4, 4, 0, unit, 0, unit);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) sum += acc[i][e];
+  if (sum == -1.0f) g_mfma_sink[0] = sum;
 }
 
 }  // namespace dqg
@@ -1297,6 +1155,35 @@ dq_status dq_gemm_mx_packed(const uint8_t* act_codes, const uint8_t* act_scales,
     }
   }
   return DQ_OK;
+}
+
+dq_status dq_bench_fp4_mfma_rate(int iters, hipStream_t stream, double* tflops) {
+  if (iters < 1 || iters > (1 << 20) || !tflops) return DQ_ERR_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return DQ_ERR_HIP;
+  const dim3 grid((unsigned)(4 * cus));  // four 4-wave workgroups per CU
+  using namespace dqg;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  dq_status st = DQ_ERR_HIP;
+  float ms = 0.0f;
+  if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+    hipLaunchKernelGGL(k_mfma_rate, grid, dim3(kThreads), 0, stream, iters);  // warm-up
+    hipEventRecord(e0, stream);
+    hipLaunchKernelGGL(k_mfma_rate, grid, dim3(kThreads), 0, stream, iters);
+    hipEventRecord(e1, stream);
+    if (hipGetLastError() == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+        hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.0f) {
+      const double flops = 2.0 * 32 * 32 * 64 * 8.0 * iters * (double)grid.x * (kThreads / 64);
+      *tflops = flops / (ms * 1e-3) / 1e12;
+      st = DQ_OK;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return st;
 }
 
 }  // extern "C"

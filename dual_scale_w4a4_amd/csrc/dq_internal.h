@@ -52,6 +52,7 @@ struct FusedArgs {
   int64_t rpc;      // rows per chunk
   int halves;       // 512-column halves per lane: 1 or 2
   int step_rows;    // rows per load step: 2 or 4
+  int ahead;        // load steps in flight: 1, or 3 with one half and two rows per step
   double2* rowpart;  // [nct][m] (sum_j W t, sum_j (W - t)^2) with t = S b: R = ra * t
   double2* colpart;  // [nrc][n] (sum_i W S, sum_i S^2)
   double* epart;     // first pass (or null): [nct][m] partial sums of W^2 over each tile's columns

@@ -308,8 +308,9 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
 }
 
 // The pass. NH: 512-column halves per lane (the tile is 512 * NH columns); S: rows per load
-// step (loads run one step ahead of the rows being computed).
-template <int FMT, int G, bool PARTIAL, bool EMIT, int NH, int S, bool STAT>
+// step; D: load steps in flight (loads run D steps ahead of the rows being computed, in a ring
+// of D + 1 register buffers).
+template <int FMT, int G, bool PARTIAL, bool EMIT, int NH, int S, int D, bool STAT>
 __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   constexpr int LPG = G / kEpl;  // lanes per group
   constexpr int kCols = kTileCols * NH;
@@ -408,26 +409,28 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
     if (STAT) RE[r * kWave + lane] = q_out;
   };
 
-  // a batch is kFusedBatch / S load steps; buffers alternate so that each step's loads
-  // were issued one step earlier
+  // a batch is kFusedBatch / S load steps; before step st computes, the loads of step st + D
+  // (of this batch or the next) go out into the buffer step st - 1 has just used, so each
+  // step's rows were requested D steps earlier
   constexpr int kSteps = kFusedBatch / S;
-  static_assert(kSteps % 2 == 0, "an even number of steps per batch");
-  uint4 bufA[S][NH], bufB[S][NH];
-  if (nbatch > 0) load(first, bufA);
+  constexpr int NB = D + 1;
+  static_assert(kSteps % NB == 0, "a batch is a whole number of turns of the buffer ring");
+  uint4 buf[NB][S][NH];
+  if (nbatch > 0) {
+#pragma unroll
+    for (int j = 0; j < D; j++) load(first + j * S, buf[j]);
+  }
   for (int bt = 0; bt < nbatch; bt++) {
     const int row0 = first + bt * (kWaves * kFusedBatch);
 #pragma unroll
-    for (int st = 0; st < kSteps; st += 2) {
-      load(row0 + (st + 1) * S, bufB);
-#pragma unroll
-      for (int r = 0; r < S; r++) row_step(bufA[r], row0 + st * S + r, st * S + r);
-      __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < kSteps)
-        load(row0 + (st + 2) * S, bufA);
+    for (int st = 0; st < kSteps; st++) {
+      const int ls = st + D;
+      if (ls < kSteps)
+        load(row0 + ls * S, buf[ls % NB]);
       else if (bt + 1 < nbatch)
-        load(row0 + kWaves * kFusedBatch, bufA);
+        load(row0 + kWaves * kFusedBatch + (ls - kSteps) * S, buf[ls % NB]);
 #pragma unroll
-      for (int r = 0; r < S; r++) row_step(bufB[r], row0 + (st + 1) * S + r, (st + 1) * S + r);
+      for (int r = 0; r < S; r++) row_step(buf[st % NB][r], row0 + st * S + r, st * S + r);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -863,30 +866,34 @@ hipError_t launch_finalize(const FinArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, bool PARTIAL, bool EMIT, int NH, int S, bool STAT>
+template <int FMT, bool PARTIAL, bool EMIT, int NH, int S, int D, bool STAT>
 static hipError_t fused_group(const FusedArgs& a, dim3 grid, hipStream_t s) {
   switch (a.G) {
-    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT, NH, S, STAT>), grid, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused_mx<FMT, 16, PARTIAL, EMIT, NH, S, D, STAT>), grid, dim3(kBlock), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_fused_mx<FMT, 32, PARTIAL, EMIT, NH, S, D, STAT>), grid, dim3(kBlock), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_fused_mx<FMT, 64, PARTIAL, EMIT, NH, S, D, STAT>), grid, dim3(kBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, bool EMIT, int NH, int S, bool STAT>
+template <int FMT, bool EMIT, int NH, int S, int D, bool STAT>
 static hipError_t fused_shape(const FusedArgs& a, dim3 grid, hipStream_t s) {
   // masking only when some tile extends past the last column
-  return a.n % (kTileCols * NH) != 0 ? fused_group<FMT, true, EMIT, NH, S, STAT>(a, grid, s)
-                                     : fused_group<FMT, false, EMIT, NH, S, STAT>(a, grid, s);
+  return a.n % (kTileCols * NH) != 0 ? fused_group<FMT, true, EMIT, NH, S, D, STAT>(a, grid, s)
+                                     : fused_group<FMT, false, EMIT, NH, S, D, STAT>(a, grid, s);
 }
 
+// (halves, rows per step, steps in flight): (1, 2, 1), (1, 2, 3), (1, 4, 1), (2, 2, 1), (2, 4, 1)
 template <int FMT, bool EMIT, bool STAT>
 static hipError_t fused_variant(const FusedArgs& a, dim3 grid, hipStream_t s) {
-  if (a.halves == 1) return a.step_rows == 4 ? fused_shape<FMT, EMIT, 1, 4, STAT>(a, grid, s)
-                                             : fused_shape<FMT, EMIT, 1, 2, STAT>(a, grid, s);
-  return a.step_rows == 4 ? fused_shape<FMT, EMIT, 2, 4, STAT>(a, grid, s)
-                          : fused_shape<FMT, EMIT, 2, 2, STAT>(a, grid, s);
+  if (a.halves == 1) {
+    if (a.step_rows == 4) return fused_shape<FMT, EMIT, 1, 4, 1, STAT>(a, grid, s);
+    return a.ahead == 3 ? fused_shape<FMT, EMIT, 1, 2, 3, STAT>(a, grid, s)
+                        : fused_shape<FMT, EMIT, 1, 2, 1, STAT>(a, grid, s);
+  }
+  return a.step_rows == 4 ? fused_shape<FMT, EMIT, 2, 4, 1, STAT>(a, grid, s)
+                          : fused_shape<FMT, EMIT, 2, 2, 1, STAT>(a, grid, s);
 }
 
 template <int FMT>

@@ -49,6 +49,8 @@ typedef struct {
  *  fused_halves:     single-sweep MX pass, 512-column halves per lane (1 or 2; default 1)
  *  fused_step_rows:  single-sweep MX pass, rows per load step (2 or 4; default 2)
  *  fused_target:     single-sweep MX pass, target workgroup count (default 512)
+ *  fused_ahead:      single-sweep MX pass, load steps in flight per wave (1 or 3; 3 only with
+ *                    one half and two rows per step; default 1)
  *  pass_target:      two-sweep pass for bf16 weights, target workgroup count (default 768)
  *  sweep_target:     general sweep (fp32 weights), target workgroup count (default 512)
  *  row_resident:     INT4_BF16 / NVFP4 on bf16 weights (tensor scale fixed for the solve), rows
@@ -64,6 +66,7 @@ typedef struct {
   int sweep_target;
   int row_resident;
   int rowres_target;
+  int fused_ahead;
 } dq_launch_shape;
 
 /* dq_workspace_bytes for a solve in the given launch shape (NULL: the default one). */
@@ -79,6 +82,16 @@ dq_status dq_solve_timed(const void* W, dq_dtype wt, int64_t rows, int64_t cols,
                          void* inner_scales, float* tensor_scale, float* a, float* b,
                          double* mse, void* workspace, size_t workspace_bytes,
                          const dq_launch_shape* shape, dq_timing* timing, hipStream_t stream);
+
+/* The matrix cores' attainable rate for the W4A4 product's instruction (the scaled 32x32x64
+ * MFMA with E2M1 operands and E8M0 scales): a stream of it on register operands only, nothing
+ * read or written in the loop, eight independent accumulators per wave and four 4-wave
+ * workgroups per CU, `iters` rounds of eight instructions per wave (1 .. 2^20), timed with HIP
+ * events on `stream` after one untimed launch. *tflops receives the dense-equivalent TFLOP/s
+ * (2 * 32 * 32 * 64 flops per instruction): what the chip sustains at the clock it holds under
+ * such load, beside the published peak. Blocks until the timed launch ends. Returns DQ_ERR_ARG
+ * for iters out of range or a null tflops, DQ_ERR_HIP if a HIP call fails. */
+dq_status dq_bench_fp4_mfma_rate(int iters, hipStream_t stream, double* tflops);
 
 #ifdef __cplusplus
 }

@@ -128,6 +128,8 @@ def test_pack_weights_layout(dq, out, K):
     (97, 70, 512),       # channels neither a multiple of 32 nor of 4
     (33, 1000, 1536),    # several channel tiles, an odd number of stage pairs
     (1, 4, 512),         # the smallest call
+    (300, 300, 3072),    # K % 1024 == 0: the four-stage ring, three trips of its loop
+    (520, 260, 2048),    # the four-stage ring over several token tiles
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_packed_gemm_matches_oracle(dq, oracle_lib, tokens, out, K, out_dtype):

@@ -105,6 +105,32 @@ def test_single_sweep_equals_two_sweep(dq, fmt):
         assert np.all(np.abs(mf - mg) <= 1e-6 * mg), (w.name, mf, mg)
 
 
+FUSED_AHEAD_CASES = [
+    # (rows, cols, format, group): row counts that end inside an 8-row batch and inside a load
+    # step, column counts that end inside a 512-column tile, every group size
+    (203, 1088, "mxfp4", 32), (77, 2080, "mxint4", 16), (300, 4096, "mxfp4", 64),
+    (33, 512, "mxint4", 32), (517, 96, "mxfp4", 32),
+]
+
+
+@pytest.mark.parametrize("rows,cols,fmt,group", FUSED_AHEAD_CASES)
+def test_single_sweep_load_distance_keeps_the_results(dq, oracle_lib, rows, cols, fmt, group):
+    # the single-sweep pass with its loads three steps ahead instead of one: the same rows in
+    # the same order per wave, so every output is bit-identical, and equal to the oracle's
+    T = 6
+    Wb = rand_w(rows, cols, seed=rows * 3 + cols, dtype="bf16", outliers=max(1, cols // 200))
+    W = to_device(Wb, "bf16")
+    print(f"[solve] fused ahead {rows}x{cols} {fmt} G{group}", flush=True)
+    far = dq.solve(W, fmt, group, T, shape={"fused_ahead": 3}, timing=True)
+    near = dq.solve(W, fmt, group, T, shape={"fused_ahead": 1}, timing=True)
+    assert far["used_fused"] and near["used_fused"]
+    for k in ("a", "b", "codes", "scales", "mse"):
+        assert np.array_equal(host(far[k]), host(near[k])), k
+    ref = oracle_lib.solve(Wb, "bf16", fmt, group, T, diag=True)
+    res = compare_solve(far, ref, fmt, rows, cols)
+    assert_parity(res, exact=float(ref["margin"].min()) > 1e-9, name=f"{rows}x{cols} {fmt}")
+
+
 def test_single_sweep_falls_back_outside_its_range(dq, oracle_lib):
     # a few groups scaled far down: their shared exponent lies outside the range where the
     # single-sweep identity is guaranteed, so the solver must re-run on the two-sweep path

@@ -17,7 +17,7 @@ BENCH_HEADER = os.path.join(ROOT, "include", "dq_bench.h")
 def _declared_functions(header=HEADER):
     src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dq_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
 
 
 def test_bench_header_declares_only_the_measurement_hooks():
-    assert _declared_functions(BENCH_HEADER) == ["dq_bench_workspace_bytes", "dq_solve_timed"]
+    assert _declared_functions(BENCH_HEADER) == ["dq_bench_fp4_mfma_rate",
+                                                 "dq_bench_workspace_bytes", "dq_solve_timed"]
     # the solver's own header carries no timing or launch-shape types
     src = open(HEADER).read()
     assert "dq_timing" not in src and "launch_shape" not in src
@@ -147,6 +148,15 @@ def test_invalid_arguments_are_rejected_on_the_host(dqlib):
     assert call_timed(shape=dqlib._Shape(3, 0, 0, 0, 0)) == 1  # halves: 1 or 2
     assert call_timed(shape=dqlib._Shape(0, 3, 0, 0, 0)) == 1  # step rows: 2 or 4
     assert call_timed(shape=dqlib._Shape(0, 0, 70000, 0, 0)) == 1
+    assert call_timed(shape=dqlib._Shape(fused_ahead=2)) == 1  # steps in flight: 1 or 3
+    assert call_timed(shape=dqlib._Shape(fused_ahead=3, fused_step_rows=4)) == 1
+    assert call_timed(shape=dqlib._Shape(fused_ahead=3, fused_halves=2)) == 1
+
+    # the matrix-core rate hook checks its arguments before any HIP call
+    rate = ctypes.c_double(0.0)
+    assert L.dq_bench_fp4_mfma_rate(0, None, ctypes.byref(rate)) == 1
+    assert L.dq_bench_fp4_mfma_rate((1 << 20) + 1, None, ctypes.byref(rate)) == 1
+    assert L.dq_bench_fp4_mfma_rate(100, None, None) == 1
 
 
 def test_workspace_size_does_not_depend_on_the_environment(dqlib):
