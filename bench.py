@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": 57457.0, "fetch_scale": 2.0,  # average over both matrices' launches
+    "fetch_kib": 57467.0, "fetch_scale": 2.0,  # average over both matrices' launches
     "write_kib": 5968.0, "write_scale": 1.0,
-    "sources_sha256": "7144f6e193e3d9fbcd014cdfa327f018ac9317c3716ac415dae73f4a217709a9",
+    "sources_sha256": "82b312624508fe2300e189178946917accde37dcf2403eda6a8a798abd26003b",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -52,7 +52,7 @@ VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
     "per_elem": {"3/fused": 10.82, "4/row": 23.23, "4/col": 22.95, "5/row": 14.24,
                  "5/col": 14.09},  # workload / pass kind
-    "sources_sha256": "96e05f7c7c6ab948ec3ebb9fc993068d97a860a584d417e79d168844b01185aa",
+    "sources_sha256": "e6563165a7ad330093cfd024610468e3537e4d5c9cc5557bf278b0c1a09ef1ec",
 }
 
 
