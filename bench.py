@@ -628,7 +628,7 @@ def bench_gemm(args, dq) -> None:
                 "frac": m["flops"] / (t * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
     tf = flops / (ms * 1e-3) / 1e12
     # what the matrix cores sustain on this instruction with nothing but register operands
-    attainable = dq.bench_fp4_mfma_rate(20000, stream=stream)
+    attainable = max(dq.bench_fp4_mfma_rate(20000, stream=stream) for _ in range(2))
     line = {
         "metric": "W4A4 MXFP4 product TFLOP/s (dense-equivalent), % FP4 matrix-core peak",
         "value": tf, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
