@@ -729,7 +729,9 @@ __device__ __forceinline__ void mfma_sel(v16f& acc, const u32x4& fa, const u32x4
 constexpr int kStageLoads = 8 + 2 + 8;
 
 // k step KS of stage s: 16 products in the order (m, n). Between them: the next step's eight
-// token fragments from LDS (KS < 3); after the last product of weight-row block m, that block's
+// token fragments from LDS (at KS 3 the next stage's first fragments and its token scales,
+// which the barrier before that step has made readable); after the last product of weight-row
+// block m, that block's
 // fragment of this step is reloaded with stage s + 2's, since its register is free from then on
 // (and at KS 3 the block's scale dword as well); two of stage s + 2's eight token loads into
 // its LDS buffer xb; and at KS 1 of a period's first stage (NX > 8) the next period's token
@@ -740,9 +742,10 @@ template <bool EDGE, int KS, int NX>
 __device__ __forceinline__ void packed_kstep(v16f (&acc)[2][8], u32x4 (&fa)[2][4],
                                                const u32x4 (&fb)[8], u32x4 (&fb_next)[8],
                                                const uint8_t* lx, int xterm, uint32_t (&sw)[2],
-                                               const uint32_t (&sx)[8], const PackedCtx& c,
-                                               PackedLds& lds, uint8_t* xb, int s2, bool on,
-                                               int q, bool xs_on) {
+                                               const uint32_t (&sx)[8], uint32_t (&sx_next)[8],
+                                               const uint8_t* lx_next, const uint8_t* bx_next,
+                                               const PackedCtx& c, PackedLds& lds, uint8_t* xb,
+                                               int s2, bool on, int q, bool xs_on) {
 #pragma unroll
   for (int t = 0; t < 16; t++) {
     const int m = t / 8, n = t % 8;
@@ -750,6 +753,11 @@ __device__ __forceinline__ void packed_kstep(v16f (&acc)[2][8], u32x4 (&fa)[2][4
     if (t % 2 == 0 && KS < 3)
       fb_next[t / 2] =
           *reinterpret_cast<const u32x4*>(lx + (t / 2) * 32 * kRowB + (((KS + 1) ^ xterm) * 16));
+    if (t % 2 == 0 && KS == 3)  // the next stage's first fragments
+      fb_next[t / 2] =
+          *reinterpret_cast<const u32x4*>(lx_next + (t / 2) * 32 * kRowB + ((0 ^ xterm) * 16));
+    if (t % 2 == 1 && KS == 3)  // and its token scales
+      sx_next[t / 2] = *reinterpret_cast<const uint32_t*>(bx_next + (t / 2) * 32 * kScaleRowB);
     if (n == 7) {
       fa[m][KS] = __builtin_amdgcn_raw_buffer_load_b128(
           on ? c.rwc : c.rnone, c.va[m], (uint32_t)((s2 * 4 + KS) * kPackBlockB), 0);
@@ -886,10 +894,10 @@ __device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int 
   u32x4 fa[2][2][4];  // [stage parity][m][ks]: the weight fragments of stages s and s + 1
   uint32_t sw[2][2];  // [stage parity][m]: their scale dwords
   u32x4 fb0[8], fb1[8];
-  uint32_t sx[8];
+  uint32_t sx[2][8];  // [stage parity][n]: token scale dwords of stages s and s + 1
 
-  // prologue: stages 0 and 1 (weights and their scales into registers, tokens into buffers 0
-  // and 1) and token scale period 0
+  // prologue: stage 0 (weights and their scales into registers, tokens into buffer 0) and
+  // token scale period 0, then stage 1; only the first two have to land before the loop starts
 #pragma unroll
   for (int st = 0; st < 2; st++) {
 #pragma unroll
@@ -903,57 +911,70 @@ __device__ __forceinline__ void gemm_tile_packed(const GemmArgs& p, int i0, int 
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) packed_load_x<EDGE>(c, L.x[st], j, st * kRowB, true);
+    if (st == 0) packed_load_xs(c, L, 0, true);
   }
-  packed_load_xs(c, L, 0, true);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads));  // stage 1's loads may be in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  auto stage_xs = [&](int par, int half) {
-    const uint8_t* bx = L.xs[par] + sx_off + half * 8;
-#pragma unroll
-    for (int n = 0; n < 8; n++) sx[n] = *reinterpret_cast<const uint32_t*>(bx + n * 32 * kScaleRowB);
-  };
-  auto first_frags = [&](int buf) {
+  // stage 0's token scales and first fragments
+  {
+    const uint8_t* bx = L.xs[0] + sx_off;
 #pragma unroll
     for (int n = 0; n < 8; n++)
-      fb0[n] = *reinterpret_cast<const u32x4*>(L.x[buf] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
-  };
-  // stage s: products from registers fa[P] / sw[P] and token buffer s % 3, while stage s + 2
-  // loads into the slots they free and buffer (s + 2) % 3. At its end, the loads issued before
-  // it (those of stage s + 1) are complete in this wave, and after the barrier in every wave.
+      sx[0][n] = *reinterpret_cast<const uint32_t*>(bx + n * 32 * kScaleRowB);
+#pragma unroll
+    for (int n = 0; n < 8; n++)
+      fb0[n] = *reinterpret_cast<const u32x4*>(L.x[0] + rx + n * 32 * kRowB + ((0 ^ xterm) * 16));
+  }
+  // stage s: products from registers fa[P] / sw[P] / sx[P] and token buffer s % 3, while stage
+  // s + 2 loads into the slots they free and buffer (s + 2) % 3. Before its last k step, every
+  // load issued before the stage (those of stage s + 1) is complete in this wave and its LDS
+  // reads are done, and after the barrier the same holds in every wave: the last step then
+  // reads stage s + 1's first fragments and token scales (into fb0 and sx[P ^ 1]) under its own
+  // products, so the matrix instructions run on across the stage boundary. The barrier also
+  // orders every wave's reads of buffer (s - 1) % 3 before stage s + 1's loads into it.
   auto stage = [&](auto pc, auto nxc, int s, int q, bool xs_on) {
     constexpr int P = decltype(pc)::value, NX = decltype(nxc)::value;
     const uint8_t* lx = L.x[s % 3] + rx;
     uint8_t* xb = L.x[(s + 2) % 3];
     const int s2 = s + 2;
     const bool on = s2 < nst;
+    // stage s + 1's scales: period (s + 1) / 2, half (s + 1) % 2 (past the last stage these
+    // reads land in buffers that no load is writing, and their values go unused)
+    const uint8_t* lxn = L.x[(s + 1) % 3] + rx;
+    const uint8_t* bxn = L.xs[((s + 1) >> 1) & 1] + sx_off + (P ^ 1) * 8;
     __builtin_amdgcn_sched_barrier(0);
-    packed_kstep<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    packed_kstep<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx, c, L, xb, s2, on, q, xs_on);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads + (NX > 8 ? 1 : 0)));
+    packed_kstep<EDGE, 0, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx[P], sx[P ^ 1], lxn, bxn,
+                              c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 1, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx[P], sx[P ^ 1], lxn, bxn,
+                              c, L, xb, s2, on, q, xs_on);
+    packed_kstep<EDGE, 2, NX>(acc, fa[P], fb0, fb1, lx, xterm, sw[P], sx[P], sx[P ^ 1], lxn, bxn,
+                              c, L, xb, s2, on, q, xs_on);
+    // steps 0-2 issued 4 loads each (2 weight fragments, 2 token loads), and at a period's
+    // first stage the token scales
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * 4 + (NX > 8 ? 1 : 0)) & ~(15 << 8));  // lgkmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
+    packed_kstep<EDGE, 3, NX>(acc, fa[P], fb1, fb0, lx, xterm, sw[P], sx[P], sx[P ^ 1], lxn, bxn,
+                              c, L, xb, s2, on, q, xs_on);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  stage_xs(0, 0);
-  first_frags(0);
 
   // two stages (one token scale period) per trip: stage 2 q (registers [0]) and stage 2 q + 1
   // (registers [1]); token scales of period q + 1 load during 2 q
   for (int q = 0; q < nst / 2; q++) {
     const bool more = 2 * q + 2 < nst;
-    const int par = q & 1;
     stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 9>{}, 2 * q, q + 1, more);
-    stage_xs(par, 1);
-    first_frags((2 * q + 1) % 3);
     stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, 2 * q + 1, q + 1,
           false);
-    stage_xs(par ^ 1, 0);
-    first_frags((2 * q + 2) % 3);
   }
+  // the last stages' loads read nothing but still write their LDS buffers: drain them before
+  // the epilogue reuses that memory
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   store_tile_rows<BF16, VECY, EDGE>(p, acc, i0, t0, reinterpret_cast<uint8_t*>(&L));
 }
 
