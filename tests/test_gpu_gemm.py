@@ -257,3 +257,12 @@ def test_gemm_random_shapes(dq, oracle_lib):
         a = rng.uniform(0.05, 3.0, out).astype(np.float32) if case % 4 else None
         _check(dq, oracle_lib, xc, xs, wc, ws, a, out_dtype, name=f"random case {case}",
                packed=packed)
+
+
+def test_matrix_core_rate_hook(dq):
+    # dq_bench_fp4_mfma_rate: a positive dense-equivalent rate below the published 10.1 PFLOP/s
+    # peak (a stream at a settled clock reaches 8.6-8.9 on MI355X; a short, cold one less)
+    print("[gemm] matrix-core rate hook", flush=True)
+    rates = [dq.bench_fp4_mfma_rate(2000) for _ in range(3)]
+    assert all(0.0 < r < 10100.0 for r in rates), rates
+    assert max(rates) > 2000.0, rates
