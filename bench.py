@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": 57467.0, "fetch_scale": 2.0,  # average over both matrices' launches
+    "fetch_kib": 57467.1, "fetch_scale": 2.0,  # average over both matrices' launches
     "write_kib": 5968.0, "write_scale": 1.0,
-    "sources_sha256": "82b312624508fe2300e189178946917accde37dcf2403eda6a8a798abd26003b",
+    "sources_sha256": "8ff0793c8cef51ef141501d4a304ed62ac8c3c1e3cbe22d9332ddff038b86e64",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -50,9 +50,9 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {"3/fused": 10.82, "4/row": 23.23, "4/col": 22.95, "5/row": 14.24,
+    "per_elem": {"3/fused": 10.45, "4/row": 23.23, "4/col": 22.95, "5/row": 14.24,
                  "5/col": 14.09},  # workload / pass kind
-    "sources_sha256": "e6563165a7ad330093cfd024610468e3537e4d5c9cc5557bf278b0c1a09ef1ec",
+    "sources_sha256": "3105ae3f1fddcfde36d9fa71f9c1c81f2bbdf1bb7fded4d2a5dced7c5f60273e",
 }
 
 

@@ -212,15 +212,15 @@ struct FusedLane {
 
 // One row of 8 * NH elements (NH 512-column halves of the tile): codes, the row's partial
 // sums and the column accumulators. PARTIAL: the tile extends past column n; amask[h]
-// zeroes a half that lies past it. gmax / gmin track the largest group max and the smallest
-// nonzero one (bit patterns, gmin offset by one so that a zero group never counts).
+// zeroes a half that lies past it. mbo[h] returns the bit pattern of the group max of half h,
+// which the caller folds into the range it tracks.
 // EMIT: the final pass; instead of the sums for the updates it stores the packed codes and
 // the E8M0 inner-scale bytes of the row (abits = bits of a_i) and keeps only the row error.
 // first: the batch's first row, which starts the batch column sums Pb / Qb.
 template <int FMT, int LPG, int NH, bool PARTIAL, bool EMIT, bool STAT>
 __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L, float& macc,
-                                          float& eacc, double& wsq, uint32_t& gmax,
-                                          uint32_t& gmin, const uint32_t (&amask)[NH],
+                                          float& eacc, double& wsq, uint32_t (&mbo)[NH],
+                                          const uint32_t (&amask)[NH],
                                           uint32_t* codes_row, uint8_t* scales_row,
                                           uint32_t abits, bool first) {
   macc = 0.0f;
@@ -247,10 +247,14 @@ __device__ __forceinline__ void fused_row(const uint4 (&v)[NH], FusedLane<NH>& L
       if (STAT) wsq = fma((double)w[k], (double)w[k], wsq);  // W^2 is exact in fp64
     }
     const uint32_t mb = group_max_bits<LPG>(f2u(mx));
-    gmax = max(gmax, mb);
-    gmin = min(gmin, mb - 1u);  // a zero group wraps to 0xFFFFFFFF
-    // c = 2^(floor(log2 mx) - 2); an all-zero group gets a harmless normal c
-    const uint32_t cb = max(mb & 0x7F800000u, 3u << 23) - (2u << 23);
+    mbo[h] = mb;
+    // c = 2^(floor(log2 mx) - 2). The scaled FP4 conversions read only the exponent field of
+    // their fp32 scale, so for MXFP4 the max's own bits less two in the exponent are c; the
+    // subtraction saturates at 0 (exponent field 0, the scale 2^-127) for an all-zero group,
+    // whose codes are 0 whatever the scale. MXINT4 divides and multiplies by c itself, so there
+    // c is an exact power of two and an all-zero group gets a harmless normal one.
+    const uint32_t cb = FMT == kMxFp4 ? __builtin_elementwise_sub_sat(mb, 2u << 23)
+                                      : max(mb & 0x7F800000u, 3u << 23) - (2u << 23);
     const float c = u2f(cb);
     float S[8];
     uint32_t packed = 0;  // the 8 codes as nibbles, column 2k low (EMIT)
@@ -383,10 +387,10 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
   };
   float2* R = smem + wave * (kFusedBatch * kWave);  // this wave's [8 rows][64 lanes] partials
   double* RE = smem_e + (STAT ? wave * (kFusedBatch * kWave) : 0);
-  // one row, skipped (uniformly) when it lies past the chunk; its lane partials go to LDS
-  auto row_step = [&](const uint4 (&v)[NH], int i, int r) {
-    float n_out = 0.0f, e_out = 0.0f;
-    double q_out = 0.0;
+  // one row, skipped (uniformly) when it lies past the chunk. Its lane partials go to LDS; a
+  // skipped row writes none, since the batch reduction stores only rows inside the chunk. mbo
+  // returns the row's group max bits per half (0, which changes no range, for a skipped row).
+  auto row_step = [&](const uint4 (&v)[NH], int i, int r, uint32_t (&mbo)[NH]) {
     // a batch's first row always lies inside the chunk (nbatch counts batches that start
     // before r_end); were it skipped, the batch column sums would still restart at zero
     if (r == 0 && !EMIT && !(i < r_end)) {
@@ -394,6 +398,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
       for (int e = 0; e < 8 * NH; e++) L.Pb[e] = L.Qb[e] = 0.0f;
     }
     if (i < r_end) {
+      float n_out, e_out;
+      double q_out;
       uint32_t* codes_row = nullptr;
       uint8_t* scales_row = nullptr;
       uint32_t abits = 0u;
@@ -402,11 +408,14 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         scales_row = p.scales + (int64_t)i * (n / G) + col[0] / G;
         abits = f2u(p.a[i]);
       }
-      fused_row<FMT, LPG, NH, PARTIAL, EMIT, STAT>(v, L, n_out, e_out, q_out, gmax, gmin, amask,
+      fused_row<FMT, LPG, NH, PARTIAL, EMIT, STAT>(v, L, n_out, e_out, q_out, mbo, amask,
                                                    codes_row, scales_row, abits, r == 0);
+      R[r * kWave + lane] = make_float2(n_out, e_out);
+      if (STAT) RE[r * kWave + lane] = q_out;
+    } else {
+#pragma unroll
+      for (int h = 0; h < NH; h++) mbo[h] = 0u;
     }
-    R[r * kWave + lane] = make_float2(n_out, e_out);
-    if (STAT) RE[r * kWave + lane] = q_out;
   };
 
   // a batch is kFusedBatch / S load steps; before step st computes, the loads of step st + D
@@ -429,8 +438,24 @@ __global__ __launch_bounds__(kBlock) void k_fused_mx(FusedArgs p) {
         load(row0 + ls * S, buf[ls % NB]);
       else if (bt + 1 < nbatch)
         load(row0 + kWaves * kFusedBatch + (ls - kSteps) * S, buf[ls % NB]);
+      uint32_t mbs[S][NH];
 #pragma unroll
-      for (int r = 0; r < S; r++) row_step(buf[st % NB][r], row0 + st * S + r, st * S + r);
+      for (int r = 0; r < S; r++) row_step(buf[st % NB][r], row0 + st * S + r, st * S + r, mbs[r]);
+      // the range of the step's group maxima: gmax the largest, gmin the smallest nonzero one
+      // less one (a zero group wraps to 0xFFFFFFFF and never counts)
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        if (S == 2) {
+          gmax = max(gmax, max(mbs[0][h], mbs[1][h]));
+          gmin = min(gmin, min(mbs[0][h] - 1u, mbs[1][h] - 1u));
+        } else {
+#pragma unroll
+          for (int r = 0; r < S; r++) {
+            gmax = max(gmax, mbs[r][h]);
+            gmin = min(gmin, mbs[r][h] - 1u);
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
