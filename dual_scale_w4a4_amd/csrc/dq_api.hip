@@ -28,6 +28,7 @@
 namespace {
 
 constexpr int kTileCols = 512;
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;  // MI355X's last-level (MALL) cache
 
 // Launch shape of the iteration passes. The defaults were measured best on MI355X for the
 // 8B shapes. Row-resident pass (INT4_BF16 / NVFP4 rows of up to 4096 columns): off, since the
@@ -35,7 +36,10 @@ constexpr int kTileCols = 512;
 // instructions per element); when on, 256 workgroups (one 8-wave workgroup per CU; 384 and
 // 512 were slower on the 14336-row matrices). Single-sweep MX pass: one 512-column half per
 // lane, two rows per load step and about two 4-wave workgroups per CU, so that two matrices solved at once on two streams
-// share the GPU (a matrix alone runs its pass as fast with three). Two-sweep pass for bf16
+// share the GPU (a matrix alone runs its pass as fast with three); a matrix whose bf16 W
+// exceeds the 256 MiB Infinity Cache reads W from HBM on every pass, where three workgroups
+// per CU keep more loads in flight (4.94 against 4.48 TB/s on a 28672 x 8192 matrix; four per
+// CU gave 4.90), so it takes about three. Two-sweep pass for bf16
 // weights: 768 workgroups (a sweep of 768-3072 moved it by under 10%). General sweep for
 // fp32 weights: 512. The product entry points always take these defaults; only the
 // measurement entry point (dq_solve_timed) takes another shape, so the fixed summation order
@@ -45,6 +49,7 @@ struct LaunchShape {
   int step_rows = 2;
   int ahead = 1;
   int target = 512;
+  int target_big = 768;  // W larger than the Infinity Cache
   int pass_target = 768;
   int sweep_target = 512;
   bool row_resident = false;
@@ -58,7 +63,7 @@ bool launch_shape(const dq_launch_shape* in, LaunchShape* out) {
     if (in->fused_halves > 0) f.halves = in->fused_halves;
     if (in->fused_step_rows > 0) f.step_rows = in->fused_step_rows;
     if (in->fused_ahead > 0) f.ahead = in->fused_ahead;
-    if (in->fused_target > 0) f.target = in->fused_target;
+    if (in->fused_target > 0) f.target = f.target_big = in->fused_target;
     if (in->pass_target > 0) f.pass_target = in->pass_target;
     if (in->sweep_target > 0) f.sweep_target = in->sweep_target;
     if (in->row_resident != 0) f.row_resident = in->row_resident > 0;
@@ -128,7 +133,8 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = 
   p.f_shape = shape;
   const int64_t f_cols = (int64_t)kTileCols * p.f_shape.halves;
   p.f_nct = (int)((n + f_cols - 1) / f_cols);
-  int64_t f_want = (p.f_shape.target + p.f_nct - 1) / p.f_nct;
+  const int f_target = m * n * 2 > kInfinityCacheBytes ? p.f_shape.target_big : p.f_shape.target;
+  int64_t f_want = (f_target + p.f_nct - 1) / p.f_nct;
   if (f_want < 1) f_want = 1;
   p.f_rpc = (m + f_want - 1) / f_want;
   p.f_rpc = (p.f_rpc + 31) / 32 * 32;  // whole 32-row batches per workgroup

@@ -48,7 +48,8 @@ typedef struct {
 /* Launch shape of the iteration passes; a field <= 0 keeps the default.
  *  fused_halves:     single-sweep MX pass, 512-column halves per lane (1 or 2; default 1)
  *  fused_step_rows:  single-sweep MX pass, rows per load step (2 or 4; default 2)
- *  fused_target:     single-sweep MX pass, target workgroup count (default 512)
+ *  fused_target:     single-sweep MX pass, target workgroup count (default 512, and 768 for a
+ *                    matrix whose bf16 W exceeds 256 MiB; a value given here applies to both)
  *  fused_ahead:      single-sweep MX pass, load steps in flight per wave (1 or 3; 3 only with
  *                    one half and two rows per step; default 1)
  *  pass_target:      two-sweep pass for bf16 weights, target workgroup count (default 768)

@@ -2,6 +2,7 @@
 no oracle: determinism, resume, the MX single-sweep path against the two-sweep path, zero
 slices, the fallback when the single-sweep identity cannot be guaranteed, and every error
 status forced from the host."""
+import dataclasses
 import os
 
 import numpy as np
@@ -68,6 +69,17 @@ def test_workload3_full_size(dq, par_oracle, which):
 def test_workload4_full_size(dq, par_oracle):
     gpu, ref, res = _run_pair(dq, par_oracle, workloads.config4())
     print(f"[solve] cfg4: {res}", flush=True)
+
+
+def test_single_sweep_beyond_the_infinity_cache(dq, par_oracle):
+    # a bf16 W of 285 MB, larger than the 256 MiB Infinity Cache, on which the single-sweep
+    # pass takes its larger launch (about three workgroups per CU): the 70B-shaped matrix's
+    # distribution at 17408 rows, MXFP4 G32 and MXINT4 G32, against the oracle
+    base = workloads.config4(rows=17408)
+    assert base.W.size * 2 > 256 << 20
+    for fmt in ("mxfp4", "mxint4"):
+        w = dataclasses.replace(base, name=f"cfg4_rows17408_{fmt}", fmt=fmt, group=32, T=4)
+        _run_pair(dq, par_oracle, w)
 
 
 def test_workload5_first_layer_full_size(dq, par_oracle):
