@@ -87,6 +87,13 @@ __global__ void k_fp4_decode(float p, float* out) {
   out[2 * t + 1] = v.y;
 }
 
+// the encode direction on given pairs: out[i] = code byte of (x[2 i], x[2 i + 1]) at scale p
+__global__ void k_fp4_encode(float p, const float* x, uint32_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[2 * i], x[2 * i + 1], p, 0) & 0xFFu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +109,13 @@ int fp4_scan(int mode, float p, uint32_t u_last, uint32_t* res, int cap, hipStre
 int fp4_decode(float p, float* out, hipStream_t s) {
   if (!out) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_fp4_decode, dim3(1), dim3(1024), 0, s, p, out);
+  return (int)hipGetLastError();
+}
+
+// x: device, 2 n floats; out: device, n words
+int fp4_encode(float p, const float* x, uint32_t* out, int n, hipStream_t s) {
+  if (!x || !out || n < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fp4_encode, dim3((n + 255) / 256), dim3(256), 0, s, p, x, out, n);
   return (int)hipGetLastError();
 }
 

@@ -38,4 +38,6 @@ def lib() -> ctypes.CDLL:
     L.fp4_scan.restype = I
     L.fp4_decode.argtypes = [F, P, P]
     L.fp4_decode.restype = I
+    L.fp4_encode.argtypes = [F, P, P, I, P]
+    L.fp4_encode.restype = I
     return L

@@ -10,7 +10,10 @@ NVFP4 块结构").
 - the NVFP4 fp32 codes (nv_pack8_fast: an odd-rounded quotient, then that conversion with
   scale 1), with and without its clamp, for E4M3 scales times several tensor scales;
 - v_cvt_scalef32_pk_f32_fp4, the decode the single-sweep pass forms code * scale with, for
-  every byte and position.
+  every byte and position;
+- that both read only the exponent field of their fp32 scale: the single-sweep MXFP4 pass
+  passes the group maximum's own bit pattern with two taken off its exponent (a saturating
+  subtract, so an all-zero group passes exponent field 0), mantissa bits and all.
 
 How one scan covers every input: the probe (tests/fp4_scan.hip) records the bit patterns
 where the code of x changes as x rises. Exact E2M1 rounding of x / d is a non-decreasing
@@ -146,3 +149,49 @@ def test_fp4_decode_every_byte(P, k):
     want = np.stack([fb.E2M1_TABLE[byte & 0xF], fb.E2M1_TABLE[byte >> 4]], axis=-1) * p
     for pos in range(4):
         assert np.array_equal(got[pos], want), (k, pos)
+
+
+# scales as the single-sweep pass forms them: exponent field e, arbitrary mantissa bits
+SCALE_MANTISSAS = [0x7FFFFF, 0x400000, 0x2A5A5B]
+
+
+def _scale_bits(k, m):
+    return float(np.array([((k + 127) << 23) | m], np.uint32).view(np.float32)[0])
+
+
+@pytest.mark.parametrize("k", [-34, -3, 0, 7, 29])
+def test_mx_conversion_reads_only_the_scale_exponent(P, k):
+    import torch
+
+    for m in SCALE_MANTISSAS:
+        p = _scale_bits(k, m)
+        r = _scan(P, 0, p, MAX_FINITE)
+        ref = lambda x: _e2m1_index(Fraction(x) / Fraction(2) ** k)
+        assert _check_scan(r, ref, MAX_FINITE, f"scale 2^{k} with mantissa {m:#x}") == 7
+        out = torch.zeros(2048, dtype=torch.float32, device="cuda")
+        assert P.fp4_decode(p, ctypes.c_void_p(out.data_ptr()), None) == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(4, 256, 2).astype(np.float64)
+        byte = np.arange(256)
+        want = np.stack([fb.E2M1_TABLE[byte & 0xF], fb.E2M1_TABLE[byte >> 4]], axis=-1) * 2.0 ** k
+        for pos in range(4):
+            assert np.array_equal(got[pos], want), (k, hex(m), pos)
+
+
+def test_all_zero_group_with_exponent_field_zero(P):
+    # an all-zero group's scale is 0 (or, below 2^-125, a value with exponent field 0): its
+    # codes are 0 (+0 and -0 inputs alike, magnitude 0) and code 0 decodes to 0
+    import torch
+
+    x = torch.tensor([0.0, -0.0, -0.0, 0.0, 0.0, 0.0], dtype=torch.float32, device="cuda")
+    out = torch.full((3,), 0xFF, dtype=torch.int32, device="cuda")
+    for p in (0.0, _scale_bits(-127, 0x7FFFFF), _scale_bits(-127, 0x000001)):
+        assert P.fp4_encode(p, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), 3,
+                            None) == 0
+        dec = torch.ones(2048, dtype=torch.float32, device="cuda")
+        assert P.fp4_decode(p, ctypes.c_void_p(dec.data_ptr()), None) == 0
+        torch.cuda.synchronize()
+        codes = out.cpu().numpy().astype(np.uint32)
+        assert np.all((codes & 0x77) == 0), (p, codes)
+        d = dec.cpu().numpy().reshape(4, 256, 2)
+        assert np.all(d[:, 0, :] == 0.0), p  # byte 0 at every position
