@@ -141,6 +141,59 @@ def test_packed_gemm_matches_oracle(dq, oracle_lib, tokens, out, K, out_dtype):
         _check(dq, oracle_lib, xc, xs, wc, ws, None, out_dtype, name="a=None", packed=True)
 
 
+# Whole 256 x 256 tiles with bf16 output (the shapes of the 8B MLP products): the 16-byte
+# aligned output path, with and without a, against the oracle.
+@pytest.mark.parametrize("tokens,out,K", [(512, 768, 1024), (256, 512, 2048), (768, 256, 3072)])
+def test_packed_gemm_whole_tiles_match_oracle(dq, oracle_lib, tokens, out, K):
+    xc, xs = workloads.mx_operands(tokens, K, seed=15)
+    wc, ws = workloads.mx_operands(out, K, seed=16)
+    a = np.random.default_rng(out + 3).uniform(0.02, 2.0, out).astype(np.float32)
+    _check(dq, oracle_lib, xc, xs, wc, ws, a, "bf16", name="whole tiles", packed=True)
+    _check(dq, oracle_lib, xc, xs, wc, ws, None, "bf16", name="whole tiles, a=None", packed=True)
+
+
+def _bf16_rne(x):
+    """float64 values that are exact in fp32, rounded to bf16 (nearest, ties to even)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_packed_gemm_whole_tiles_bf16_exact(dq, oracle_lib):
+    # sums that fit fp32 exactly and power-of-two a: the bf16 output is the exact product
+    # rounded once, the same bits as the oracle's value rounded to bf16
+    tokens, out, K = 512, 512, 2048
+    xc, xs = workloads.mx_operands(tokens, K, seed=17, lo=126, hi=129)
+    wc, ws = workloads.mx_operands(out, K, seed=18, lo=126, hi=129)
+    a = (2.0 ** np.random.default_rng(19).integers(-3, 4, out)).astype(np.float32)
+    print(f"[gemm] whole tiles bf16 exact tokens={tokens} out={out} K={K}", flush=True)
+    y = _bf16_host(_gemm(dq, xc, xs, wc, ws, a, "bf16", True))
+    ref = oracle_lib.gemm_mx(xc, xs, wc, ws, a)
+    assert np.array_equal(y, _bf16_rne(ref))
+
+
+def test_packed_gemm_whole_tiles_more_than_one_per_cu(dq, oracle_lib):
+    # 16 x 17 = 272 tiles, more than one per CU; sampled rows and channels, every tile's first
+    # and last ones included
+    tokens, out, K = 4096, 4352, 1024
+    xc, xs = workloads.mx_operands(tokens, K, seed=25)
+    wc, ws = workloads.mx_operands(out, K, seed=26)
+    a = np.random.default_rng(27).uniform(0.5, 2.0, out).astype(np.float32)
+    rng = np.random.default_rng(28)
+    ts = np.unique(np.concatenate([np.arange(0, tokens, 256), np.arange(255, tokens, 256),
+                                   rng.choice(tokens, 16, replace=False)]))
+    cs = np.unique(np.concatenate([np.arange(0, out, 256), np.arange(255, out, 256),
+                                   rng.choice(out, 16, replace=False)]))
+    for aa in (a, None):
+        print(f"[gemm] whole tiles x272 a={'yes' if aa is not None else 'no'}", flush=True)
+        got = _bf16_host(_gemm(dq, xc, xs, wc, ws, aa, "bf16", True))[np.ix_(ts, cs)]
+        asub = None if aa is None else aa[cs]
+        ref = oracle_lib.gemm_mx(xc[ts], xs[ts], wc[cs], ws[cs], asub)
+        tol = _bound(oracle_lib, xc[ts], xs[ts], wc[cs], ws[cs], asub, K)
+        tol = tol + 2.0 ** -8 * (np.abs(ref) + tol)
+        assert np.all(np.abs(got - ref) <= tol)
+
+
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("tokens,out,K", [(256, 512, 2048), (97, 131, 224)])
 def test_gemm_exact_when_the_sums_fit_fp32(dq, oracle_lib, tokens, out, K, packed):
