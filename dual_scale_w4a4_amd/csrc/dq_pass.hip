@@ -48,9 +48,14 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
   constexpr bool EMIT = (MODE & kModeEmit) != 0;
   constexpr int E = kPassEpl;
   uint32_t u[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
-  if (PARTIAL) {
+  // NVFP4's iteration passes need only the codes' magnitudes: q has the sign of x, which is
+  // that of w (x = w rb ra with positive scales, and fp32 rounding is symmetric), so they
+  // read |w| (sign bits cleared here), scale it into |x|, and the sums take w q = |w| |q|
+  constexpr bool kMag = FMT == kNvFp4 && !EMIT;
+  if (PARTIAL || kMag) {
+    const uint32_t keep = (PARTIAL ? amask : 0xFFFFFFFFu) & (kMag ? 0x7FFF7FFFu : 0xFFFFFFFFu);
 #pragma unroll
-    for (int k = 0; k < 8; k++) u[k] &= amask;
+    for (int k = 0; k < 8; k++) u[k] &= keep;
   }
   float w[E], x[E];
 #pragma unroll
@@ -63,7 +68,7 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
   for (int k = 0; k < E; k++) {
     const float y = w[k] * rb[k];  // column scale first, then row scale; two fp32 roundings
     x[k] = y * ra;
-    mx = fmaxf(mx, fabsf(x[k]));
+    mx = fmaxf(mx, kMag ? x[k] : fabsf(x[k]));
     if (MODE & kModeYmax) ym = fmaxf(ym, fabsf(y));
   }
   ymax = ym;
@@ -102,6 +107,9 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
     if (FMT == kInt4Bf16 && __any(int4_needs_clamp(gq.d))) {  // rare: a subnormal scale
 #pragma unroll
       for (int k = 0; k < E; k++) q[k] = int4_clamp(code64<FMT>(x[k], r, gq));
+    } else if (kMag) {
+#pragma unroll
+      for (int k = 0; k < E; k++) q[k] = e2m1_grid64(snap_quotient((double)x[k], r));
     } else {
 #pragma unroll
       for (int k = 0; k < E; k++) q[k] = code64<FMT>(x[k], r, gq);

@@ -337,3 +337,43 @@ def test_per_pass_tensor_scale_rejects_a_fixed_one(dq):
     with pytest.raises(dq.DQError) as e:
         dq.solve(W, "nvfp4", 16, 2, g0=0.01, per_pass_g=True)
     assert e.value.status == 1
+
+
+def _nvfp4_tie_rows(rows, cols, seed):
+    """bf16 weights whose first NVFP4 pass meets exact E2M1 ties: the largest element is
+    2688 * 2^-10, so g = 2^-10 exactly, and every third row has groups whose maximum is 6 s0 g
+    (inner scale s0 = 1 or 1.5, d = s0 g) with the other elements on the decision points
+    (1/4, 3/4, ..., 5) times d."""
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0, 0.003, (rows, cols)).astype(np.float32)
+    W[0, 0] = np.float32(2688 * 2.0 ** -10)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for i in range(1, rows, 3):
+        d = (1.0 if i % 2 else 1.5) * 2.0 ** -10
+        for c0 in range(16 * (i % 4), cols - 15, 64):
+            ks = rng.choice(mids, 16) * rng.choice([-1.0, 1.0], 16)
+            ks[rng.integers(16)] = 6.0
+            W[i, c0:c0 + 16] = (ks * d).astype(np.float32)
+    return workloads.fp32_to_bf16_bits(W)
+
+
+@pytest.mark.parametrize("rows,cols,per_pass_g", [(96, 1024, False), (301, 2080, False),
+                                                  (160, 1104, True)])
+def test_nvfp4_ties_in_the_iteration_passes(dq, oracle_lib, rows, cols, per_pass_g):
+    # bf16 weights and E4M3 scales make exact E2M1 ties common in NVFP4's two-sweep passes
+    # (here planted in the first pass): the codes must settle them to the even index, as the
+    # oracle's exact quotient does
+    T = 5
+    Wb = _nvfp4_tie_rows(rows, cols, seed=rows + cols)
+    print(f"[solve] nvfp4 ties {rows}x{cols} per_pass_g={per_pass_g}", flush=True)
+    gpu = dq.solve(to_device(Wb, "bf16"), "nvfp4", 16, T, per_pass_g=per_pass_g)
+    if per_pass_g:
+        ref = oracle_lib.solve_pass_g(Wb, "bf16", 16, T)
+        res = compare_solve(gpu, ref, "nvfp4", rows, cols)
+        assert_parity(res, exact=False, name=f"ties per-pass g {rows}x{cols}")
+        assert res["code_diffs"] == 0 and res["a_flips"] == 0 and res["b_flips"] == 0, res
+    else:
+        ref = oracle_lib.solve(Wb, "bf16", "nvfp4", 16, T, diag=True)
+        assert host(gpu["g"])[0] == np.float32(2.0 ** -10) == np.float32(ref["g"])
+        res = compare_solve(gpu, ref, "nvfp4", rows, cols)
+        assert_parity(res, exact=float(ref["margin"].min()) > 1e-9, name=f"ties {rows}x{cols}")
