@@ -50,9 +50,9 @@ METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracl
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
-    "per_elem": {"3/fused": 10.45, "4/row": 23.23, "4/col": 22.95, "5/row": 14.24,
+    "per_elem": {"3/fused": 10.45, "4/row": 19.73, "4/col": 19.45, "5/row": 14.24,
                  "5/col": 14.09},  # workload / pass kind
-    "sources_sha256": "3105ae3f1fddcfde36d9fa71f9c1c81f2bbdf1bb7fded4d2a5dced7c5f60273e",
+    "sources_sha256": "efab8287fd9424f2b644aab564874f3c21eb10e9ebfbf127df37f98a3b6e0c4b",
 }
 
 
