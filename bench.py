@@ -52,7 +52,7 @@ VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
     "per_elem": {"3/fused": 10.45, "4/row": 19.73, "4/col": 19.45, "5/row": 14.24,
                  "5/col": 14.09},  # workload / pass kind
-    "sources_sha256": "efab8287fd9424f2b644aab564874f3c21eb10e9ebfbf127df37f98a3b6e0c4b",
+    "sources_sha256": "0be194ba2a4914354b104641fa4118d478e1ee1fc58f4d63ee6e00a2b7156f6a",
 }
 
 

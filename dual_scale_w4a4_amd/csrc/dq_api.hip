@@ -181,9 +181,11 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = 
     p.off_ymax = o;
     o = align_up(o + sizeof(float) * (size_t)p.g_nct * m);
   }
-  if (fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4) {  // single sweep: the first pass's W^2 partials
+  if (fmt != DQ_FMT_NVFP4) {  // the first pass's W^2 partials (single sweep or bf16 two-sweep)
+    const bool mx = fmt == DQ_FMT_MXINT4 || fmt == DQ_FMT_MXFP4;
+    const size_t parts = (size_t)(mx && p.f_nct > p.g_nct ? p.f_nct : p.g_nct);
     p.off_epart = o;
-    o = align_up(o + sizeof(double) * (size_t)p.f_nct * m);
+    o = align_up(o + sizeof(double) * parts * m);
   }
   p.total = o;
   return p;
@@ -311,14 +313,19 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   // take the general single-sweep kernel)
   const bool fast = fused && io.bf16 && fast_shape_ok(p);
   const bool pass_g = nv && io.init && (io.init->flags & DQ_SOLVE_PER_PASS_G);
+  // the row-resident pass (bf16 weights, a tensor scale fixed for the solve, shapes it takes)
+  const bool rowres = !fused && io.bf16 && !pass_g && p.rr_ok;
   VecArgs va{a_src, io.a, ra, again ? nullptr : a0s, p.m, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(va, s));
   VecArgs vb{b_src, io.b, rb, again ? nullptr : b0s, p.n, p.fmt, 1, fast ? 1 : 0, status};
   DQ_TRY(launch_vec(vb, s));
-  // E_i = sum_j W_ij^2 and the finite check: in their own sweep of W, or, on the single-sweep
-  // path with at least one iteration, inside the first iteration's pass
+  // E_i = sum_j W_ij^2 and the finite check: in their own sweep of W, or, with at least one
+  // iteration, inside the first iteration's pass: the single-sweep pass, or the bf16 two-sweep
+  // row pass where no tensor scale has to be known before it (not NVFP4) and the row-resident
+  // pass is not taken
   const bool stat_in_pass = fast && io.T > 0;
-  if (!stat_in_pass) {
+  const bool stat_in_row_pass = !fused && io.bf16 && !nv && !rowres && io.T > 0;
+  if (!stat_in_pass && !stat_in_row_pass) {
     RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
     DQ_TRY(launch_rowstat(io.bf16, rs, s));
   }
@@ -399,8 +406,6 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
   fu.a = io.a;
   fu.status = status;
 
-  // the row-resident pass (bf16 weights, a tensor scale fixed for the solve, shapes it takes)
-  const bool rowres = io.bf16 && !pass_g && p.rr_ok;
   RowResArgs rr{};
   rr.W = static_cast<const uint16_t*>(io.W);
   rr.m = p.m;
@@ -478,16 +483,23 @@ dq_status enqueue_solve(const Plan& p, char* ws, const SolveIo& io, bool fused, 
       if (pass_g && t > 0 && (st = pass_scale()) != DQ_OK) return st;
       tm.before(DQ_K_ROW);
       // per-pass tensor scale: the row pass also records each row's max |fl32(W rb)|, from
-      // which the finalize forms the column pass's row maxima of |X| without a read of W
-      DQ_TRY(launch_pass(p.fmt, pass_g ? (kModeRow | kModeYmax) : kModeRow, sp, s));
+      // which the finalize forms the column pass's row maxima of |X| without a read of W; the
+      // first row pass of a solve may also sum W^2 (E_i, and the finite check)
+      const bool stat = stat_in_row_pass && t == 0;
+      sp.epart = stat ? at<double>(ws, p.off_epart) : nullptr;
+      DQ_TRY(launch_pass(p.fmt, pass_g ? (kModeRow | kModeYmax) : (stat ? kModeRow | kModeStat : kModeRow),
+                         sp, s));
       tm.after();
       fa.nct = p.g_nct;
       fa.nrc = p.g_nrc;
       fa.ymax = pass_g ? sp.ymax : nullptr;
       fa.amax_out = pass_g ? amax : nullptr;
+      fa.epart = sp.epart;
       if ((st = finalize(true, false, true)) != DQ_OK) return st;
       fa.ymax = nullptr;
       fa.amax_out = nullptr;
+      fa.epart = nullptr;
+      sp.epart = nullptr;
       if (pass_g) {
         tm.before(DQ_K_SETUP);
         ScaleArgs s2{amax, p.m, nullptr, 0.0f, gs, io.tensor_scale, status};
@@ -551,9 +563,11 @@ struct BatchMat {
   char* ws = nullptr;
   SolveIo io{};
   bool pass_g = false;
+  bool stat_first = false;  // E_i and the finite check from the first row pass (as enqueue_solve)
   int* status = nullptr;
   float *ra = nullptr, *rb = nullptr, *amax = nullptr, *gs = nullptr;
   double* E = nullptr;
+  double* epart = nullptr;
   double* msepart = nullptr;
   dq::SweepArgs sp{};
   dq::FinArgs fa{};
@@ -574,8 +588,12 @@ struct BatchMat {
     DQ_TRY(launch_vec(va, s));
     VecArgs vb{init->b0, io.b, rb, nullptr, p.n, p.fmt, 1, 0, status};
     DQ_TRY(launch_vec(vb, s));
-    RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
-    DQ_TRY(launch_rowstat(true, rs, s));
+    stat_first = !nv && io.T > 0;
+    epart = stat_first ? at<double>(ws, p.off_epart) : nullptr;
+    if (!stat_first) {
+      RowStatArgs rs{io.W, p.m, p.n, ra, rb, E, nv ? amax : nullptr, status};
+      DQ_TRY(launch_rowstat(true, rs, s));
+    }
     if (nv) {
       ScaleArgs sa{amax, p.m, nullptr, init->g0, gs, io.tensor_scale, status};
       DQ_TRY(launch_tensor_scale(sa, s));
@@ -674,22 +692,29 @@ dq_status batch_iteration(BatchMat* mats, int n, int t, hipStream_t s) {
         const dq_status st = b[k].pass_scale(s);
         if (st != DQ_OK) return st;
       }
+    // the first row pass also sums W^2 per row where no tensor scale comes first (every
+    // matrix of a batch has the same format)
+    const bool stat = t == 0 && b[0].stat_first;
     PassMulti pm{};
     pm.n = cnt;
     for (int k = 0; k < cnt; k++) {
       pm.a[k] = b[k].sp;
+      pm.a[k].epart = stat ? b[k].epart : nullptr;
       pm.start[k + 1] = pm.start[k] + b[k].p.g_nct * b[k].p.g_nrc;
     }
-    DQ_TRY(launch_pass_multi(fmt, pass_g ? (kModeRow | kModeYmax) : kModeRow, pm, s));
+    DQ_TRY(launch_pass_multi(fmt, pass_g ? (kModeRow | kModeYmax) : (stat ? kModeRow | kModeStat : kModeRow),
+                             pm, s));
     FinMulti fm{};
     fm.n = cnt;
     for (int k = 0; k < cnt; k++) {
       b[k].fa.ymax = pass_g ? b[k].sp.ymax : nullptr;
       b[k].fa.amax_out = pass_g ? b[k].amax : nullptr;
+      b[k].fa.epart = stat ? b[k].epart : nullptr;
       fm.a[k] = b[k].fin(true, false, true);
       fm.start[k + 1] = fm.start[k] + b[k].p.nblk_rows;
       b[k].fa.ymax = nullptr;
       b[k].fa.amax_out = nullptr;
+      b[k].fa.epart = nullptr;
     }
     DQ_TRY(launch_finalize_multi(fm, s));
     if (pass_g)

@@ -18,7 +18,7 @@ enum : int {
 };
 
 // sweep modes (bit set)
-enum : int { kModeRow = 1, kModeCol = 2, kModeEmit = 4, kModeGauge = 8, kModeYmax = 16 };
+enum : int { kModeRow = 1, kModeCol = 2, kModeEmit = 4, kModeGauge = 8, kModeYmax = 16, kModeStat = 32 };
 
 struct SweepArgs {
   const void* W;
@@ -38,6 +38,7 @@ struct SweepArgs {
   void* scales;
   int* status;
   float* ymax;       // kModeYmax: [nct][m] row maxima of |fl32(W rb)| per column tile
+  double* epart;     // kModeStat (two-sweep pass): [nct][m] sums of W^2 over each tile's columns
 };
 
 // Single-sweep MX pass on bf16 weights (see k_fused_mx).

@@ -39,8 +39,8 @@ template <int FMT, int LPG, int MODE, bool PARTIAL>
 __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[kPassEpl],
                                          const double (&bbd)[kPassEpl], float ra, float ai,
                                          float g, float sixg, double r6, uint32_t amask,
-                                         double& nacc,
-                                         double& dacc, double (&P)[kPassEpl],
+                                         double& nacc, double& dacc, double& wacc,
+                                         double (&P)[kPassEpl],
                                          double (&Q)[kPassEpl], int& flags, uint32_t* code_word,
                                          void* scale_ptr, float& ymax) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
@@ -121,13 +121,15 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
   }
 
   if (ROW) {
-    double nl = 0.0, dl = 0.0;
+    double nl = 0.0, dl = 0.0, wl = 0.0;
 #pragma unroll
     for (int k = 0; k < E; k++) {
       const double t = q[k] * bbd[k];  // R / d, exact
       nl = fma((double)w[k], t, nl);
       dl = fma(t, t, dl);
+      if (MODE & kModeStat) wl = fma((double)w[k], (double)w[k], wl);  // W^2, exact
     }
+    wacc = wl;
     const double dd = (double)gq.d;
     nacc = nl * dd;
     dacc = dl * (dd * dd);
@@ -154,7 +156,9 @@ __device__ __forceinline__ void pass_row(const uint4 (&v)[2], const float (&rb)[
 
 // The pass on one workgroup's tile (block `bid` of the matrix's grid). MODE: kModeRow,
 // kModeCol or kModeRow | kModeEmit (the final Q with the row sums of its error), optionally
-// | kModeYmax. S: rows per load step. G >= 16; LPG = G / 16 lanes per group.
+// | kModeYmax (NVFP4's per-pass tensor scale), or kModeRow | kModeStat (a solve's first row
+// pass, which also sums W^2 per row and tile for E_i and the finite check). S: rows per load
+// step. G >= 16; LPG = G / 16 lanes per group.
 template <int FMT, int G, int MODE, bool PARTIAL, int S>
 __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
   constexpr bool ROW = (MODE & kModeRow) != 0;
@@ -232,9 +236,13 @@ __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
   __shared__ float ysmem[YMAX ? kWaves * kPassBatch * kWave : 1];
   float* Ry = ysmem + (YMAX ? wave * (kPassBatch * kWave) : 0);  // [8 rows][64 lanes] max |y|
   double2* R = smem + wave * (kPassBatch * kWave);  // this wave's [8 rows][64 lanes] partials
+  // the first pass of a solve (STAT): each row's sum of W^2 over the tile's columns, for E_i
+  constexpr bool STAT = (MODE & kModeStat) != 0;
+  __shared__ double wsmem[STAT ? kWaves * kPassBatch * kWave : 1];
+  double* Rw = wsmem + (STAT ? wave * (kPassBatch * kWave) : 0);
   float ra_cur = 0.0f, a_cur = 0.0f, ra_nxt = 0.0f, a_nxt = 0.0f;
   auto row_step = [&](const uint4 (&v)[2], int64_t i, int r) {
-    double nacc = 0.0, dacc = 0.0;
+    double nacc = 0.0, dacc = 0.0, wacc = 0.0;
     float ym = 0.0f;
     if (i < r_end) {  // uniform across the wave
       const float ra = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_cur), r));
@@ -247,11 +255,12 @@ __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
         scale_ptr = FMT == kInt4Bf16 ? (void*)(static_cast<uint16_t*>(p.scales) + si)
                                      : (void*)(static_cast<uint8_t*>(p.scales) + si);
       }
-      pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, r6, amask, nacc, dacc, P,
+      pass_row<FMT, LPG, MODE, PARTIAL>(v, rb, bbd, ra, ai, g, sixg, r6, amask, nacc, dacc, wacc, P,
                                         Q, flags, code_word, scale_ptr, ym);
     }
     if (ROW) R[r * kWave + lane] = make_double2(nacc, dacc);
     if (YMAX) Ry[r * kWave + lane] = ym;
+    if (STAT) Rw[r * kWave + lane] = wacc;
   };
 
   constexpr int kSteps = kPassBatch / S;
@@ -296,6 +305,14 @@ __device__ __forceinline__ void pass_block(const SweepArgs& p, int bid) {
       D = sum8_dpp(D);
       const int64_t i = row0 + (lane >> 3);
       if ((lane & 7) == 0 && i < r_end) p.rowpart[(int64_t)ct * p.m + i] = make_double2(N, D);
+      if (STAT) {  // the same for the row's W^2
+        const double* wsrc = Rw + (lane >> 3) * kWave + (lane & 7) * 8;
+        double Wq = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) Wq += wsrc[k];
+        Wq = sum8_dpp(Wq);
+        if ((lane & 7) == 0 && i < r_end) p.epart[(int64_t)ct * p.m + i] = Wq;
+      }
       if (YMAX) {  // the same for the row max of |y| (bit patterns of non-negative floats)
         const float* ysrc = Ry + (lane >> 3) * kWave + (lane & 7) * 8;
         uint32_t yb = 0u;
@@ -352,7 +369,7 @@ __global__ __launch_bounds__(kBlock) void k_pass_multi(PassMulti m) {
 // Rows per load step: INT4's row pass loads one row ahead instead of two, which keeps it at
 // 168 VGPRs (three waves per SIMD instead of two)
 template <int FMT, int MODE>
-constexpr int pass_step_rows() { return FMT == kInt4Bf16 && MODE == kModeRow ? 1 : 2; }
+constexpr int pass_step_rows() { return FMT == kInt4Bf16 && (MODE & ~kModeStat) == kModeRow ? 1 : 2; }
 
 template <int FMT, int G, int MODE>
 static hipError_t pass_partial(const SweepArgs& a, dim3 grid, hipStream_t s) {
@@ -395,6 +412,9 @@ static hipError_t pass_multi_mode(int mode, const PassMulti& m, hipStream_t s) {
     case kModeRow | kModeYmax:
       if constexpr (FMT == kNvFp4) return pass_multi_group<FMT, kModeRow | kModeYmax>(m, s);
       return hipErrorInvalidValue;
+    case kModeRow | kModeStat:
+      if constexpr (FMT != kNvFp4) return pass_multi_group<FMT, kModeRow | kModeStat>(m, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -426,6 +446,9 @@ static hipError_t pass_mode(int mode, const SweepArgs& a, dim3 grid, hipStream_t
     case kModeRow: return pass_group<FMT, kModeRow>(a, grid, s);
     case kModeCol: return pass_group<FMT, kModeCol>(a, grid, s);
     case kModeRow | kModeEmit: return pass_group<FMT, kModeRow | kModeEmit>(a, grid, s);
+    case kModeRow | kModeStat:
+      if constexpr (FMT != kNvFp4) return pass_group<FMT, kModeRow | kModeStat>(a, grid, s);
+      return hipErrorInvalidValue;  // NVFP4 needs its tensor scale before the first pass
     case kModeRow | kModeYmax:
       if constexpr (FMT == kNvFp4) return pass_group<FMT, kModeRow | kModeYmax>(a, grid, s);
       return hipErrorInvalidValue;  // only NVFP4 has a tensor scale

@@ -243,12 +243,14 @@ def test_error_statuses(dq):
     assert np.array_equal(host(x["codes"]), host(y["codes"]))
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
-def test_single_sweep_first_pass_row_statistics(dq, oracle_lib, fmt):
-    """On the single-sweep path for bf16 W (T >= 1) the first iteration's pass also forms
-    E_i = sum_j W_ij^2 and the finite check: a NaN or an infinity anywhere in W is reported
-    as non-finite, by the blocking call and in the asynchronous status word (bit 1); T = 0
-    solves (no iteration pass) keep the separate row-statistics sweep and match the oracle."""
+@pytest.mark.parametrize("fmt,two_sweep", [("mxfp4", False), ("mxint4", False),
+                                           ("int4_bf16", False), ("mxfp4", True)])
+def test_first_pass_row_statistics(dq, oracle_lib, fmt, two_sweep):
+    """For bf16 W (T >= 1) the first iteration's pass also forms E_i = sum_j W_ij^2 and the
+    finite check, on the single-sweep path and in the two-sweep path's first row pass: a NaN
+    or an infinity anywhere in W is reported as non-finite, by the blocking call and in the
+    asynchronous status word (bit 1); T = 0 solves (no iteration pass) keep the separate
+    row-statistics sweep and match the oracle."""
     import torch
 
     W = rand_w(96, 1536, seed=31, dtype="bf16", outliers=3)  # bf16 bits
@@ -258,17 +260,19 @@ def test_single_sweep_first_pass_row_statistics(dq, oracle_lib, fmt):
         print(f"[solve] {fmt} bf16 with {bits:#06x} at {where}", flush=True)
         Wd = to_device(bad, "bf16")
         with pytest.raises(dq.DQError) as e:
-            dq.solve(Wd, fmt, 32, 4)
+            dq.solve(Wd, fmt, 32, 4, two_sweep=two_sweep)
         assert e.value.status == 3
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         out = dq.solve_outputs(Wd, fmt, 32, 4)
-        dq.solve_async(Wd, fmt, 32, 4, out, status)
+        dq.solve_async(Wd, fmt, 32, 4, out, status, two_sweep=two_sweep)
         torch.cuda.synchronize()
         assert int(host(status)[0]) & 1
-    # T = 0: setup and emit only
-    ref = oracle_lib.solve(W, "bf16", fmt, 32, 0, diag=True)
-    gpu = dq.solve(to_device(W, "bf16"), fmt, 32, 0)
-    assert_parity(compare_solve(gpu, ref, fmt, 96, 1536), exact=True, name=f"{fmt} T=0")
+    # T = 0: setup and emit only; T = 3: the first pass's E_i in every mse[t]
+    for T in (0, 3):
+        ref = oracle_lib.solve(W, "bf16", fmt, 32, T, diag=True)
+        gpu = dq.solve(to_device(W, "bf16"), fmt, 32, T, two_sweep=two_sweep)
+        assert_parity(compare_solve(gpu, ref, fmt, 96, 1536),
+                      exact=T == 0 or float(ref["margin"].min()) > 1e-9, name=f"{fmt} T={T}")
 
 
 @pytest.mark.parametrize("row_resident", [1, -1])
