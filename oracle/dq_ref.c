@@ -693,7 +693,9 @@ static int solve_core(const void* W, int wt, int64_t rows, int64_t cols, int fmt
     }
 
     /* 5: column update with codes fixed, S = D_a Qhat (eq. 2, right); each column's
-     * sums run over rows in ascending order */
+     * sums run over rows in ascending order. The blocks of 256 columns only hand the columns
+     * out to threads: every column's two sums are the same fp64 additions, in the same order,
+     * as the plain loop over i for that j. */
     const int64_t JB = 256;
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t j0 = 0; j0 < n; j0 += JB) {
