@@ -275,6 +275,29 @@ def test_first_pass_row_statistics(dq, oracle_lib, fmt, two_sweep):
                       exact=T == 0 or float(ref["margin"].min()) > 1e-9, name=f"{fmt} T={T}")
 
 
+FIRST_PASS_CASES = [
+    # (rows, cols, format, group, T, two_sweep): the two-sweep path's first row pass, which
+    # also forms E_i, on ragged shapes (rows ending inside a load step and an 8-row batch,
+    # columns ending inside a 1024-column tile, a single row, a 16-column matrix), every group
+    # size, T = 1 (that pass and the final one only) and a little more; the MX formats on
+    # their two-sweep path
+    (203, 1088, "int4_bf16", 32, 1, False), (77, 2112, "int4_bf16", 64, 2, False),
+    (1, 512, "int4_bf16", 16, 1, False), (517, 16, "int4_bf16", 16, 3, False),
+    (300, 4096, "mxint4", 32, 1, True), (64, 96, "mxfp4", 32, 2, True),
+]
+
+
+@pytest.mark.parametrize("rows,cols,fmt,group,T,two_sweep", FIRST_PASS_CASES)
+def test_two_sweep_first_pass_statistics_on_ragged_shapes(dq, oracle_lib, rows, cols, fmt, group,
+                                                            T, two_sweep):
+    Wb = rand_w(rows, cols, seed=7 * rows + cols, dtype="bf16", outliers=max(1, cols // 200))
+    print(f"[solve] first pass {rows}x{cols} {fmt} G{group} T={T}", flush=True)
+    gpu = dq.solve(to_device(Wb, "bf16"), fmt, group, T, two_sweep=two_sweep)
+    ref = oracle_lib.solve(Wb, "bf16", fmt, group, T, diag=True)
+    res = compare_solve(gpu, ref, fmt, rows, cols)
+    assert_parity(res, exact=float(ref["margin"].min()) > 1e-9, name=f"{rows}x{cols} {fmt}")
+
+
 @pytest.mark.parametrize("row_resident", [1, -1])
 @pytest.mark.parametrize("fmt", ["int4_bf16", "nvfp4"])
 def test_subnormal_groups_on_the_bf16_passes(dq, oracle_lib, fmt, row_resident):
