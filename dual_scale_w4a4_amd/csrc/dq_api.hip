@@ -156,7 +156,7 @@ Plan make_plan(int64_t m, int64_t n, int fmt, int G, const LaunchShape& shape = 
     p.rr_nwg = (int)((m + p.rr_rpc - 1) / p.rr_rpc);
   }
   p.nblk_rows = (int)((m + 255) / 256);
-  p.nblk_cols = (int)((n + 31) / 32);  // finalize: 8 lanes per column
+  p.nblk_cols = (int)((n + dq::kFinColsPerBlock - 1) / dq::kFinColsPerBlock);  // finalize
   size_t o = 0;
   p.off_status = o; o = align_up(o + 64);
   p.off_ra = o; o = align_up(o + sizeof(float) * m);

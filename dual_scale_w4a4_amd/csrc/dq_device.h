@@ -430,6 +430,33 @@ __device__ __forceinline__ double sum8_dpp(double v) {
   return v;
 }
 
+// sum over aligned groups of 16 lanes, fixed order, result in all 16 lanes
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i within each 16 lanes
+__device__ __forceinline__ double sum16_dpp(double v) {
+  v = sum8_dpp(v);
+  v += dpp_f64<kDppRowMirror>(v);
+  return v;
+}
+
+// sum over aligned groups of 32 lanes, fixed order, result in all 32 lanes (the pair of
+// 16-lane sums added the same way round in both halves)
+__device__ __forceinline__ double sum32_lanes(double v) {
+  v = sum16_dpp(v);
+  return v + __shfl_xor(v, 16, kWave);
+}
+
+// sum over a workgroup of 4 waves in a fixed order, the result returned to every thread:
+// 16-lane sums, the wave's four in lane order, the waves' in wave order. `red` is LDS of at
+// least 4 doubles; one barrier (the caller keeps `red` untouched until all have read it).
+__device__ __forceinline__ double block_sum4(double v, double* red) {
+  v = sum16_dpp(v);
+  const double w = ((__shfl(v, 0, kWave) + __shfl(v, 16, kWave)) + __shfl(v, 32, kWave)) +
+                   __shfl(v, 48, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = w;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
 // butterfly sum over the 64 lanes, the same fixed order in every lane and run
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

@@ -8,6 +8,9 @@ namespace dq {
 
 enum Fmt : int { kInt4Bf16 = 0, kMxInt4 = 1, kMxFp4 = 2, kNvFp4 = 3 };
 
+// finalize: columns per 256-thread block (32 lanes add each column's partial sums)
+constexpr int kFinColsPerBlock = 8;
+
 // device status word bits
 enum : int {
   kStNonFinite = 1,  // W has a NaN / Inf

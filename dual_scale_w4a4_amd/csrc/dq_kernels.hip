@@ -697,13 +697,8 @@ __device__ void mse_collect(const double* part, int count, double* out, double i
   const int tid = threadIdx.x;
   double s = 0.0;
   for (int k = tid; k < count; k += 256) s += part[k];
-  red[tid] = s;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  if (tid == 0) *out = red[0] * inv_mn;
+  s = block_sum4(s, red);
+  if (tid == 0) *out = s * inv_mn;
 }
 
 __global__ __launch_bounds__(256) void k_mse_collect(const double* part, int count, double* out,
@@ -714,8 +709,9 @@ __global__ __launch_bounds__(256) void k_mse_collect(const double* part, int cou
 
 // Closed-form updates (eq. 2) and projections, plus the error of the state the row sums were
 // taken at, e_i = E_i - 2 a_i N_i + a_i^2 D_i (or the directly summed row error). Per block
-// the row errors are added in a fixed tree order into part_out; the next finalize (or a
-// final collect kernel) adds the block sums in a fixed order.
+// the row errors are added in a fixed order (block_sum4: lane trees, then waves) into
+// part_out; the next finalize (or a final collect kernel) adds the block sums in a fixed
+// order.
 __device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
   __shared__ double red[256];
   const int tid = threadIdx.x;
@@ -788,22 +784,18 @@ __device__ __forceinline__ void finalize_block(const FinArgs& p, int bid) {
         if (p.ymax) p.amax_out[i] = Y * p.ra[i];
       }
     }
-    red[tid] = err;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s) red[tid] += red[tid + s];
-      __syncthreads();
-    }
+    const double esum = block_sum4(err, red);
     if (flags) atomicOr(p.status, flags);
-    if (tid == 0 && p.part_out) p.part_out[bid] = red[0];
+    if (tid == 0 && p.part_out) p.part_out[bid] = esum;
   } else {
-    // 8 lanes per column: lane s adds partials s, s + 8, ... in order, then a fixed tree
-    const int64_t j = (int64_t)(bid - p.nblk_rows) * 32 + tid / 8;
-    const int sub = tid & 7;
+    // 32 lanes per column: lane s adds partials s, s + 32, ... in order (one round of loads
+    // for up to 256 row chunks), then a fixed tree over the 32 lanes
+    const int64_t j = (int64_t)(bid - p.nblk_rows) * kFinColsPerBlock + tid / 32;
+    const int sub = tid & 31;
     double2 nd = make_double2(0.0, 0.0);
-    if (j < p.n) nd = sum_parts(p.colpart + j, p.n, sub, 8, p.nrc);
-    const double N = sum8_dpp(nd.x);
-    const double D = sum8_dpp(nd.y);
+    if (j < p.n) nd = sum_parts(p.colpart + j, p.n, sub, 32, p.nrc);
+    const double N = sum32_lanes(nd.x);
+    const double D = sum32_lanes(nd.y);
     if (j >= p.n || sub != 0) return;
     float bn = 1.0f;
     if (D > 0.0) {
