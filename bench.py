@@ -35,9 +35,9 @@ KERNEL_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_kernels.hip", "dual_scale_w4a4_am
 COUNTERS = {
     "workload": 3,
     "kernel": "k_fused_mx<MXFP4, 32, no emit>",
-    "fetch_kib": 57466.8, "fetch_scale": 2.0,  # average over both matrices' launches
+    "fetch_kib": 57466.9, "fetch_scale": 2.0,  # average over both matrices' launches
     "write_kib": 5968.0, "write_scale": 1.0,
-    "sources_sha256": "e925c15a5ef6aa8214ab910d964649261772f26524ff62577fd3179c77b6dd1e",
+    "sources_sha256": "7658cbac43745f57d0242d226029a0c27ff94d68e64a0d0b8b7b52bc0e001c07",
 }
 METRIC = "weight elems/s per BCD iteration, % HBM peak; final recon MSE vs oracle"
 
@@ -52,7 +52,7 @@ VALU_SOURCES = KERNEL_SOURCES + ("dual_scale_w4a4_amd/csrc/dq_pass.hip",)
 VALU_COUNTERS = {
     "per_elem": {"3/fused": 10.45, "4/row": 19.73, "4/col": 19.45, "5/row": 14.24,
                  "5/col": 14.09},  # workload / pass kind
-    "sources_sha256": "0be194ba2a4914354b104641fa4118d478e1ee1fc58f4d63ee6e00a2b7156f6a",
+    "sources_sha256": "dc8264d85ba0c30b7d3a8eef58cc43adcf9968a1bae2e96702fc54638ac3ce92",
 }
 
 
@@ -78,9 +78,9 @@ ACT_SOURCES = ("dual_scale_w4a4_amd/csrc/dq_act.hip", "dual_scale_w4a4_amd/csrc/
 # rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch, summed over the two dispatches of
 # a step), scaled as above; valid only for the sources they were taken on.
 ACT_COUNTERS = {
-    "fetch_kib": 32899.4 + 114917.7, "fetch_scale": 2.0,
+    "fetch_kib": 32899.8 + 114916.3, "fetch_scale": 2.0,
     "write_kib": 17408.0 + 60928.0, "write_scale": 1.0,
-    "sources_sha256": "6662650f314a762227168da3af80d6ac94ed17d3b512e58794134108362d8e5b",
+    "sources_sha256": "a12db08262690d61829bd69b718dde69dd7d5bdcccce22688031ba01851c2732",
 }
 
 
